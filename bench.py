@@ -1,0 +1,219 @@
+"""Throughput of one MoE-layer training update (forward, backward, clip, AdamW)
+on one MI355X, run as one persistent HIP kernel per update.
+
+Prints ONE JSON line.  ``value`` is tokens/s over the timed updates with every
+input resident in HBM; ``roofline`` relates the persistent kernel's average
+launch time (HIP events on its own stream) to the update's algorithmic HBM
+bytes; ``cpu_baseline`` is the FP64 oracle timed on this host's cores on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec per MoE-layer train update (fwd+bwd+AdamW); ms/update @2×1024"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+F32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_bytes(cfg) -> dict:
+    """HBM bytes the update must move, phase by phase, with every cross-phase value
+    stored once: token rows gathered into expert order, H and A in the activation
+    dtype, expert outputs O in fp32, dO and dH and the per-slot input gradient in
+    the activation dtype, fp32 gradients, 30 bytes per parameter for clip+AdamW
+    (28 in fp32 mode).  Per microbatch unless marked."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, d, f, E, k = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k
+    N = T * k
+    W = E * d * f
+    P = d * E + 2 * W
+    ph = {
+        "router_topk": T * d * es + d * E * 4 + T * k * 8,
+        "gather": T * d * es + N * d * es,
+        "ffn1": N * d * es + W * es + N * f * es,
+        "ffn2": N * f * es + W * es + N * d * 4,
+        "combine": N * d * 4 + T * d * es + N * d * es,
+        "router_bwd": T * d * es,
+        "dA_gelu": N * d * es + W * es + 2 * N * f * es,
+        "dW2": N * f * es + N * d * es + W * 4,
+        "dW1": N * d * es + N * f * es + W * 4,
+        "dXs": N * f * es + W * es + N * d * es,
+        "row_sum": N * d * es + T * d * 4,
+    }
+    per_mb = sum(ph.values())
+    adamw = P * (30 if cfg.dtype == "bf16" else 28)
+    return {"per_microbatch": per_mb, "adamw": adamw,
+            "per_update": per_mb * cfg.microbatches + adamw, "phases": ph}
+
+
+def gemm_flops(cfg) -> int:
+    return 6 * 2 * cfg.tokens * cfg.top_k * cfg.d_model * cfg.d_ff * cfg.microbatches
+
+
+def cpu_baseline(cfg, inp, budget_s: float) -> dict:
+    """The oracle as it stands, on this host's cores, repeated over the same batch
+    until about ``budget_s`` seconds of work (at least one update)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    params = inp.flat_params().astype(np.float64)
+    m = np.zeros_like(params)
+    v = np.zeros_like(params)
+    xs = [inp.microbatch(i)[0] for i in range(cfg.microbatches)]
+    ts = [inp.microbatch(i)[1] for i in range(cfg.microbatches)]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        out = oracle.step(xs, ts, params, m, v, reps + 1, d=cfg.d_model, f=cfg.d_ff, E=cfg.n_experts,
+                          top_k=cfg.top_k, lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
+                          weight_decay=cfg.weight_decay, clip_norm=cfg.clip_norm, bias=inp.router_bias)
+        params, m, v = out["params"], out["exp_avg"], out["exp_avg_sq"]
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    tok = cfg.tokens_in_update * reps
+    return {"value": tok / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full FP64 update(s) of the {cfg.name} layer ({cfg.tokens_in_update} tokens each), "
+                      f"{el:.1f} s", "ms_per_update": 1e3 * el / reps}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="bf16_2x1024")
+    ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the update's multi-GPU sharding is described, not built)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    from moe_step_megakernel_amd import trace as trace_mod
+    from moe_step_megakernel_amd.layer import MoeLayerStep
+
+    cfg = synth.CONFIGS[args.config]
+    print(f"# bench {cfg.name}: T={cfg.tokens}x{cfg.microbatches} d={cfg.d_model} f={cfg.d_ff} "
+          f"E={cfg.n_experts} k={cfg.top_k} {cfg.dtype}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg, 0)
+    dev = torch.device("cuda", 0)
+    layer = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.tokens, cfg.dtype, lr=cfg.lr,
+                         beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.eps, weight_decay=cfg.weight_decay,
+                         clip_norm=cfg.clip_norm, wg_per_cu=args.wg_per_cu)
+    layer.load_params(torch.from_numpy(inp.flat_params()))
+
+    def tok(a, bits):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    X, Tg = tok(inp.x, inp.x_bits), tok(inp.t, inp.t_bits)
+    bias = None if inp.router_bias is None else torch.from_numpy(inp.router_bias).to(dev)
+    dx = torch.empty(cfg.tokens, cfg.d_model, dtype=torch.float32, device=dev)
+    T, M = cfg.tokens, cfg.microbatches
+    stream = torch.cuda.current_stream(dev)
+    step_no = [0]
+
+    def one_update(events=None, trace=None):
+        step_no[0] += 1
+        for mb in range(M):
+            if events is not None:
+                events[mb][0].record(stream)
+            layer.run(X[mb * T:(mb + 1) * T], Tg[mb * T:(mb + 1) * T], tokens_in_update=cfg.tokens_in_update,
+                      step=step_no[0], zero_grad=(mb == 0), apply=(mb == M - 1), dx=dx, router_bias=bias,
+                      trace=trace)
+            if events is not None:
+                events[mb][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_update()
+    torch.cuda.synchronize()
+    layer.status()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(M)]
+          for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        one_update(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    layer.status()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = np.array([[s.elapsed_time(e) for s, e in row] for row in ev])
+    upd_ms = launch_ms.sum(axis=1)
+    ms_per_step = total_ms / args.steps
+    value = cfg.tokens_in_update * args.steps / (total_ms / 1e3)
+    print(f"# {args.steps} updates in {total_ms:.3f} ms; per update median {np.median(upd_ms):.4f} ms "
+          f"p10 {np.percentile(upd_ms, 10):.4f} p90 {np.percentile(upd_ms, 90):.4f}", file=sys.stderr, flush=True)
+
+    phases = None
+    if not args.no_trace:
+        words = layer.trace_words()
+        tr = torch.zeros(words, dtype=torch.int64, device=dev)
+        ev_tr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(M)]
+        one_update(ev_tr, trace=tr)
+        torch.cuda.synchronize()
+        layer.status()
+        phases = trace_mod.decode(tr.cpu().numpy(), layer.grid)
+        phases["traced_launch_ms"] = float(ev_tr[-1][0].elapsed_time(ev_tr[-1][1]))
+        print("# phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in phases["phase_us"].items())
+              + f"  barrier idle mean {phases['barrier_idle_frac_mean']:.3f}", file=sys.stderr, flush=True)
+
+    ab = algorithmic_bytes(cfg)
+    # the dominant (and only) kernel: one launch per microbatch
+    avg_launch_s = float(launch_ms.mean()) / 1e3
+    bytes_per_launch = ab["per_microbatch"] + ab["adamw"] / M
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "moe::moe_step_kernel (persistent, one launch per update)",
+                "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                "avg_launch_us": avg_launch_s * 1e6,
+                "gemm_tflops_effective": gemm_flops(cfg) / M / avg_launch_s / 1e12}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the FP64 oracle on the host ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, inp, args.cpu_budget)
+
+    layer.close()
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"MoE-FFN layer update {cfg.name}: {cfg.tokens}x{cfg.microbatches} tokens, "
+                               f"d_model={cfg.d_model}, d_ff={cfg.d_ff}, E={cfg.n_experts}, top-{cfg.top_k}",
+                   "tokens_per_update": cfg.tokens_in_update, "global_batch": cfg.tokens_in_update,
+                   "seq_len": 1024, "parallelism": "single-gpu"},
+        "ms_per_update_median": float(np.median(upd_ms)), "ms_per_update_p10": float(np.percentile(upd_ms, 10)),
+        "ms_per_update_p90": float(np.percentile(upd_ms, 90)),
+        "roofline": roofline, "cpu_baseline": cpu, "phases": phases,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

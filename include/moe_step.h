@@ -1,0 +1,168 @@
+/*
+ * moe_step.h -- C ABI of one training update of a top-k mixture-of-experts
+ * feed-forward layer, run as a single persistent HIP program on one MI355X
+ * (gfx950).
+ *
+ * What one update computes (Latch pages, "How a training megakernel works"):
+ *   "One training update": forward pass, loss, backward pass by the chain rule,
+ *   then a weight update;
+ *   "From two weights to 200 million": a router sends each token to k of E small
+ *   feed-forward networks; AdamW updates the weights from running averages of
+ *   the gradients and of their squares;
+ *   "What Latch does", steps 1, 3 and 4: the routing operations token_topk and
+ *   route_order, grouped expert products ragged_mm, global-norm clipping and
+ *   AdamW as tensor arithmetic; gradients return to the tokens routed through
+ *   each expert; FP32 master weights and Adam moments with BF16 matrix products;
+ *   "What Latch does", step 5: the whole update is one cooperative launch.
+ *
+ * Layer (readings where the pages are silent are stated in the design notes):
+ *   z = x W_r (+ b)                 router logits, fp32
+ *   sel_i = k largest z_i, descending, lower expert index first on ties
+ *   g_i = softmax over the k selected logits
+ *   y_i = sum_j g_ij * gelu_tanh(x_i W1[sel_ij]) W2[sel_ij]
+ *   L = sum_i ||y_i - t_i||^2 / (2 * tokens_in_update)
+ *   backward through everything except the choice of experts; dx included
+ *   c = min(1, clip_norm / (||grad|| + 1e-6)); AdamW with decoupled decay.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers in moe_step_io are DEVICE pointers on the handle's
+ *     device; the caller owns them and keeps them alive until the stream has
+ *     finished the launch.  Row-major, densely packed.
+ *   - Nothing throws.  Every function returns a moe_status (0 = success) except
+ *     the size queries and moe_step_last_error.
+ *   - Argument validation happens on the host before any HIP call.
+ */
+#ifndef MOE_STEP_H
+#define MOE_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_STEP_ABI_VERSION 1u
+
+typedef struct moe_step* moe_step_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,    /* NULL or out-of-range argument */
+  MOE_ERR_SHAPE = -2,  /* layer shape the kernels do not support */
+  MOE_ERR_HIP = -3,    /* a HIP runtime call failed (incl. no device) */
+  MOE_ERR_NOMEM = -4,  /* device allocation failed */
+  MOE_ERR_DEVICE = -5, /* the kernel reported an error (see last_error) */
+  MOE_ERR_STATE = -6   /* handle in a state that forbids the call */
+} moe_status;
+
+typedef enum {
+  MOE_DTYPE_F32 = 0,  /* x, t, activations and products in fp32 */
+  MOE_DTYPE_BF16 = 1  /* x, t, stored activations and GEMM operands in bf16;
+                         router, accumulation, grads, master weights fp32 */
+} moe_dtype;
+
+/* Layer and optimizer configuration, fixed for the life of a handle.
+ * Supported shapes: d_model and d_ff multiples of 8 (>= 8), 1 <= n_experts <= 64,
+ * 1 <= top_k <= min(8, n_experts), 1 <= max_tokens <= 2^24. */
+typedef struct {
+  uint32_t struct_size;   /* sizeof(moe_step_config) */
+  uint32_t abi_version;   /* MOE_STEP_ABI_VERSION */
+  int32_t d_model;        /* d */
+  int32_t d_ff;           /* f, expert hidden width */
+  int32_t n_experts;      /* E */
+  int32_t top_k;          /* k */
+  int32_t max_tokens;     /* largest n_tokens of any run; sizes the arena */
+  int32_t dtype;          /* moe_dtype */
+  double lr, beta1, beta2, adam_eps, weight_decay;  /* AdamW; the library derives
+                             1-beta and the bias corrections in double and
+                             rounds them to fp32 once */
+  double clip_norm;       /* global-norm clip; <= 0 disables clipping */
+  int32_t device;         /* HIP device ordinal */
+  int32_t wg_per_cu;      /* persistent workgroups per compute unit; 0 = 1 */
+} moe_step_config;
+
+/* Buffers of one launch.  Shapes use T = n_tokens, P = moe_step_param_count. */
+typedef struct {
+  const void* x;            /* [T, d] in dtype (fp32 or bf16)               */
+  const void* target;       /* [T, d] in dtype                               */
+  const float* router_bias; /* [E] constant logit bias, or NULL for none    */
+  float* params;            /* [P] fp32 master weights W_r[d,E] | W1[E,d,f] | W2[E,f,d];
+                               updated in place when MOE_RUN_APPLY is set    */
+  float* grads;             /* [P] fp32; written (MOE_RUN_ZERO_GRAD) or added to;
+                               holds the pre-clip gradient afterwards        */
+  float* exp_avg;           /* [P] fp32 first moment, updated on APPLY      */
+  float* exp_avg_sq;        /* [P] fp32 second moment, updated on APPLY     */
+  float* dx;                /* [T, d] fp32 input gradient, or NULL to skip it */
+  float* stats;             /* [4] fp32 or NULL: loss (set with ZERO_GRAD, else
+                               added to), grad norm, clip coefficient, unused */
+  /* optional debug outputs (NULL = not written): */
+  float* router_logits;     /* [T, E] fp32 (bias included)                   */
+  int32_t* topk_idx;        /* [T, k] selected experts, largest logit first  */
+  float* topk_gate;         /* [T, k] gates                                  */
+  int32_t* expert_counts;   /* [E] tokens routed to each expert              */
+  int32_t* route_perm;      /* [T*k] flat id i*k+j at each expert-sorted slot */
+  uint64_t* trace;          /* [moe_step_trace_words] per-workgroup phase clocks,
+                               written only with MOE_RUN_TRACE               */
+} moe_step_io;
+
+/* run_flags */
+#define MOE_RUN_ZERO_GRAD 0x1u      /* grads := this launch's gradient (else +=) */
+#define MOE_RUN_APPLY 0x2u          /* global-norm clip + AdamW after the backward */
+#define MOE_RUN_REFRESH_SHADOW 0x4u /* rebuild the bf16 weight copy from params
+                                       first (needed after create and whenever the
+                                       caller changed params itself) */
+#define MOE_RUN_TRACE 0x8u          /* record per-phase clocks into io.trace */
+
+/* Status-word bits reported by moe_step_status as MOE_ERR_DEVICE. */
+#define MOE_DEVICE_BARRIER_TIMEOUT 0x1u
+#define MOE_DEVICE_NONFINITE_LOGIT 0x2u
+#define MOE_DEVICE_BAD_ROUTE 0x4u        /* internal consistency check of the routing */
+
+/* Number of fp32 parameters P = d*E + 2*E*d*f (0 if cfg is NULL). Host only. */
+size_t moe_step_param_count(const moe_step_config* cfg);
+
+/* Host-only check of a configuration: MOE_OK, MOE_ERR_ARG or MOE_ERR_SHAPE.
+ * Makes no HIP call. */
+int moe_step_check_config(const moe_step_config* cfg);
+
+/* Creates a handle on cfg->device: validates cfg, allocates the device arena
+ * (routing structures, stored activations, bf16 weight copy, barrier words) and
+ * checks that the persistent grid fits co-resident.  Synchronous.
+ * On failure *out is set to NULL and the reason is available from
+ * moe_step_last_error(NULL). */
+int moe_step_create(const moe_step_config* cfg, moe_step_t* out);
+
+/* Enqueues one update on hip_stream (a hipStream_t; NULL = default stream):
+ * one cooperative launch of the persistent kernel.  Asynchronous.
+ * n_tokens in [0, max_tokens]; tokens_in_update >= max(1, n_tokens) is the loss
+ * denominator (the tokens of all microbatches of one update); step >= 1 is the
+ * 1-based AdamW step, used only with MOE_RUN_APPLY.
+ * Gradient accumulation over microbatches: ZERO_GRAD on the first, neither flag
+ * on the middle ones, APPLY on the last. */
+int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
+                 int64_t step, uint32_t run_flags, void* hip_stream);
+
+/* Waits for the handle's last stream and reads the device status word.
+ * Returns MOE_ERR_DEVICE (with the bits in last_error) if a kernel reported an
+ * error, after resetting the device-side barrier state. */
+int moe_step_status(moe_step_t h);
+
+/* Words of io.trace needed for MOE_RUN_TRACE: workgroups * phases * 3. */
+size_t moe_step_trace_words(moe_step_t h);
+
+/* Persistent workgroups of the handle's launches. */
+int moe_step_grid_size(moe_step_t h);
+
+/* Text of the last error on h (or of the last failed create if h is NULL).
+ * Valid until the next call on the same handle. Never NULL. */
+const char* moe_step_last_error(moe_step_t h);
+
+/* Waits for the last stream, frees the arena and the handle.  NULL-safe. */
+void moe_step_destroy(moe_step_t h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_STEP_H */

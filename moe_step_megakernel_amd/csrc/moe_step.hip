@@ -1,0 +1,431 @@
+// Host side of the C ABI declared in include/moe_step.h: validation, the device
+// arena, and one cooperative launch of the persistent kernel per update.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/moe_step.h"
+#include "phases.h"
+
+namespace {
+
+thread_local char g_create_error[512] = "no error";
+
+void set_err(char* buf, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, 512, fmt, ap);
+  va_end(ap);
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+int check_config(const moe_step_config* c, char* err) {
+  if (!c) { set_err(err, "config is NULL"); return MOE_ERR_ARG; }
+  if (c->struct_size != sizeof(moe_step_config)) {
+    set_err(err, "config.struct_size %u != %zu", c->struct_size, sizeof(moe_step_config));
+    return MOE_ERR_ARG;
+  }
+  if (c->abi_version != MOE_STEP_ABI_VERSION) {
+    set_err(err, "config.abi_version %u != %u", c->abi_version, MOE_STEP_ABI_VERSION);
+    return MOE_ERR_ARG;
+  }
+  if (c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->max_tokens <= 0) {
+    set_err(err, "dimensions must be positive (d=%d f=%d E=%d k=%d max_tokens=%d)", c->d_model, c->d_ff,
+            c->n_experts, c->top_k, c->max_tokens);
+    return MOE_ERR_ARG;
+  }
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) {
+    set_err(err, "unknown dtype %d", c->dtype);
+    return MOE_ERR_ARG;
+  }
+  if (!(c->lr >= 0.0) || !(c->beta1 >= 0.0 && c->beta1 < 1.0) || !(c->beta2 >= 0.0 && c->beta2 < 1.0) ||
+      !(c->adam_eps >= 0.0) || !(c->weight_decay >= 0.0) || std::isnan(c->clip_norm)) {
+    set_err(err, "optimizer hyper-parameters out of range");
+    return MOE_ERR_ARG;
+  }
+  if (c->wg_per_cu < 0 || c->wg_per_cu > 2) {
+    set_err(err, "wg_per_cu must be 0, 1 or 2");
+    return MOE_ERR_ARG;
+  }
+  if (c->top_k > c->n_experts) {
+    set_err(err, "top_k %d > n_experts %d", c->top_k, c->n_experts);
+    return MOE_ERR_ARG;
+  }
+  if (c->d_model % 8 || c->d_ff % 8) {
+    set_err(err, "d_model and d_ff must be multiples of 8 (got %d, %d)", c->d_model, c->d_ff);
+    return MOE_ERR_SHAPE;
+  }
+  if (c->n_experts > moe::kMaxExperts) {
+    set_err(err, "n_experts %d > %d", c->n_experts, moe::kMaxExperts);
+    return MOE_ERR_SHAPE;
+  }
+  if (c->top_k > moe::kMaxTopK) {
+    set_err(err, "top_k %d > %d", c->top_k, moe::kMaxTopK);
+    return MOE_ERR_SHAPE;
+  }
+  if (c->max_tokens > (1 << 24)) {
+    set_err(err, "max_tokens %d > 2^24", c->max_tokens);
+    return MOE_ERR_SHAPE;
+  }
+  const long long P = (long long)c->d_model * c->n_experts + 2LL * c->n_experts * c->d_model * c->d_ff;
+  if (P >= (1LL << 31) * 4LL) {
+    set_err(err, "too many parameters");
+    return MOE_ERR_SHAPE;
+  }
+  if ((long long)c->max_tokens * c->top_k * (long long)(c->d_model > c->d_ff ? c->d_model : c->d_ff) >=
+      (1LL << 40)) {
+    set_err(err, "activation arena too large");
+    return MOE_ERR_SHAPE;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+struct moe_step {
+  moe_step_config cfg;
+  int grid = 0;
+  int cus = 0;
+  char* arena = nullptr;
+  size_t arena_bytes = 0;
+  hipStream_t last_stream = nullptr;
+  bool launched = false;
+  char err[512] = "no error";
+  // arena sub-buffers
+  int* idx;
+  float* gate;
+  float* dzsel;
+  int* hist;
+  int* perm;
+  int* inv;
+  void* act;
+  void* gp;
+  float* out;
+  void* dout;
+  void* dh;
+  void* dxs;
+  float* wrt;
+  float* rpart;
+  float* loss_part;
+  float* norm_part;
+  uint16_t* shadow;
+  unsigned* ctrl;
+};
+
+extern "C" {
+
+size_t moe_step_param_count(const moe_step_config* c) {
+  if (!c) return 0;
+  return (size_t)c->d_model * c->n_experts + 2ull * c->n_experts * c->d_model * c->d_ff;
+}
+
+int moe_step_check_config(const moe_step_config* cfg) {
+  char err[512];
+  return check_config(cfg, err);
+}
+
+const char* moe_step_last_error(moe_step_t h) { return h ? h->err : g_create_error; }
+
+int moe_step_grid_size(moe_step_t h) { return h ? h->grid : 0; }
+
+size_t moe_step_trace_words(moe_step_t h) { return h ? (size_t)h->grid * moe::kPhases * 3 : 0; }
+
+int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
+  if (!out) {
+    set_err(g_create_error, "out is NULL");
+    return MOE_ERR_ARG;
+  }
+  *out = nullptr;
+  int rc = check_config(cfg, g_create_error);
+  if (rc != MOE_OK) return rc;
+
+  int ndev = 0;
+  hipError_t he = hipGetDeviceCount(&ndev);
+  if (he != hipSuccess || ndev <= 0) {
+    set_err(g_create_error, "no HIP device (%s)", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  if (cfg->device < 0 || cfg->device >= ndev) {
+    set_err(g_create_error, "device %d out of range (%d devices)", cfg->device, ndev);
+    return MOE_ERR_ARG;
+  }
+  if ((he = hipSetDevice(cfg->device)) != hipSuccess) {
+    set_err(g_create_error, "hipSetDevice: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  hipDeviceProp_t prop;
+  if ((he = hipGetDeviceProperties(&prop, cfg->device)) != hipSuccess) {
+    set_err(g_create_error, "hipGetDeviceProperties: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    set_err(g_create_error, "device %d is %s; this library is built for gfx950 only", cfg->device,
+            prop.gcnArchName);
+    return MOE_ERR_DEVICE;
+  }
+  if (!prop.cooperativeLaunch) {
+    set_err(g_create_error, "device does not support cooperative launches");
+    return MOE_ERR_DEVICE;
+  }
+
+  const void* kern = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t>)
+                                                  : reinterpret_cast<const void*>(&moe::moe_step_kernel<float>);
+  he = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, moe::kSmemBytes);
+  if (he != hipSuccess) {
+    set_err(g_create_error, "hipFuncSetAttribute(shared memory %d): %s", moe::kSmemBytes, hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  int per_cu = 0;
+  he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, moe::kThreads, moe::kSmemBytes);
+  if (he != hipSuccess || per_cu < 1) {
+    set_err(g_create_error, "occupancy query failed or zero (%s, %d)", hipGetErrorString(he), per_cu);
+    return MOE_ERR_HIP;
+  }
+  const int want = cfg->wg_per_cu == 0 ? 1 : cfg->wg_per_cu;
+  const int use = want < per_cu ? want : per_cu;
+
+  moe_step* h = new (std::nothrow) moe_step();
+  if (!h) {
+    set_err(g_create_error, "host allocation failed");
+    return MOE_ERR_NOMEM;
+  }
+  h->cfg = *cfg;
+  h->cus = prop.multiProcessorCount;
+  h->grid = h->cus * use;
+
+  const int d = cfg->d_model, f = cfg->d_ff, E = cfg->n_experts, k = cfg->top_k;
+  const size_t Tm = (size_t)cfg->max_tokens, N = Tm * k;
+  const size_t es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const int n10 = E * cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
+  const int n11 = E * cdiv(d, moe::gemm::BM) * cdiv(f, moe::gemm::BN);
+  const int nrr = cdiv(d * E, moe::kThreads);
+  const size_t rch = (size_t)cdiv(cfg->max_tokens, moe::kRouterTokens);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return o;
+  };
+  const size_t o_ctrl = take(4 * 128 * sizeof(unsigned));
+  const size_t o_idx = take(N * 4), o_gate = take(N * 4), o_dz = take(N * 4);
+  const size_t o_hist = take((size_t)h->grid * E * 4);
+  const size_t o_perm = take(N * 4), o_inv = take(N * 4);
+  const size_t o_act = take(N * f * es), o_gp = take(N * f * es);
+  const size_t o_out = take(N * d * 4), o_dout = take(N * d * es), o_dh = take(N * f * es);
+  const size_t o_dxs = take(N * d * es);
+  const size_t o_wrt = take((size_t)E * d * 4);
+  const size_t o_rpart = take(rch * E * d * 4);
+  const size_t o_loss = take((size_t)h->grid * 4);
+  const size_t o_norm = take((size_t)(n10 + n11 + nrr) * 4);
+  const size_t o_shadow = cfg->dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
+  h->arena_bytes = off;
+
+  he = hipMalloc(reinterpret_cast<void**>(&h->arena), h->arena_bytes);
+  if (he != hipSuccess) {
+    set_err(g_create_error, "hipMalloc(%zu bytes): %s", h->arena_bytes, hipGetErrorString(he));
+    delete h;
+    return MOE_ERR_NOMEM;
+  }
+  char* a = h->arena;
+  h->ctrl = reinterpret_cast<unsigned*>(a + o_ctrl);
+  h->idx = reinterpret_cast<int*>(a + o_idx);
+  h->gate = reinterpret_cast<float*>(a + o_gate);
+  h->dzsel = reinterpret_cast<float*>(a + o_dz);
+  h->hist = reinterpret_cast<int*>(a + o_hist);
+  h->perm = reinterpret_cast<int*>(a + o_perm);
+  h->inv = reinterpret_cast<int*>(a + o_inv);
+  h->act = a + o_act;
+  h->gp = a + o_gp;
+  h->out = reinterpret_cast<float*>(a + o_out);
+  h->dout = a + o_dout;
+  h->dh = a + o_dh;
+  h->dxs = a + o_dxs;
+  h->wrt = reinterpret_cast<float*>(a + o_wrt);
+  h->rpart = reinterpret_cast<float*>(a + o_rpart);
+  h->loss_part = reinterpret_cast<float*>(a + o_loss);
+  h->norm_part = reinterpret_cast<float*>(a + o_norm);
+  h->shadow = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a + o_shadow) : nullptr;
+
+  // barrier words and status start at zero (synchronous; not part of any run)
+  he = hipMemset(h->ctrl, 0, 4 * 128 * sizeof(unsigned));
+  if (he == hipSuccess) he = hipDeviceSynchronize();
+  if (he != hipSuccess) {
+    set_err(g_create_error, "clearing barrier words: %s", hipGetErrorString(he));
+    (void)hipFree(h->arena);
+    delete h;
+    return MOE_ERR_HIP;
+  }
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update, int64_t step,
+                 uint32_t run_flags, void* hip_stream) {
+  if (!h) return MOE_ERR_ARG;
+  if (!io) {
+    set_err(h->err, "io is NULL");
+    return MOE_ERR_ARG;
+  }
+  const moe_step_config& c = h->cfg;
+  if (n_tokens < 0 || n_tokens > c.max_tokens) {
+    set_err(h->err, "n_tokens %d outside [0, max_tokens=%d]", n_tokens, c.max_tokens);
+    return MOE_ERR_ARG;
+  }
+  if (tokens_in_update < 1 || tokens_in_update < n_tokens) {
+    set_err(h->err, "tokens_in_update %lld must be >= max(1, n_tokens)", (long long)tokens_in_update);
+    return MOE_ERR_ARG;
+  }
+  if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE)) {
+    set_err(h->err, "unknown run flags 0x%x", run_flags);
+    return MOE_ERR_ARG;
+  }
+  if ((run_flags & MOE_RUN_APPLY) && step < 1) {
+    set_err(h->err, "step must be >= 1 with MOE_RUN_APPLY (got %lld)", (long long)step);
+    return MOE_ERR_ARG;
+  }
+  if (n_tokens > 0 && (!io->x || !io->target)) {
+    set_err(h->err, "x and target are required");
+    return MOE_ERR_ARG;
+  }
+  if (!io->params || !io->grads) {
+    set_err(h->err, "params and grads are required");
+    return MOE_ERR_ARG;
+  }
+  if ((run_flags & MOE_RUN_APPLY) && (!io->exp_avg || !io->exp_avg_sq)) {
+    set_err(h->err, "exp_avg and exp_avg_sq are required with MOE_RUN_APPLY");
+    return MOE_ERR_ARG;
+  }
+  if ((run_flags & MOE_RUN_TRACE) && !io->trace) {
+    set_err(h->err, "MOE_RUN_TRACE needs io.trace");
+    return MOE_ERR_ARG;
+  }
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(io->x) | reinterpret_cast<uintptr_t>(io->target) |
+                        reinterpret_cast<uintptr_t>(io->params) | reinterpret_cast<uintptr_t>(io->grads) |
+                        reinterpret_cast<uintptr_t>(io->exp_avg) | reinterpret_cast<uintptr_t>(io->exp_avg_sq) |
+                        reinterpret_cast<uintptr_t>(io->dx);
+  if (mis & 15u) {
+    set_err(h->err, "x, target, params, grads, exp_avg, exp_avg_sq and dx must be 16-byte aligned");
+    return MOE_ERR_ARG;
+  }
+
+  moe::KParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.T = n_tokens;
+  p.d = c.d_model;
+  p.f = c.d_ff;
+  p.E = c.n_experts;
+  p.k = c.top_k;
+  p.inv_tupd = (float)(1.0 / (double)tokens_in_update);
+  p.flags = run_flags;
+  if (!h->shadow) p.flags &= ~MOE_RUN_REFRESH_SHADOW;
+  p.lr = (float)c.lr;
+  p.beta1 = (float)c.beta1;
+  p.beta2 = (float)c.beta2;
+  p.omb1 = (float)(1.0 - c.beta1);
+  p.omb2 = (float)(1.0 - c.beta2);
+  p.eps = (float)c.adam_eps;
+  p.wd = (float)c.weight_decay;
+  p.clip = (float)c.clip_norm;
+  const double s = step >= 1 ? (double)step : 1.0;
+  const double bc1 = 1.0 - std::pow(c.beta1, s), bc2 = 1.0 - std::pow(c.beta2, s);
+  p.inv_bc1 = bc1 > 0.0 ? (float)(1.0 / bc1) : 1.f;
+  p.inv_sqrt_bc2 = bc2 > 0.0 ? (float)(1.0 / std::sqrt(bc2)) : 1.f;
+  p.x = io->x;
+  p.t = io->target;
+  p.bias = io->router_bias;
+  p.params = io->params;
+  p.grads = io->grads;
+  p.m = io->exp_avg;
+  p.v = io->exp_avg_sq;
+  p.dx = io->dx;
+  p.stats = io->stats;
+  p.dbg_logits = io->router_logits;
+  p.dbg_idx = io->topk_idx;
+  p.dbg_gate = io->topk_gate;
+  p.dbg_counts = io->expert_counts;
+  p.dbg_perm = io->route_perm;
+  p.trace = io->trace;
+  p.idx = h->idx;
+  p.gate = h->gate;
+  p.dzsel = h->dzsel;
+  p.hist = h->hist;
+  p.perm = h->perm;
+  p.inv = h->inv;
+  p.act = h->act;
+  p.gp = h->gp;
+  p.out = h->out;
+  p.dout = h->dout;
+  p.dh = h->dh;
+  p.dxs = h->dxs;
+  p.wrt = h->wrt;
+  p.rpart = h->rpart;
+  p.loss_part = h->loss_part;
+  p.norm_part = h->norm_part;
+  p.shadow = h->shadow;
+  p.ctrl.count = h->ctrl;
+  p.ctrl.gen = h->ctrl + 32;
+  p.ctrl.status = h->ctrl + 64;
+  p.ctrl.abort = h->ctrl + 96;
+
+  hipError_t he = hipSetDevice(c.device);
+  if (he != hipSuccess) {
+    set_err(h->err, "hipSetDevice: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  void* args[] = {&p};
+  const void* kern = c.dtype == MOE_DTYPE_BF16 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t>)
+                                               : reinterpret_cast<const void*>(&moe::moe_step_kernel<float>);
+  he = hipLaunchCooperativeKernel(kern, dim3(h->grid), dim3(moe::kThreads), args, moe::kSmemBytes, stream);
+  if (he != hipSuccess) {
+    set_err(h->err, "hipLaunchCooperativeKernel: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  h->last_stream = stream;
+  h->launched = true;
+  return MOE_OK;
+}
+
+int moe_step_status(moe_step_t h) {
+  if (!h) return MOE_ERR_ARG;
+  hipError_t he = hipSetDevice(h->cfg.device);
+  if (he == hipSuccess && h->launched) he = hipStreamSynchronize(h->last_stream);
+  if (he != hipSuccess) {
+    set_err(h->err, "waiting for the stream: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  unsigned st = 0;
+  he = hipMemcpy(&st, h->ctrl + 64, sizeof(unsigned), hipMemcpyDeviceToHost);
+  if (he != hipSuccess) {
+    set_err(h->err, "reading the status word: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  if (st != 0u) {
+    set_err(h->err, "device error 0x%x:%s%s%s", st, (st & MOE_DEVICE_BARRIER_TIMEOUT) ? " grid-barrier timeout" : "",
+            (st & MOE_DEVICE_NONFINITE_LOGIT) ? " non-finite router logit" : "",
+            (st & MOE_DEVICE_BAD_ROUTE) ? " expert index out of range" : "");
+    he = hipMemset(h->ctrl, 0, 4 * 128 * sizeof(unsigned));
+    if (he == hipSuccess) he = hipDeviceSynchronize();
+    return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
+}
+
+void moe_step_destroy(moe_step_t h) {
+  if (!h) return;
+  if (hipSetDevice(h->cfg.device) == hipSuccess) {
+    if (h->launched) (void)hipStreamSynchronize(h->last_stream);
+    if (h->arena) (void)hipFree(h->arena);
+  }
+  delete h;
+}
+
+}  // extern "C"

@@ -1,0 +1,842 @@
+// The phases of one MoE-layer training update, as device functions of the
+// persistent kernel.  Each phase is spread over every workgroup; phases that
+// read results produced on other compute units are separated by a grid barrier
+// (Latch pages, "What Latch does", step 4: phases across all SMs, a grid-wide
+// barrier where results cross SMs, values between phases in a planned arena).
+//
+//   P0  bf16 weight copy refresh (optional); copy of W_r^T;
+//       router logits, token_topk, gates, per-workgroup expert histogram
+//   P1  route_order: global offsets, stable scatter into perm / inv
+//   P2  ragged_mm 1 + GELU        A = gelu(X_e W1[e]),  G' = gelu'(X_e W1[e])
+//   P3  ragged_mm 2               O = A_e W2[e]
+//   P4  weighted combine, loss, dL/dO, dL/dgate, dL/dlogit
+//   P5  dH = (dO W2[e]^T) * G';  dW2[e] = A_e^T dO;  router-gradient partials
+//   P6  dW1[e] = X_e^T dH;  dXs = dH W1[e]^T;  router gradient (fixed-order sum)
+//   P7  dx = router part + the k expert contributions of each token, in order;
+//       global norm from the per-tile partials (fixed order); clip + AdamW
+#pragma once
+
+#include "device_common.h"
+#include "ragged_gemm.h"
+
+namespace moe {
+
+constexpr int kPhases = 8;
+constexpr int kMetaBytes = 2048;
+constexpr int kScratchBytes = gemm::LDS_BYTES;
+constexpr int kSmemBytes = kMetaBytes + kScratchBytes;
+constexpr int kRouterTokens = 256;   // tokens per router-gradient partial
+constexpr int kRouterBlockTokens = 32;
+
+// Routing metadata kept in LDS for the whole launch (every workgroup computes
+// it in P1 from the global histogram).
+struct Meta {
+  int cnt[kMaxExperts];         // routed rows per expert
+  int off[kMaxExperts + 1];     // first sorted position of each expert
+  int moff[kMaxExperts + 1];    // first 128-row tile of each expert
+  float red[8];                 // block reductions
+  unsigned flag;                // barrier result broadcast
+};
+static_assert(sizeof(Meta) <= kMetaBytes, "meta");
+
+struct KParams {
+  // shape of this launch
+  int T, d, f, E, k;
+  float inv_tupd;     // 1 / tokens_in_update
+  unsigned flags;
+  // optimizer
+  float lr, beta1, beta2, omb1, omb2, eps, wd, clip, inv_bc1, inv_sqrt_bc2;
+  // caller buffers
+  const void* x;
+  const void* t;
+  const float* bias;
+  float* params;
+  float* grads;
+  float* m;
+  float* v;
+  float* dx;
+  float* stats;
+  float* dbg_logits;
+  int* dbg_idx;
+  float* dbg_gate;
+  int* dbg_counts;
+  int* dbg_perm;
+  uint64_t* trace;
+  // arena
+  int* idx;        // [T*k] expert of flat id i*k+j
+  float* gate;     // [T*k]
+  float* dzsel;    // [T*k] dL/dlogit of the selected experts
+  int* hist;       // [G][E]
+  int* perm;       // [T*k] sorted position -> flat id
+  int* inv;        // [T*k] flat id -> sorted position
+  void* act;       // [N, f] gelu(H)            (T-typed)
+  void* gp;        // [N, f] gelu'(H)           (T-typed)
+  float* out;      // [N, d] expert outputs O
+  void* dout;      // [N, d] dL/dO              (T-typed)
+  void* dh;        // [N, f] dL/dH              (T-typed)
+  void* dxs;       // [T*k, d] per-(token, slot) input gradient (T-typed)
+  float* wrt;      // [E, d] W_r^T as it was before this update
+  float* rpart;    // [ceil(T/256)][E][d] router-gradient partials
+  float* loss_part;  // [G]
+  float* norm_part;  // [n10 + n11 + nr]
+  uint16_t* shadow;  // [2*E*d*f] bf16 copy of W1 | W2 (bf16 mode)
+  Ctrl ctrl;
+};
+
+__device__ __forceinline__ int logical_wg() {
+  // Workgroups are dealt to the 8 XCDs round-robin; renumber so that
+  // consecutive logical indices sit on the same XCD and share its L2.
+  const int G = gridDim.x, b = blockIdx.x;
+  if ((G & 7) != 0) return b;
+  return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot) {
+  if ((p.flags & 0x8u) && p.trace && threadIdx.x == 0)
+    p.trace[((size_t)blockIdx.x * kPhases + phase) * 3 + slot] = wall_clock64();
+}
+
+// ===========================================================================
+// P0: weight-copy refresh, W_r^T, router logits + token_topk + gates + histogram
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& meta) {
+  const int tid = threadIdx.x;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, E = p.E, k = p.k;
+
+  // bf16 copy of W1 | W2 from the fp32 master weights
+  if ((p.flags & 0x4u) && p.shadow) {
+    const long nw = 2L * E * d * p.f;
+    const float* src = p.params + (long)d * E;
+    for (long i = ((long)lwg * kThreads + tid) * 8; i < nw; i += (long)G * kThreads * 8)
+      st8(p.shadow + i, ld8(src + i));
+  }
+  // W_r^T, read by the input-gradient phase after AdamW may have changed W_r
+  for (int i = lwg * kThreads + tid; i < d * E; i += G * kThreads) {
+    const int c = i / E, e = i % E;
+    p.wrt[(long)e * d + c] = p.params[i];
+  }
+
+  int* hist = reinterpret_cast<int*>(smem);                  // [E]
+  float* zacc = reinterpret_cast<float*>(smem + 256);        // [32][EP]
+  int EP = 1;
+  while (EP < E) EP <<= 1;
+  const int TPI = kThreads / EP;          // tokens per pass
+  // chunk of d so that the padded W_r^T and x chunks each fit in 32 KB
+  int DC = min(d, min(8192 / E - 4, 32 * EP - 4));
+  DC &= ~7;
+  const int LDW = DC + 4;
+  float* ws = reinterpret_cast<float*>(smem + 256 + kRouterBlockTokens * kMaxExperts * 4);  // [E][LDW]
+  float* xs = ws + E * LDW;                                                               // [TPI][LDW]
+
+  const int per = ceil_div(p.T, G);
+  const int t_lo = min(p.T, lwg * per), t_hi = min(p.T, t_lo + per);
+  if (tid < kMaxExperts) hist[tid] = 0;
+  const int e_me = tid % EP, slot = tid / EP;
+  const T* x = reinterpret_cast<const T*>(p.x);
+
+  for (int b0 = t_lo; b0 < t_hi; b0 += kRouterBlockTokens) {
+    const int nb = min(kRouterBlockTokens, t_hi - b0);
+    __syncthreads();
+    for (int i = tid; i < kRouterBlockTokens * EP; i += kThreads) zacc[i] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += DC) {
+      const int dc = min(DC, d - c0);
+      __syncthreads();
+      for (int i = tid; i < E * dc; i += kThreads) {
+        const int c = i / E, e = i % E;
+        ws[e * LDW + c] = p.params[(long)(c0 + c) * E + e];
+      }
+      for (int g0 = 0; g0 < nb; g0 += TPI) {
+        __syncthreads();
+        const int ng = min(TPI, nb - g0);
+        for (int i = tid * 8; i < ng * dc; i += kThreads * 8) {
+          const int tk = i / dc, c = i % dc;
+          F8 v = ld8(x + (long)(b0 + g0 + tk) * d + c0 + c);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) xs[tk * LDW + c + q] = v.v[q];
+        }
+        __syncthreads();
+        if (slot < ng && e_me < E) {
+          float s = 0.f;
+          const float4* wr = reinterpret_cast<const float4*>(ws + e_me * LDW);
+          const float4* xr = reinterpret_cast<const float4*>(xs + slot * LDW);
+          for (int c = 0; c < dc / 4; ++c) {
+            const float4 a = wr[c], b = xr[c];
+            s += a.x * b.x;
+            s += a.y * b.y;
+            s += a.z * b.z;
+            s += a.w * b.w;
+          }
+          zacc[(g0 + slot) * EP + e_me] += s;
+        }
+      }
+    }
+    __syncthreads();
+    // token_topk over each group of EP lanes (the group never crosses a wave)
+    for (int g0 = 0; g0 < nb; g0 += TPI) {
+      const int tok = b0 + g0 + slot;
+      const bool live = (g0 + slot) < nb;
+      float z = -INFINITY;
+      bool active = false;
+      if (live && e_me < E) {
+        z = zacc[(g0 + slot) * EP + e_me];
+        if (p.bias) z += p.bias[e_me];
+        if (p.dbg_logits) p.dbg_logits[(long)tok * E + e_me] = z;
+        if (!(z == z) || z == INFINITY || z == -INFINITY) {   // NaN or infinite: device error
+          __hip_atomic_fetch_or(p.ctrl.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          z = -INFINITY;
+        }
+        active = true;
+      }
+      float zsel[kMaxTopK];
+      int esel[kMaxTopK];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        zsel[j] = 0.f;
+        esel[j] = 0;
+        if (j < k) {
+          // best = (active, larger z, lower index)
+          float bv = z;
+          int be = active ? e_me : 0x7fffffff;
+          for (int m = EP >> 1; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, 64);
+            const int oe = __shfl_xor(be, m, 64);
+            const bool o_act = oe != 0x7fffffff, me_act = be != 0x7fffffff;
+            const bool take = o_act && (!me_act || ov > bv || (ov == bv && oe < be));
+            if (take) { bv = ov; be = oe; }
+          }
+          zsel[j] = bv;
+          esel[j] = be;
+          if (be == e_me) active = false;
+        }
+      }
+      if (live) {
+        float den = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+          if (j < k) den += expf(zsel[j] - zsel[0]);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j < k && e_me == j) {
+            const float gj = expf(zsel[j] - zsel[0]) / den;
+            const int q = tok * k + j;
+            int ej = esel[j];
+            if ((unsigned)ej >= (unsigned)E) {   // cannot happen; keeps every later index in range
+              __hip_atomic_fetch_or(p.ctrl.status, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              ej = 0;
+            }
+            p.idx[q] = ej;
+            p.gate[q] = gj;
+            if (p.dbg_idx) p.dbg_idx[q] = ej;
+            if (p.dbg_gate) p.dbg_gate[q] = gj;
+            atomicAdd(&hist[ej], 1);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < E) p.hist[(long)lwg * E + tid] = hist[tid];
+}
+
+// ===========================================================================
+// P1: route_order -- offsets and a stable scatter of the flat ids by expert
+// ===========================================================================
+__device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& meta) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int E = p.E, k = p.k;
+  int EP = 1, EB = 0;
+  while (EP < E) { EP <<= 1; ++EB; }
+  const int parts = kThreads / EP;
+
+  int* sp = reinterpret_cast<int*>(smem);             // [parts][EP] prefix (w < lwg)
+  int* st = sp + kThreads;                            // [parts][EP] totals
+  int* base = st + kThreads;                          // [EP]
+  int* cw = base + kMaxExperts;                       // [kWaves][EP]
+  {
+    const int e = tid % EP, part = tid / EP;
+    int pre = 0, tot = 0;
+    if (e < E) {
+      for (int w = part; w < G; w += parts) {
+        const int h = p.hist[(long)w * E + e];
+        tot += h;
+        if (w < lwg) pre += h;
+      }
+    }
+    sp[tid] = pre;
+    st[tid] = tot;
+  }
+  __syncthreads();
+  if (tid < EP) {
+    int pre = 0, tot = 0;
+    for (int q = 0; q < parts; ++q) {
+      pre += sp[q * EP + tid];
+      tot += st[q * EP + tid];
+    }
+    sp[tid] = pre;       // reuse row 0
+    st[tid] = tot;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, mo = 0;
+    for (int e = 0; e < E; ++e) {
+      meta.cnt[e] = st[e];
+      meta.off[e] = o;
+      meta.moff[e] = mo;
+      o += st[e];
+      mo += ceil_div(st[e], gemm::BM);
+    }
+    meta.off[E] = o;
+    meta.moff[E] = mo;
+  }
+  __syncthreads();
+  if (tid < E) base[tid] = meta.off[tid] + sp[tid];
+  if (lwg == 0 && tid < E && p.dbg_counts) p.dbg_counts[tid] = meta.cnt[tid];
+
+  const int per = ceil_div(p.T, G);
+  const int t_lo = min(p.T, lwg * per), t_hi = min(p.T, t_lo + per);
+  const int q_lo = t_lo * k, q_hi = t_hi * k;
+  for (int q0 = q_lo; q0 < q_hi; q0 += kThreads) {
+    __syncthreads();
+    for (int i = tid; i < kWaves * EP; i += kThreads) cw[i] = 0;
+    __syncthreads();
+    const int q = q0 + tid;
+    const bool valid = q < q_hi;
+    const int e = valid ? p.idx[q] : 0;
+    unsigned long long mask = __ballot(valid);
+    for (int b = 0; b < EB; ++b) {
+      const unsigned long long bb = __ballot(valid && ((e >> b) & 1));
+      mask &= ((e >> b) & 1) ? bb : ~bb;
+    }
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(mask & lt);
+    if (valid && (mask >> lane) == 1ull) cw[wave * EP + e] = __popcll(mask);   // highest lane of its group
+    __syncthreads();
+    if (valid) {
+      int pos = base[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += cw[w * EP + e];
+      p.perm[pos] = q;
+      p.inv[q] = pos;
+      if (p.dbg_perm) p.dbg_perm[pos] = q;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int s = 0;
+      for (int w = 0; w < kWaves; ++w) s += cw[w * EP + tid];
+      base[tid] += s;
+    }
+  }
+}
+
+// Expert owning global row-tile mg (moff is ascending).
+__device__ __forceinline__ int expert_of_tile(const Meta& meta, int E, int mg) {
+  int e = 0;
+  while (e + 1 < E && meta.moff[e + 1] <= mg) ++e;
+  return e;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* w1_ptr(const KParams& p) {
+  if constexpr (sizeof(T) == 2) return reinterpret_cast<const T*>(p.shadow);
+  else return reinterpret_cast<const T*>(p.params + (long)p.d * p.E);
+}
+template <typename T>
+__device__ __forceinline__ const T* w2_ptr(const KParams& p) {
+  return w1_ptr<T>(p) + (long)p.E * p.d * p.f;
+}
+
+// ===========================================================================
+// P2: ragged_mm 1 + GELU.  Rows of expert e: x[perm[p]/k], p in its segment.
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Meta& meta) {
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, f = p.f;
+  const int NT = ceil_div(f, gemm::BN);
+  const int ntiles = meta.moff[p.E] * NT;
+  T* act = reinterpret_cast<T*>(p.act);
+  T* gp = reinterpret_cast<T*>(p.gp);
+  for (int tI = lwg; tI < ntiles; tI += G) {
+    const int mg = tI / NT, nt = tI % NT;
+    const int e = expert_of_tile(meta, p.E, mg);
+    const int m0 = (mg - meta.moff[e]) * gemm::BM;
+    const int p0 = meta.off[e] + m0;
+    const int mrows = min(gemm::BM, meta.cnt[e] - m0);
+    gemm::Operand A{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, p0, mrows, d, 0};
+    gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1, 0, d, f,
+                    nt * gemm::BN};
+    const int n0 = nt * gemm::BN;
+    gemm::tile<T, false, true>(lds, A, B, d, [&](int r, int c, float h) {
+      if (r < mrows && n0 + c < f) {
+        float a, da;
+        gelu_and_grad(h, a, da);
+        const long o = (long)(p0 + r) * f + n0 + c;
+        store_elem(act + o, a);
+        store_elem(gp + o, da);
+      }
+    });
+  }
+}
+
+// ===========================================================================
+// P3: ragged_mm 2:  O = A_e W2[e]
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Meta& meta) {
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, f = p.f;
+  const int NT = ceil_div(d, gemm::BN);
+  const int ntiles = meta.moff[p.E] * NT;
+  for (int tI = lwg; tI < ntiles; tI += G) {
+    const int mg = tI / NT, nt = tI % NT;
+    const int e = expert_of_tile(meta, p.E, mg);
+    const int m0 = (mg - meta.moff[e]) * gemm::BM;
+    const int p0 = meta.off[e] + m0;
+    const int mrows = min(gemm::BM, meta.cnt[e] - m0);
+    gemm::Operand A{reinterpret_cast<const char*>(p.act), f, nullptr, 1, p0, mrows, f, 0};
+    gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1, 0, f, d,
+                    nt * gemm::BN};
+    const int n0 = nt * gemm::BN;
+    gemm::tile<T, false, true>(lds, A, B, f, [&](int r, int c, float v) {
+      if (r < mrows && n0 + c < d) p.out[(long)(p0 + r) * d + n0 + c] = v;
+    });
+  }
+}
+
+// ===========================================================================
+// P4: combine, loss, dL/dO, dL/dgate -> dL/dlogit (one wave per token)
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, k = p.k;
+  const T* tg = reinterpret_cast<const T*>(p.t);
+  T* dout = reinterpret_cast<T*>(p.dout);
+  float lsum = 0.f;
+  for (int tok = lwg * kWaves + wave; tok < p.T; tok += G * kWaves) {
+    float g[kMaxTopK], dg[kMaxTopK];
+    int pos[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      g[j] = 0.f;
+      dg[j] = 0.f;
+      pos[j] = 0;
+      if (j < k) {
+        g[j] = p.gate[tok * k + j];
+        pos[j] = p.inv[tok * k + j];
+      }
+    }
+    for (int c = lane * 8; c < d; c += 64 * 8) {
+      const F8 tv = ld8(tg + (long)tok * d + c);
+      F8 o[kMaxTopK];
+      F8 y;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y.v[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          o[j] = ld8(p.out + (long)pos[j] * d + c);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) y.v[q] += g[j] * o[j].v[q];
+        }
+      }
+      F8 dy;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float r = y.v[q] - tv.v[q];
+        lsum += r * r;
+        dy.v[q] = r * p.inv_tupd;
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          F8 w;
+          float s = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            w.v[q] = g[j] * dy.v[q];
+            s += dy.v[q] * o[j].v[q];
+          }
+          dg[j] += s;
+          st8(dout + (long)pos[j] * d + c, w);
+        }
+      }
+    }
+    float sg = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        dg[j] = wave_sum(dg[j]);
+        sg += g[j] * dg[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k && lane == j) p.dzsel[tok * k + j] = g[j] * (dg[j] - sg);
+  }
+  const float s = block_sum(lsum, meta.red);
+  if (tid == 0) p.loss_part[lwg] = s;
+}
+
+// ===========================================================================
+// P5: dH = (dO W2[e]^T) * G' ; dW2[e] = A_e^T dO ; router-gradient partials
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_grad) {
+  const int tid = threadIdx.x;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, f = p.f, E = p.E, k = p.k;
+  const int NTf = ceil_div(f, gemm::BN);
+  const int n9 = meta.moff[E] * NTf;
+  const int MT10 = ceil_div(f, gemm::BM), NT10 = ceil_div(d, gemm::BN);
+  const int n10 = E * MT10 * NT10;
+  const int RCH = ceil_div(p.T, kRouterTokens), CCH = ceil_div(d, kThreads);
+  const int nr = RCH * CCH;
+  const T* gp = reinterpret_cast<const T*>(p.gp);
+  T* dh = reinterpret_cast<T*>(p.dh);
+  float* gw2 = p.grads + (long)d * E + (long)E * d * f;
+  const T* x = reinterpret_cast<const T*>(p.x);
+
+  for (int item = lwg; item < n10 + n9 + nr; item += G) {
+    if (item < n10) {
+      // dW2[e] (f x d) = A_e^T dO_e, contraction over the expert's rows
+      const int e = item / (MT10 * NT10), rem = item % (MT10 * NT10);
+      const int mt = rem / NT10, nt = rem % NT10;
+      const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
+      const int pe = meta.off[e], ce = meta.cnt[e];
+      gemm::Operand A{reinterpret_cast<const char*>(p.act), f, nullptr, 1, pe, ce, f, m0};
+      gemm::Operand B{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, pe, ce, d, n0};
+      float* g = gw2 + (long)e * f * d;
+      float sq = 0.f;
+      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, float v) {
+        if (m0 + r < f && n0 + c < d) {
+          float* q = g + (long)(m0 + r) * d + n0 + c;
+          const float nv = zero_grad ? v : *q + v;
+          *q = nv;
+          sq += nv * nv;
+        }
+      });
+      const float s = block_sum(sq, meta.red);
+      if (tid == 0) p.norm_part[item] = s;
+    } else if (item < n10 + n9) {
+      const int tI = item - n10;
+      const int mg = tI / NTf, nt = tI % NTf;
+      const int e = expert_of_tile(meta, E, mg);
+      const int m0 = (mg - meta.moff[e]) * gemm::BM;
+      const int p0 = meta.off[e] + m0;
+      const int mrows = min(gemm::BM, meta.cnt[e] - m0);
+      // B[k = d][n = f] = W2[e][n][k]: rows of W2[e] run along k -> direct
+      gemm::Operand A{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, p0, mrows, d, 0};
+      gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1,
+                      nt * gemm::BN, min(gemm::BN, f - nt * gemm::BN), d, 0};
+      const int n0 = nt * gemm::BN;
+      gemm::tile<T, false, false>(lds, A, B, d, [&](int r, int c, float v) {
+        if (r < mrows && n0 + c < f) {
+          const long o = (long)(p0 + r) * f + n0 + c;
+          store_elem(dh + o, v * to_f32(gp[o]));
+        }
+      });
+    } else {
+      // router-gradient partial: tokens [rc*256, +256) x columns [cc*256, +256)
+      const int ir = item - n10 - n9;
+      const int rc = ir / CCH, cc = ir % CCH;
+      float* acc = reinterpret_cast<float*>(lds);                      // [E][256]
+      int* se = reinterpret_cast<int*>(acc + E * kThreads);            // [64*k] experts
+      float* sz = reinterpret_cast<float*>(se + 64 * kMaxTopK);        // [64*k] dL/dlogit
+      const int t0 = rc * kRouterTokens, t1 = min(p.T, t0 + kRouterTokens);
+      const int c = cc * kThreads + tid;
+      __syncthreads();
+      for (int i = tid; i < E * kThreads; i += kThreads) acc[i] = 0.f;
+      for (int s0 = t0; s0 < t1; s0 += 64) {
+        const int s1 = min(t1, s0 + 64);
+        __syncthreads();
+        for (int i = tid; i < (s1 - s0) * k; i += kThreads) {
+          se[i] = p.idx[s0 * k + i];
+          sz[i] = p.dzsel[s0 * k + i];
+        }
+        __syncthreads();
+        if (c < d) {
+          constexpr int U = 8;
+          int tok = s0;
+          for (; tok + U <= s1; tok += U) {
+            float xv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) xv[u] = to_f32(x[(long)(tok + u) * d + c]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              for (int j = 0; j < k; ++j) {
+                const int q = (tok + u - s0) * k + j;
+                acc[se[q] * kThreads + tid] += xv[u] * sz[q];
+              }
+          }
+          for (; tok < s1; ++tok) {
+            const float xv = to_f32(x[(long)tok * d + c]);
+            for (int j = 0; j < k; ++j) {
+              const int q = (tok - s0) * k + j;
+              acc[se[q] * kThreads + tid] += xv * sz[q];
+            }
+          }
+        }
+      }
+      if (c < d) {
+        for (int e = 0; e < E; ++e) p.rpart[((long)rc * E + e) * d + c] = acc[e * kThreads + tid];
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// P6: dW1[e] = X_e^T dH ; dXs = dH W1[e]^T ; router gradient reduction
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& meta, bool zero_grad, bool want_dx) {
+  const int tid = threadIdx.x;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, f = p.f, E = p.E;
+  const int MT11 = ceil_div(d, gemm::BM), NT11 = ceil_div(f, gemm::BN);
+  const int n11 = E * MT11 * NT11;
+  const int NTd = ceil_div(d, gemm::BN);
+  const int n12 = want_dx ? meta.moff[E] * NTd : 0;
+  const int nrr = ceil_div(d * E, kThreads);
+  const int n10 = E * ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
+  const int RCH = ceil_div(p.T, kRouterTokens);
+  float* gw1 = p.grads + (long)d * E;
+  T* dxs = reinterpret_cast<T*>(p.dxs);
+
+  for (int item = lwg; item < n11 + n12 + nrr; item += G) {
+    if (item < n11) {
+      // dW1[e] (d x f) = X_e^T dH_e; X_e rows gathered from x through perm
+      const int e = item / (MT11 * NT11), rem = item % (MT11 * NT11);
+      const int mt = rem / NT11, nt = rem % NT11;
+      const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
+      const int pe = meta.off[e], ce = meta.cnt[e];
+      gemm::Operand A{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, pe, ce, d, m0};
+      gemm::Operand B{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, pe, ce, f, n0};
+      float* g = gw1 + (long)e * d * f;
+      float sq = 0.f;
+      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, float v) {
+        if (m0 + r < d && n0 + c < f) {
+          float* q = g + (long)(m0 + r) * f + n0 + c;
+          const float nv = zero_grad ? v : *q + v;
+          *q = nv;
+          sq += nv * nv;
+        }
+      });
+      const float s = block_sum(sq, meta.red);
+      if (tid == 0) p.norm_part[n10 + item] = s;
+    } else if (item < n11 + n12) {
+      const int tI = item - n11;
+      const int mg = tI / NTd, nt = tI % NTd;
+      const int e = expert_of_tile(meta, E, mg);
+      const int m0 = (mg - meta.moff[e]) * gemm::BM;
+      const int p0 = meta.off[e] + m0;
+      const int mrows = min(gemm::BM, meta.cnt[e] - m0);
+      // B[k = f][n = d] = W1[e][n][k]: rows of W1[e] run along k -> direct
+      gemm::Operand A{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, p0, mrows, f, 0};
+      gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1,
+                      nt * gemm::BN, min(gemm::BN, d - nt * gemm::BN), f, 0};
+      const int n0 = nt * gemm::BN;
+      gemm::tile<T, false, false>(lds, A, B, f, [&](int r, int c, float v) {
+        if (r < mrows && n0 + c < d) store_elem(dxs + (long)p.perm[p0 + r] * d + n0 + c, v);
+      });
+    } else {
+      // dW_r[c][e] = sum over token chunks (ascending) of the partials
+      const int ir = item - n11 - n12;
+      const int o = ir * kThreads + tid;
+      float sq = 0.f;
+      if (o < d * E) {
+        const int c = o / E, e = o % E;
+        float s = 0.f;
+        for (int r = 0; r < RCH; ++r) s += p.rpart[((long)r * E + e) * d + c];
+        const float nv = zero_grad ? s : p.grads[o] + s;
+        p.grads[o] = nv;
+        sq = nv * nv;
+      }
+      const float s = block_sum(sq, meta.red);
+      if (tid == 0) p.norm_part[n10 + n11 + ir] = s;
+    }
+  }
+}
+
+// ===========================================================================
+// P7: dx row sums; global norm; clip + AdamW (+ bf16 weight copy)
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& meta, bool zero_grad, bool apply,
+                            bool want_dx) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, f = p.f, E = p.E, k = p.k;
+
+  if (want_dx) {
+    const T* dxs = reinterpret_cast<const T*>(p.dxs);
+    for (int tok = lwg * kWaves + wave; tok < p.T; tok += G * kWaves) {
+      float dzv[kMaxTopK];
+      int ev[kMaxTopK];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        dzv[j] = 0.f;
+        ev[j] = 0;
+        if (j < k) {
+          dzv[j] = p.dzsel[tok * k + j];
+          ev[j] = p.idx[tok * k + j];
+        }
+      }
+      for (int c = lane * 8; c < d; c += 64 * 8) {
+        F8 s;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s.v[q] = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j < k) {
+            const F8 w = ld8(p.wrt + (long)ev[j] * d + c);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s.v[q] += dzv[j] * w.v[q];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j < k) {
+            const F8 v = ld8(dxs + ((long)tok * k + j) * d + c);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s.v[q] += v.v[q];
+          }
+        }
+        st8(p.dx + (long)tok * d + c, s);
+      }
+    }
+  }
+
+  // loss of this launch, summed over workgroups in index order
+  if (lwg == 0 && p.stats) {
+    float* red = reinterpret_cast<float*>(smem);
+    float s = 0.f;
+    for (int w = tid; w < G; w += kThreads) s += p.loss_part[w];
+    red[tid] = s;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.f;
+      for (int i = 0; i < kThreads; ++i) tot += red[i];
+      tot *= 0.5f * p.inv_tupd;
+      p.stats[0] = zero_grad ? tot : p.stats[0] + tot;
+    }
+    __syncthreads();
+  }
+  if (!apply) return;
+
+  // global norm from the per-tile partials, fixed order (same in every workgroup)
+  const int n10 = E * ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
+  const int n11 = E * ceil_div(d, gemm::BM) * ceil_div(f, gemm::BN);
+  const int nrr = ceil_div(d * E, kThreads);
+  const int np = n10 + n11 + nrr;
+  float* red = reinterpret_cast<float*>(smem);
+  {
+    float s = 0.f;
+    for (int i = tid; i < np; i += kThreads) s += p.norm_part[i];
+    __syncthreads();
+    red[tid] = s;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.f;
+      for (int i = 0; i < kThreads; ++i) tot += red[i];
+      red[kThreads] = tot;
+    }
+    __syncthreads();
+  }
+  const float norm = sqrtf(red[kThreads]);
+  const float c = (p.clip > 0.f) ? fminf(1.f, p.clip / (norm + 1e-6f)) : 1.f;
+  if (lwg == 0 && tid == 0 && p.stats) {
+    p.stats[1] = norm;
+    p.stats[2] = c;
+  }
+
+  // clip + AdamW over the flat parameter vector, 4 parameters per thread-step
+  const long P = (long)d * E + 2L * E * d * f;
+  const long P4 = P / 4;
+  const long nr4 = (long)d * E / 4;
+  const float b1 = p.beta1, b2 = p.beta2, omb1 = p.omb1, omb2 = p.omb2, lr = p.lr, eps = p.eps, wd = p.wd;
+  const float ib1 = p.inv_bc1, isb2 = p.inv_sqrt_bc2;
+  float4* P_ = reinterpret_cast<float4*>(p.params);
+  const float4* G_ = reinterpret_cast<const float4*>(p.grads);
+  float4* M_ = reinterpret_cast<float4*>(p.m);
+  float4* V_ = reinterpret_cast<float4*>(p.v);
+  for (long i = (long)lwg * kThreads + tid; i < P4; i += (long)G * kThreads) {
+    float4 w = P_[i], g = G_[i], m = M_[i], v = V_[i];
+    float* wv = &w.x;
+    float* gv = &g.x;
+    float* mv = &m.x;
+    float* vv = &v.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float gc = c * gv[q];
+      mv[q] = b1 * mv[q] + omb1 * gc;
+      vv[q] = b2 * vv[q] + omb2 * gc * gc;
+      const float upd = (mv[q] * ib1) / (sqrtf(vv[q]) * isb2 + eps) + wd * wv[q];
+      wv[q] = wv[q] - lr * upd;
+    }
+    P_[i] = w;
+    M_[i] = m;
+    V_[i] = v;
+    if (p.shadow && i >= nr4) {
+      uint2 s;
+      s.x = pack_bf16x2(w.x, w.y);
+      s.y = pack_bf16x2(w.z, w.w);
+      reinterpret_cast<uint2*>(p.shadow)[i - nr4] = s;
+    }
+  }
+}
+
+// ===========================================================================
+// The persistent kernel: one cooperative launch per update (or microbatch)
+// ===========================================================================
+template <typename T>
+__global__ void __launch_bounds__(kThreads) moe_step_kernel(KParams p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  Meta& meta = *reinterpret_cast<Meta*>(smem_raw);
+  char* scratch = smem_raw + kMetaBytes;
+  const bool zero_grad = (p.flags & 0x1u) != 0u;
+  const bool apply = (p.flags & 0x2u) != 0u;
+  const bool want_dx = p.dx != nullptr;
+
+#define MOE_SYNC(ph)                                                 \
+  do {                                                               \
+    trace_mark(p, ph, 1);                                            \
+    if (!grid_barrier(p.ctrl, &meta.flag)) return;                   \
+    trace_mark(p, ph, 2);                                            \
+  } while (0)
+
+  trace_mark(p, 0, 0);
+  phase_route<T>(p, scratch, meta);
+  MOE_SYNC(0);
+  trace_mark(p, 1, 0);
+  phase_order(p, scratch, meta);
+  MOE_SYNC(1);
+  trace_mark(p, 2, 0);
+  phase_ffn1<T>(p, scratch, meta);
+  MOE_SYNC(2);
+  trace_mark(p, 3, 0);
+  phase_ffn2<T>(p, scratch, meta);
+  MOE_SYNC(3);
+  trace_mark(p, 4, 0);
+  phase_combine<T>(p, meta);
+  MOE_SYNC(4);
+  trace_mark(p, 5, 0);
+  phase_bwd2<T>(p, scratch, meta, zero_grad);
+  MOE_SYNC(5);
+  trace_mark(p, 6, 0);
+  phase_bwd1<T>(p, scratch, meta, zero_grad, want_dx);
+  MOE_SYNC(6);
+  trace_mark(p, 7, 0);
+  phase_final<T>(p, scratch, meta, zero_grad, apply, want_dx);
+  __syncthreads();
+  trace_mark(p, 7, 1);
+  trace_mark(p, 7, 2);
+#undef MOE_SYNC
+}
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+"""Training state of one MoE feed-forward layer on the GPU, driven through the
+C ABI.  Holds the caller-owned tensors (fp32 master weights, gradients, Adam
+moments, stats) and hands their pointers to ``moe_step_run``; it computes
+nothing itself."""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class MoeLayerStep:
+    def __init__(self, d_model, d_ff, n_experts, top_k, max_tokens, dtype="bf16", lr=1e-3, beta1=0.9,
+                 beta2=0.999, adam_eps=1e-8, weight_decay=0.01, clip_norm=1.0, device=0, wg_per_cu=0):
+        self.cfg = B.make_config(d_model, d_ff, n_experts, top_k, max_tokens, dtype, lr, beta1, beta2, adam_eps,
+                                 weight_decay, clip_norm, device, wg_per_cu)
+        self.dtype = dtype
+        self.dev = torch.device("cuda", device)
+        self.P = B.moe_step_param_count(self.cfg)
+        self.handle = B.moe_step_create(self.cfg)
+        self.grid = B.moe_step_grid_size(self.handle)
+        z = lambda: torch.zeros(self.P, dtype=torch.float32, device=self.dev)  # noqa: E731
+        self.params, self.grads, self.exp_avg, self.exp_avg_sq = z(), z(), z(), z()
+        self.stats = torch.zeros(4, dtype=torch.float32, device=self.dev)
+        self._shadow_valid = False
+
+    def load_params(self, flat):
+        """Copies fp32 master weights in (W_r | W1 | W2 order); resets the moments."""
+        self.params.copy_(torch.as_tensor(flat, dtype=torch.float32))
+        self.exp_avg.zero_()
+        self.exp_avg_sq.zero_()
+        self._shadow_valid = False
+
+    def run(self, x, target, *, tokens_in_update=None, step=1, zero_grad=True, apply=True, dx=None,
+            router_bias=None, debug=None, trace=None, stream=None):
+        """Enqueues one launch.  ``debug`` is an optional dict of preallocated debug tensors
+        (router_logits, topk_idx, topk_gate, expert_counts, route_perm)."""
+        n = 0 if x is None else int(x.shape[0])
+        flags = 0
+        if zero_grad:
+            flags |= B.MOE_RUN_ZERO_GRAD
+        if apply:
+            flags |= B.MOE_RUN_APPLY
+        if not self._shadow_valid:
+            flags |= B.MOE_RUN_REFRESH_SHADOW
+        if trace is not None:
+            flags |= B.MOE_RUN_TRACE
+        dbg = debug or {}
+        io = B.make_io(x=x, target=target, router_bias=router_bias, params=self.params, grads=self.grads,
+                       exp_avg=self.exp_avg, exp_avg_sq=self.exp_avg_sq, dx=dx, stats=self.stats,
+                       router_logits=dbg.get("router_logits"), topk_idx=dbg.get("topk_idx"),
+                       topk_gate=dbg.get("topk_gate"), expert_counts=dbg.get("expert_counts"),
+                       route_perm=dbg.get("route_perm"), trace=trace)
+        s = torch.cuda.current_stream(self.dev) if stream is None else stream
+        B.moe_step_run(self.handle, io, n, tokens_in_update or max(1, n), step, flags, s.cuda_stream)
+        self._shadow_valid = True
+
+    def status(self):
+        B.moe_step_status(self.handle)
+
+    def trace_words(self):
+        return B.moe_step_trace_words(self.handle)
+
+    def close(self):
+        if self.handle:
+            B.moe_step_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,147 @@
+"""Parity of the HIP update with the FP64 oracle on an MI355X.
+
+Routing (top-k indices, expert counts, route_order permutation) must be bit-exact
+given the GPU's own fp32 router logits.  Floating-point outputs are compared per
+tensor with relative L2:
+  fp32 mode: every output <= 1e-5;
+  bf16 mode: gradients and dx <= 0.08 (the pages' FP64 gradient gate, Latch
+  "Results", numerical scope), updated weights and moments <= 1e-2, loss <= 1e-2.
+The full-step oracle runs with the GPU's selection (``forced_topk``) so a near-tie
+that fp32 and fp64 logits resolve differently cannot fail a numeric gate; the
+number of tokens whose FP64 routing differs is printed."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import GpuRun, compare_update, oracle_update, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = dict(grad_tol=1e-5, weight_tol=1e-5, loss_tol=1e-5)
+BF16_TOL = dict(grad_tol=0.08, weight_tol=1e-2, loss_tol=1e-2)
+
+
+def _check_routing(cfg, inp, out, w_router):
+    for mb in range(cfg.microbatches):
+        z = out["logits"][mb].astype(np.float64)
+        ref_idx = oracle.token_topk(z, cfg.top_k)
+        np.testing.assert_array_equal(out["idx"][mb], ref_idx)
+        counts, offsets, perm, inv = oracle.route_order(ref_idx, cfg.n_experts)
+        np.testing.assert_array_equal(out["counts"][mb], counts)
+        np.testing.assert_array_equal(out["perm"][mb], perm)
+        np.testing.assert_allclose(out["gate"][mb], oracle.topk_gates(z, ref_idx), rtol=2e-6, atol=1e-7)
+        x, _ = inp.microbatch(mb)
+        zr = oracle.router_logits(x, w_router, inp.router_bias)
+        assert rel_l2(z, zr) < 1e-5
+        diff = int((oracle.token_topk(zr, cfg.top_k) != ref_idx).any(axis=1).sum())
+        say(f"  microbatch {mb}: tokens routed differently by FP64 logits: {diff}")
+
+
+def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0):
+    say(f"[gpu] {cfg.name} T={cfg.tokens}x{cfg.microbatches} d={cfg.d_model} f={cfg.d_ff} E={cfg.n_experts} "
+        f"k={cfg.top_k} {cfg.dtype} clip={cfg.clip_norm if clip_norm is None else clip_norm}")
+    run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu)
+    try:
+        params = inp.flat_params().astype(np.float64)
+        m = np.zeros_like(params)
+        v = np.zeros_like(params)
+        for s in range(1, steps + 1):
+            out = run.update(s)
+            _check_routing(cfg, inp, out, params[:cfg.d_model * cfg.n_experts].reshape(cfg.d_model, cfg.n_experts))
+            ref = oracle_update(cfg, inp, params, m, v, s, out["idx"], clip_norm=clip_norm)
+            errs, bad = compare_update(cfg, out, ref, **tol)
+            assert not bad, f"step {s}: {bad}: {errs}"
+            # the next step starts from the GPU's state so each step is checked on its own
+            params, m, v = (a.astype(np.float64) for a in run.state())
+    finally:
+        run.close()
+
+
+def test_tiny_f32_two_steps():
+    cfg = synth.CONFIGS["tiny_f32"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), F32_TOL)
+
+
+def test_tiny_f32_clipping_active():
+    cfg = synth.CONFIGS["tiny_f32"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), F32_TOL, steps=1, clip_norm=0.1)
+
+
+@pytest.mark.parametrize("T,d,f,E,k", [(333, 72, 136, 5, 2), (77, 8, 8, 1, 1), (190, 64, 200, 7, 7),
+                                       (257, 136, 264, 64, 8)])
+def test_ragged_shapes_f32(T, d, f, E, k):
+    cfg = synth.small_config("ragged_f32", T, d, f, E, k, "f32")
+    _run_and_compare(cfg, synth.make_inputs(cfg, 3), F32_TOL, steps=1)
+
+
+@pytest.mark.parametrize("T,d,f,E,k", [(333, 72, 136, 5, 2), (1000, 256, 384, 16, 2), (300, 128, 64, 64, 8)])
+def test_ragged_shapes_bf16(T, d, f, E, k):
+    cfg = synth.small_config("ragged_bf16", T, d, f, E, k, "bf16")
+    _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1)
+
+
+def test_bf16_2x1024_two_steps():
+    cfg = synth.CONFIGS["bf16_2x1024"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL)
+
+
+def test_bf16_2x1024_two_workgroups_per_cu():
+    cfg = synth.CONFIGS["bf16_2x1024"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL, steps=1, wg_per_cu=2)
+
+
+def test_routing_ties_and_empty_experts():
+    # identical router columns give bitwise-identical logits: the lower expert index
+    # must win; a zero router sends every token to experts 0..k-1 (the rest get no rows)
+    cfg = synth.small_config("ties", 200, 64, 64, 6, 2, "f32")
+    inp = synth.make_inputs(cfg, 5)
+    inp.w_router[:, 3] = inp.w_router[:, 1]
+    inp.w_router[:, 5] = inp.w_router[:, 0]
+    _run_and_compare(cfg, inp, F32_TOL, steps=1)
+    inp.w_router[:] = 0.0
+    run = GpuRun(cfg, inp)
+    try:
+        out = run.update(1)
+        assert np.all(out["idx"][0] == np.array([0, 1]))
+        np.testing.assert_array_equal(out["counts"][0], [200, 200, 0, 0, 0, 0])
+        np.testing.assert_allclose(out["gate"][0], 0.5, rtol=0, atol=0)
+    finally:
+        run.close()
+
+
+def test_gradient_accumulation_f32():
+    cfg = synth.small_config("accum_f32", 96, 64, 128, 4, 2, "f32", microbatches=3)
+    _run_and_compare(cfg, synth.make_inputs(cfg, 6), F32_TOL, steps=1)
+
+
+def test_deterministic_reruns():
+    cfg = synth.CONFIGS["bf16_2x1024"]
+    inp = synth.make_inputs(cfg, 1)
+    outs = []
+    for _ in range(2):
+        run = GpuRun(cfg, inp)
+        try:
+            outs.append(run.update(1))
+        finally:
+            run.close()
+    for key in ("grads", "params", "exp_avg", "exp_avg_sq"):
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+    assert np.array_equal(outs[0]["dx"][0], outs[1]["dx"][0])
+    assert outs[0]["loss"] == outs[1]["loss"]
+
+
+def test_zero_tokens_only_decays():
+    cfg = synth.small_config("empty", 0, 64, 128, 4, 2, "f32")
+    inp = synth.make_inputs(synth.small_config("empty_src", 1, 64, 128, 4, 2, "f32"), 0)
+    run = GpuRun(cfg, inp)
+    try:
+        p0 = inp.flat_params().astype(np.float64)
+        run.layer.run(None, None, tokens_in_update=1, step=1, zero_grad=True, apply=True)
+        run.layer.status()
+        torch.cuda.synchronize()
+        assert np.all(run.layer.grads.cpu().numpy() == 0.0)
+        assert rel_l2(run.layer.params.cpu().numpy(), p0 * (1 - cfg.lr * cfg.weight_decay)) < 1e-7
+    finally:
+        run.close()
