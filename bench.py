@@ -100,6 +100,7 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--dump-trace", default=None, help="write the raw phase clocks (.npy) here")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -176,7 +177,10 @@ def main(argv=None):
         one_update(ev_tr, trace=tr)
         torch.cuda.synchronize()
         layer.status()
-        phases = trace_mod.decode(tr.cpu().numpy(), layer.grid)
+        raw = tr.cpu().numpy()
+        if args.dump_trace:
+            np.save(args.dump_trace, raw.reshape(layer.grid, -1, 3))
+        phases = trace_mod.decode(raw, layer.grid)
         phases["traced_launch_ms"] = float(ev_tr[-1][0].elapsed_time(ev_tr[-1][1]))
         print("# phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in phases["phase_us"].items())
               + f"  barrier idle mean {phases['barrier_idle_frac_mean']:.3f}", file=sys.stderr, flush=True)

@@ -113,6 +113,15 @@ typedef struct {
                                        first (needed after create and whenever the
                                        caller changed params itself) */
 #define MOE_RUN_TRACE 0x8u          /* record per-phase clocks into io.trace */
+/* Profiling aid: skip phase i (0..7) of the persistent kernel and reuse what the
+ * previous launch on this handle left in the arena.  Accepted only when the
+ * previous launch ran every phase with the same n_tokens (else MOE_ERR_STATE);
+ * results are then those of the previous launch for the skipped phases.  Phase
+ * order: 0 routing, 1 route_order, 2 expert GEMM 1, 3 expert GEMM 2,
+ * 4 combine/loss, 5 dH + dW2 + router partials, 6 dW1 + dX + router gradient,
+ * 7 dx sum + norm + clip/AdamW. */
+#define MOE_RUN_SKIP_PHASE(i) (0x100u << (i))
+#define MOE_RUN_SKIP_MASK 0xff00u
 
 /* Status-word bits reported by moe_step_status as MOE_ERR_DEVICE. */
 #define MOE_DEVICE_BARRIER_TIMEOUT 0x1u

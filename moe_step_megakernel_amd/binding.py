@@ -10,13 +10,19 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_step.so")
+LIB_PATH = os.environ.get("MOE_STEP_LIB") or os.path.join(_HERE, "_lib", "libmoe_step.so")
 
 MOE_STEP_ABI_VERSION = 1
 MOE_OK, MOE_ERR_ARG, MOE_ERR_SHAPE, MOE_ERR_HIP, MOE_ERR_NOMEM, MOE_ERR_DEVICE, MOE_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_RUN_ZERO_GRAD, MOE_RUN_APPLY, MOE_RUN_REFRESH_SHADOW, MOE_RUN_TRACE = 0x1, 0x2, 0x4, 0x8
-MOE_DEVICE_BARRIER_TIMEOUT, MOE_DEVICE_NONFINITE_LOGIT = 0x1, 0x2
+MOE_RUN_SKIP_MASK = 0xFF00
+
+
+def MOE_RUN_SKIP_PHASE(i: int) -> int:
+    return 0x100 << i
+
+MOE_DEVICE_BARRIER_TIMEOUT, MOE_DEVICE_NONFINITE_LOGIT, MOE_DEVICE_BAD_ROUTE = 0x1, 0x2, 0x4
 N_PHASES = 8
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_HIP", -4: "MOE_ERR_NOMEM",

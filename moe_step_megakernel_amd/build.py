@@ -6,6 +6,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "moe_step.hip")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libmoe_step.so")
+BENCH_SRC = os.path.join(HERE, "csrc", "moe_step_bench.cpp")
+BENCH = os.path.join(OUT_DIR, "moe_step_bench")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -25,6 +27,14 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd))
     os.replace(tmp, LIB)
+    # C++ driver of the ABI (profiling runs without Python)
+    tmpb = BENCH + ".tmp"
+    cmdb = [hipcc, "--offload-arch=gfx950", "-O2", "-std=c++17", "-x", "hip", BENCH_SRC, "-o", tmpb,
+            "-L" + OUT_DIR, "-lmoe_step", "-Wl,-rpath,$ORIGIN"]
+    res = subprocess.run(cmdb, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc (bench driver) failed:\n" + res.stdout + res.stderr)
+    os.replace(tmpb, BENCH)
     return LIB
 
 

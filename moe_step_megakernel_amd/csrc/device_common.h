@@ -114,11 +114,15 @@ __device__ __forceinline__ void gelu_and_grad(float h, float& a, float& da) {
 }
 
 // ---------------------------------------------------------------------------
-// Control words of the grid barrier (one 128-byte line each)
+// Grid barrier state.  Each workgroup owns one arrival slot (its own 128-byte
+// line, so arrivals never contend); workgroup 0 publishes the generation.
+// Barrier instances are numbered by a target value that the host makes unique
+// per launch (launch epoch * 8 + barrier index + 1), so no reset is needed
+// between launches.
 // ---------------------------------------------------------------------------
 struct Ctrl {
-  unsigned* count;   // arrivals at the current barrier
-  unsigned* gen;     // barrier generation, bumped by the last arrival
+  unsigned* arrive;  // [grid][32]: slot w at arrive[w * 32]
+  unsigned* gen;     // last released target
   unsigned* status;  // error bits (MOE_DEVICE_*)
   unsigned* abort;   // nonzero once any workgroup gave up waiting
 };
@@ -126,44 +130,56 @@ struct Ctrl {
 // Bounded wait: about two seconds of the 100 MHz constant clock.
 constexpr uint64_t kBarrierTimeoutTicks = 200000000ull;
 
+// Polls *p (relaxed, agent scope) until it equals target; false on timeout or
+// when another workgroup already gave up.
+__device__ __forceinline__ bool wait_for(const Ctrl& c, const unsigned* p, unsigned target) {
+  const uint64_t t0 = wall_clock64();
+  unsigned polls = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target) {
+    __builtin_amdgcn_s_sleep(2);
+    if ((++polls & 255u) == 0u) {
+      if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+          wall_clock64() - t0 > kBarrierTimeoutTicks) {
+        __hip_atomic_fetch_or(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(c.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+      }
+    }
+  }
+  return true;
+}
+
 // Grid-wide barrier.  Every wave first releases its own global writes at agent
 // scope (waits for its stores and writes dirty L2 lines back, so the other XCDs
-// see them); one thread per workgroup arrives on the counter; the last arrival
-// resets the counter and bumps the generation; the others poll the generation
-// with plain (relaxed) loads and sleep in between, and acquire once after it
-// moved, so waiting workgroups do not keep invalidating the caches under the
-// ones still working.  Returns false if the wait timed out or another
-// workgroup already gave up; the caller then skips all further phases so that
-// every workgroup still exits.
-__device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned* lds_flag) {
+// see them).  A workgroup other than 0 then stores `target` into its arrival
+// slot and polls the generation word; workgroup 0 polls all arrival slots in
+// parallel (one per thread), acquires, and stores `target` into the generation
+// word.  Polling uses plain relaxed loads with a sleep in between, and each
+// poller acquires once afterwards, so waiting does not keep invalidating the
+// caches under the workgroups still working.  Returns false if a wait timed out
+// or another workgroup already gave up; the caller then skips all further
+// phases so that every workgroup still exits.
+__device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, unsigned* lds_flag) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned ok = 1u;
-    const unsigned g = __hip_atomic_load(c.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned a = __hip_atomic_fetch_add(c.count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    if (a == gridDim.x - 1) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(c.count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(c.gen, g + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const uint64_t t0 = wall_clock64();
-      unsigned polls = 0;
-      while (__hip_atomic_load(c.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
-        __builtin_amdgcn_s_sleep(2);
-        if ((++polls & 255u) == 0u) {
-          if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-              wall_clock64() - t0 > kBarrierTimeoutTicks) {
-            __hip_atomic_fetch_or(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(c.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = 0u;
-            break;
-          }
-        }
+  if (threadIdx.x == 0) *lds_flag = 1u;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    bool ok = true;
+    for (int w = threadIdx.x; w < (int)gridDim.x; w += kThreads)
+      if (w != 0 && !wait_for(c, c.arrive + (size_t)w * 32, target)) {
+        ok = false;
+        break;
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    *lds_flag = ok;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!ok) *lds_flag = 0u;
+    __syncthreads();
+    if (threadIdx.x == 0 && *lds_flag != 0u)
+      __hip_atomic_store(c.gen, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (threadIdx.x == 0) {
+    __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (!wait_for(c, c.gen, target)) *lds_flag = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   return *lds_flag != 0u;

@@ -97,6 +97,8 @@ struct moe_step {
   size_t arena_bytes = 0;
   hipStream_t last_stream = nullptr;
   bool launched = false;
+  int last_full_tokens = -1;   // n_tokens of the last launch that ran every phase
+  unsigned epoch = 0;          // launches so far (barrier targets are unique per launch)
   char err[512] = "no error";
   // arena sub-buffers
   int* idx;
@@ -214,7 +216,8 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
     off = align_up(off + (bytes ? bytes : 1), 256);
     return o;
   };
-  const size_t o_ctrl = take(4 * 128 * sizeof(unsigned));
+  const size_t ctrl_words = (size_t)(h->grid + 4) * 32;
+  const size_t o_ctrl = take(ctrl_words * sizeof(unsigned));
   const size_t o_idx = take(N * 4), o_gate = take(N * 4), o_dz = take(N * 4);
   const size_t o_hist = take((size_t)h->grid * E * 4);
   const size_t o_perm = take(N * 4), o_inv = take(N * 4);
@@ -254,8 +257,9 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   h->norm_part = reinterpret_cast<float*>(a + o_norm);
   h->shadow = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a + o_shadow) : nullptr;
 
-  // barrier words and status start at zero (synchronous; not part of any run)
-  he = hipMemset(h->ctrl, 0, 4 * 128 * sizeof(unsigned));
+  // the arena starts zeroed (every stored index is then in range) and so do
+  // the barrier words and status (synchronous; not part of any run)
+  he = hipMemset(h->arena, 0, h->arena_bytes);
   if (he == hipSuccess) he = hipDeviceSynchronize();
   if (he != hipSuccess) {
     set_err(g_create_error, "clearing barrier words: %s", hipGetErrorString(he));
@@ -283,9 +287,14 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
     set_err(h->err, "tokens_in_update %lld must be >= max(1, n_tokens)", (long long)tokens_in_update);
     return MOE_ERR_ARG;
   }
-  if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE)) {
+  if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK)) {
     set_err(h->err, "unknown run flags 0x%x", run_flags);
     return MOE_ERR_ARG;
+  }
+  if ((run_flags & MOE_RUN_SKIP_MASK) && h->last_full_tokens != n_tokens) {
+    set_err(h->err, "skipping phases needs a previous full launch with the same n_tokens (%d, last %d)", n_tokens,
+            h->last_full_tokens);
+    return MOE_ERR_STATE;
   }
   if ((run_flags & MOE_RUN_APPLY) && step < 1) {
     set_err(h->err, "step must be >= 1 with MOE_RUN_APPLY (got %lld)", (long long)step);
@@ -370,10 +379,11 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
   p.loss_part = h->loss_part;
   p.norm_part = h->norm_part;
   p.shadow = h->shadow;
-  p.ctrl.count = h->ctrl;
-  p.ctrl.gen = h->ctrl + 32;
-  p.ctrl.status = h->ctrl + 64;
-  p.ctrl.abort = h->ctrl + 96;
+  p.ctrl.gen = h->ctrl;
+  p.ctrl.status = h->ctrl + 32;
+  p.ctrl.abort = h->ctrl + 64;
+  p.ctrl.arrive = h->ctrl + 128;
+  p.epoch = ++h->epoch;
 
   hipError_t he = hipSetDevice(c.device);
   if (he != hipSuccess) {
@@ -391,6 +401,7 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
   }
   h->last_stream = stream;
   h->launched = true;
+  if (!(run_flags & MOE_RUN_SKIP_MASK)) h->last_full_tokens = n_tokens;
   return MOE_OK;
 }
 
@@ -403,7 +414,7 @@ int moe_step_status(moe_step_t h) {
     return MOE_ERR_HIP;
   }
   unsigned st = 0;
-  he = hipMemcpy(&st, h->ctrl + 64, sizeof(unsigned), hipMemcpyDeviceToHost);
+  he = hipMemcpy(&st, h->ctrl + 32, sizeof(unsigned), hipMemcpyDeviceToHost);
   if (he != hipSuccess) {
     set_err(h->err, "reading the status word: %s", hipGetErrorString(he));
     return MOE_ERR_HIP;
@@ -412,8 +423,9 @@ int moe_step_status(moe_step_t h) {
     set_err(h->err, "device error 0x%x:%s%s%s", st, (st & MOE_DEVICE_BARRIER_TIMEOUT) ? " grid-barrier timeout" : "",
             (st & MOE_DEVICE_NONFINITE_LOGIT) ? " non-finite router logit" : "",
             (st & MOE_DEVICE_BAD_ROUTE) ? " expert index out of range" : "");
-    he = hipMemset(h->ctrl, 0, 4 * 128 * sizeof(unsigned));
+    he = hipMemset(h->ctrl, 0, (size_t)(h->grid + 4) * 32 * sizeof(unsigned));
     if (he == hipSuccess) he = hipDeviceSynchronize();
+    h->epoch = 0;
     return MOE_ERR_DEVICE;
   }
   return MOE_OK;

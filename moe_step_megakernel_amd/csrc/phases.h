@@ -46,6 +46,7 @@ struct KParams {
   unsigned flags;
   // optimizer
   float lr, beta1, beta2, omb1, omb2, eps, wd, clip, inv_bc1, inv_sqrt_bc2;
+  unsigned epoch;     // launch number on this handle (barrier targets)
   // caller buffers
   const void* x;
   const void* t;
@@ -92,6 +93,22 @@ __device__ __forceinline__ int logical_wg() {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Work items [0, n) of a phase, dealt so that each XCD gets one contiguous
+// block of items (shared operands stay in that XCD's L2) and the blocks are
+// equal to within one item.  Workgroup b runs on XCD b % 8.
+struct Span {
+  int begin, end, step;
+};
+__device__ __forceinline__ Span xcd_span(int n) {
+  const int G = gridDim.x;
+  if ((G & 7) != 0) return {(int)blockIdx.x, n, G};
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per = G >> 3;
+  const int chunk = (n + 7) >> 3;
+  const int lo = min(n, x * chunk);
+  const int hi = min(n, lo + chunk);
+  return {lo + j, hi, per};
+}
 
 __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot) {
   if ((p.flags & 0x8u) && p.trace && threadIdx.x == 0)
@@ -145,9 +162,28 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
     for (int c0 = 0; c0 < d; c0 += DC) {
       const int dc = min(DC, d - c0);
       __syncthreads();
-      for (int i = tid; i < E * dc; i += kThreads) {
-        const int c = i / E, e = i % E;
-        ws[e * LDW + c] = p.params[(long)(c0 + c) * E + e];
+      {
+        // rows c0..c0+dc of W_r are contiguous: float4 loads, all issued first
+        const float4* src = reinterpret_cast<const float4*>(p.params + (long)c0 * E);
+        const int n4 = E * dc / 4;
+        for (int i0 = tid; i0 < n4; i0 += kThreads * 8) {
+          float4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + u * kThreads < n4) v[u] = src[i0 + u * kThreads];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i4 = i0 + u * kThreads;
+            if (i4 < n4) {
+              const float* vv = &v[u].x;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int i = i4 * 4 + q;
+                ws[(i % E) * LDW + i / E] = vv[q];
+              }
+            }
+          }
+        }
       }
       for (int g0 = 0; g0 < nb; g0 += TPI) {
         __syncthreads();
@@ -245,7 +281,7 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
 // ===========================================================================
 // P1: route_order -- offsets and a stable scatter of the flat ids by expert
 // ===========================================================================
-__device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& meta) {
+__device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& meta, bool skip_scatter) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, lwg = logical_wg();
   const int E = p.E, k = p.k;
@@ -261,10 +297,18 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     const int e = tid % EP, part = tid / EP;
     int pre = 0, tot = 0;
     if (e < E) {
-      for (int w = part; w < G; w += parts) {
-        const int h = p.hist[(long)w * E + e];
-        tot += h;
-        if (w < lwg) pre += h;
+      for (int w0 = part; w0 < G; w0 += parts * 8) {
+        int h[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int w = w0 + u * parts;
+          h[u] = (w < G) ? p.hist[(long)w * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tot += h[u];
+          if (w0 + u * parts < lwg) pre += h[u];
+        }
       }
     }
     sp[tid] = pre;
@@ -296,6 +340,7 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   __syncthreads();
   if (tid < E) base[tid] = meta.off[tid] + sp[tid];
   if (lwg == 0 && tid < E && p.dbg_counts) p.dbg_counts[tid] = meta.cnt[tid];
+  if (skip_scatter) return;
 
   const int per = ceil_div(p.T, G);
   const int t_lo = min(p.T, lwg * per), t_hi = min(p.T, t_lo + per);
@@ -360,7 +405,8 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
   const int ntiles = meta.moff[p.E] * NT;
   T* act = reinterpret_cast<T*>(p.act);
   T* gp = reinterpret_cast<T*>(p.gp);
-  for (int tI = lwg; tI < ntiles; tI += G) {
+  const Span sp = xcd_span(ntiles);
+  for (int tI = sp.begin; tI < sp.end; tI += sp.step) {
     const int mg = tI / NT, nt = tI % NT;
     const int e = expert_of_tile(meta, p.E, mg);
     const int m0 = (mg - meta.moff[e]) * gemm::BM;
@@ -370,13 +416,14 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
     gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1, 0, d, f,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
-    gemm::tile<T, false, true>(lds, A, B, d, [&](int r, int c, float h) {
+    gemm::tile<T, false, true>(lds, A, B, d, [&](int r, int c, const float (&h)[8]) {
       if (r < mrows && n0 + c < f) {
-        float a, da;
-        gelu_and_grad(h, a, da);
+        F8 a, da;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) gelu_and_grad(h[q], a.v[q], da.v[q]);
         const long o = (long)(p0 + r) * f + n0 + c;
-        store_elem(act + o, a);
-        store_elem(gp + o, da);
+        st8(act + o, a);
+        st8(gp + o, da);
       }
     });
   }
@@ -391,7 +438,8 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
   const int d = p.d, f = p.f;
   const int NT = ceil_div(d, gemm::BN);
   const int ntiles = meta.moff[p.E] * NT;
-  for (int tI = lwg; tI < ntiles; tI += G) {
+  const Span sp = xcd_span(ntiles);
+  for (int tI = sp.begin; tI < sp.end; tI += sp.step) {
     const int mg = tI / NT, nt = tI % NT;
     const int e = expert_of_tile(meta, p.E, mg);
     const int m0 = (mg - meta.moff[e]) * gemm::BM;
@@ -401,8 +449,13 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
     gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1, 0, f, d,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
-    gemm::tile<T, false, true>(lds, A, B, f, [&](int r, int c, float v) {
-      if (r < mrows && n0 + c < d) p.out[(long)(p0 + r) * d + n0 + c] = v;
+    gemm::tile<T, false, true>(lds, A, B, f, [&](int r, int c, const float (&v)[8]) {
+      if (r < mrows && n0 + c < d) {
+        F8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o.v[q] = v[q];
+        st8(p.out + (long)(p0 + r) * d + n0 + c, o);
+      }
     });
   }
 }
@@ -502,7 +555,16 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
   float* gw2 = p.grads + (long)d * E + (long)E * d * f;
   const T* x = reinterpret_cast<const T*>(p.x);
 
-  for (int item = lwg; item < n10 + n9 + nr; item += G) {
+  // each kind of work is dealt over the XCDs on its own, so every XCD gets the
+  // same mix (the kinds differ a lot in cost)
+  const Span s10 = xcd_span(n10), s9 = xcd_span(n9), sr = xcd_span(nr);
+  const int c10 = max(0, ceil_div(s10.end - s10.begin, s10.step));
+  const int c9 = max(0, ceil_div(s9.end - s9.begin, s9.step));
+  const int cr = max(0, ceil_div(sr.end - sr.begin, sr.step));
+  for (int q = 0; q < c10 + c9 + cr; ++q) {
+    const int item = q < c10 ? s10.begin + q * s10.step
+                   : q < c10 + c9 ? n10 + s9.begin + (q - c10) * s9.step
+                                  : n10 + n9 + sr.begin + (q - c10 - c9) * sr.step;
     if (item < n10) {
       // dW2[e] (f x d) = A_e^T dO_e, contraction over the expert's rows
       const int e = item / (MT10 * NT10), rem = item % (MT10 * NT10);
@@ -513,12 +575,21 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, pe, ce, d, n0};
       float* g = gw2 + (long)e * f * d;
       float sq = 0.f;
-      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, float v) {
+      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, const float (&v)[8]) {
         if (m0 + r < f && n0 + c < d) {
           float* q = g + (long)(m0 + r) * d + n0 + c;
-          const float nv = zero_grad ? v : *q + v;
-          *q = nv;
-          sq += nv * nv;
+          F8 nv;
+          if (zero_grad) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) nv.v[u] = v[u];
+          } else {
+            nv = ld8(q);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) nv.v[u] += v[u];
+          }
+          st8(q, nv);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
         }
       });
       const float s = block_sum(sq, meta.red);
@@ -535,10 +606,13 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, f - nt * gemm::BN), d, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(lds, A, B, d, [&](int r, int c, float v) {
+      gemm::tile<T, false, false>(lds, A, B, d, [&](int r, int c, const float (&v)[8]) {
         if (r < mrows && n0 + c < f) {
           const long o = (long)(p0 + r) * f + n0 + c;
-          store_elem(dh + o, v * to_f32(gp[o]));
+          F8 g8 = ld8(gp + o);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) g8.v[u] *= v[u];
+          st8(dh + o, g8);
         }
       });
     } else {
@@ -561,7 +635,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
         }
         __syncthreads();
         if (c < d) {
-          constexpr int U = 8;
+          constexpr int U = 32;
           int tok = s0;
           for (; tok + U <= s1; tok += U) {
             float xv[U];
@@ -608,7 +682,14 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
-  for (int item = lwg; item < n11 + n12 + nrr; item += G) {
+  const Span s11 = xcd_span(n11), s12 = xcd_span(n12), srr = xcd_span(nrr);
+  const int c11 = max(0, ceil_div(s11.end - s11.begin, s11.step));
+  const int c12 = max(0, ceil_div(s12.end - s12.begin, s12.step));
+  const int crr = max(0, ceil_div(srr.end - srr.begin, srr.step));
+  for (int q = 0; q < c11 + c12 + crr; ++q) {
+    const int item = q < c11 ? s11.begin + q * s11.step
+                   : q < c11 + c12 ? n11 + s12.begin + (q - c11) * s12.step
+                                   : n11 + n12 + srr.begin + (q - c11 - c12) * srr.step;
     if (item < n11) {
       // dW1[e] (d x f) = X_e^T dH_e; X_e rows gathered from x through perm
       const int e = item / (MT11 * NT11), rem = item % (MT11 * NT11);
@@ -619,12 +700,21 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, pe, ce, f, n0};
       float* g = gw1 + (long)e * d * f;
       float sq = 0.f;
-      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, float v) {
+      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, const float (&v)[8]) {
         if (m0 + r < d && n0 + c < f) {
           float* q = g + (long)(m0 + r) * f + n0 + c;
-          const float nv = zero_grad ? v : *q + v;
-          *q = nv;
-          sq += nv * nv;
+          F8 nv;
+          if (zero_grad) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) nv.v[u] = v[u];
+          } else {
+            nv = ld8(q);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) nv.v[u] += v[u];
+          }
+          st8(q, nv);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
         }
       });
       const float s = block_sum(sq, meta.red);
@@ -641,8 +731,13 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, d - nt * gemm::BN), f, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(lds, A, B, f, [&](int r, int c, float v) {
-        if (r < mrows && n0 + c < d) store_elem(dxs + (long)p.perm[p0 + r] * d + n0 + c, v);
+      gemm::tile<T, false, false>(lds, A, B, f, [&](int r, int c, const float (&v)[8]) {
+        if (r < mrows && n0 + c < d) {
+          F8 o;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o.v[u] = v[u];
+          st8(dxs + (long)p.perm[p0 + r] * d + n0 + c, o);
+        }
       });
     } else {
       // dW_r[c][e] = sum over token chunks (ascending) of the partials
@@ -765,10 +860,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   const float4* G_ = reinterpret_cast<const float4*>(p.grads);
   float4* M_ = reinterpret_cast<float4*>(p.m);
   float4* V_ = reinterpret_cast<float4*>(p.v);
-  for (long i = (long)lwg * kThreads + tid; i < P4; i += (long)G * kThreads) {
-    float4 w = P_[i], g = G_[i], m = M_[i], v = V_[i];
+  auto adamw4 = [&](float4& w, const float4& g, float4& m, float4& v) {
     float* wv = &w.x;
-    float* gv = &g.x;
+    const float* gv = &g.x;
     float* mv = &m.x;
     float* vv = &v.x;
 #pragma unroll
@@ -779,6 +873,8 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
       const float upd = (mv[q] * ib1) / (sqrtf(vv[q]) * isb2 + eps) + wd * wv[q];
       wv[q] = wv[q] - lr * upd;
     }
+  };
+  auto store4 = [&](long i, const float4& w, const float4& m, const float4& v) {
     P_[i] = w;
     M_[i] = m;
     V_[i] = v;
@@ -788,6 +884,29 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
       s.y = pack_bf16x2(w.z, w.w);
       reinterpret_cast<uint2*>(p.shadow)[i - nr4] = s;
     }
+  };
+  constexpr int U = 2;
+  const long stride = (long)G * kThreads;
+  long i = (long)lwg * kThreads + tid;
+  for (; i + (U - 1) * stride < P4; i += U * stride) {
+    float4 w[U], g[U], m[U], v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w[u] = P_[i + u * stride];
+      g[u] = G_[i + u * stride];
+      m[u] = M_[i + u * stride];
+      v[u] = V_[i + u * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      adamw4(w[u], g[u], m[u], v[u]);
+      store4(i + u * stride, w[u], m[u], v[u]);
+    }
+  }
+  for (; i < P4; i += stride) {
+    float4 w = P_[i], g = G_[i], m = M_[i], v = V_[i];
+    adamw4(w, g, m, v);
+    store4(i, w, m, v);
   }
 }
 
@@ -806,33 +925,34 @@ __global__ void __launch_bounds__(kThreads) moe_step_kernel(KParams p) {
 #define MOE_SYNC(ph)                                                 \
   do {                                                               \
     trace_mark(p, ph, 1);                                            \
-    if (!grid_barrier(p.ctrl, &meta.flag)) return;                   \
+    if (!grid_barrier(p.ctrl, p.epoch * 8u + (ph) + 1u, &meta.flag)) return; \
     trace_mark(p, ph, 2);                                            \
   } while (0)
 
+  const unsigned skip = p.flags >> 8;
   trace_mark(p, 0, 0);
-  phase_route<T>(p, scratch, meta);
+  if (!(skip & 1u)) phase_route<T>(p, scratch, meta);
   MOE_SYNC(0);
   trace_mark(p, 1, 0);
-  phase_order(p, scratch, meta);
+  phase_order(p, scratch, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
   MOE_SYNC(1);
   trace_mark(p, 2, 0);
-  phase_ffn1<T>(p, scratch, meta);
+  if (!(skip & 4u)) phase_ffn1<T>(p, scratch, meta);
   MOE_SYNC(2);
   trace_mark(p, 3, 0);
-  phase_ffn2<T>(p, scratch, meta);
+  if (!(skip & 8u)) phase_ffn2<T>(p, scratch, meta);
   MOE_SYNC(3);
   trace_mark(p, 4, 0);
-  phase_combine<T>(p, meta);
+  if (!(skip & 16u)) phase_combine<T>(p, meta);
   MOE_SYNC(4);
   trace_mark(p, 5, 0);
-  phase_bwd2<T>(p, scratch, meta, zero_grad);
+  if (!(skip & 32u)) phase_bwd2<T>(p, scratch, meta, zero_grad);
   MOE_SYNC(5);
   trace_mark(p, 6, 0);
-  phase_bwd1<T>(p, scratch, meta, zero_grad, want_dx);
+  if (!(skip & 64u)) phase_bwd1<T>(p, scratch, meta, zero_grad, want_dx);
   MOE_SYNC(6);
   trace_mark(p, 7, 0);
-  phase_final<T>(p, scratch, meta, zero_grad, apply, want_dx);
+  if (!(skip & 128u)) phase_final<T>(p, scratch, meta, zero_grad, apply, want_dx);
   __syncthreads();
   trace_mark(p, 7, 1);
   trace_mark(p, 7, 2);

@@ -1,23 +1,27 @@
 // ragged_mm on CDNA4 matrix cores: one 128x128 output tile of a grouped
 // (per-expert) matrix product, computed by one 256-thread workgroup.
 //
-// The Latch pages ("What Latch does", step 1 and step 3) name ragged_mm as the
+// The Latch pages ("What Latch does", steps 1 and 3) name ragged_mm as the
 // grouped expert product whose bucket sizes change every update, with
 // derivative rules for its backward.  Here each tile is C[m,n] = sum_k A[m,k]
 // B[k,n] with fp32 accumulation on MFMA (bf16: v_mfma_f32_32x32x16_bf16; fp32
-// mode: v_mfma_f32_32x32x2_f32).
+// mode: v_mfma_f32_32x32x2_f32), four wavefronts of 64x64 each.
 //
-// Operands are staged through LDS in a [row][k] layout (k contiguous, 128
-// bytes of k per row and stage, rows padded to 144 bytes).  An operand whose
-// source rows run along k ("direct": activations in the forward products,
-// weights read as W^T) is copied 16 bytes at a time.  An operand whose source
-// rows run along m or n ("transposed": weights read as W, and both operands of
-// the weight-gradient products, where k runs over the routed tokens) is loaded
-// as 4 k-rows x 16 bytes per thread and transposed in registers before the
-// LDS write.  Row indices may go through a map (the dispatch gather: row =
-// perm[p] / k), so no gathered copy of the tokens is ever materialised.
-// Two LDS stages: the global loads of k-tile i+1 are in flight while the
-// matrix cores work on k-tile i.
+// Each operand is read from global memory in whichever orientation it is
+// stored, always 16 contiguous bytes per lane, and copied to LDS unchanged:
+//  * K-rows operand ("k runs along the source row": activations in the forward
+//    products, weights read as W^T): LDS [m or n][k], 128 bytes of k per row;
+//    an MFMA fragment is one ds_read_b128.
+//  * MN-rows operand ("m or n runs along the source row": weights read as W,
+//    and both operands of the weight-gradient products, where k runs over the
+//    routed tokens): LDS [k][m or n], 256 bytes per row; in bf16 an MFMA
+//    fragment is two ds_read_b64_tr_b16, the gfx950 LDS read that transposes
+//    16-bit data across each group of 16 lanes.  (fp32 mode has no such read;
+//    its MN-rows operands are transposed in registers before the LDS write.)
+// Row indices may go through a map (the dispatch gather: row = perm[p] / k),
+// so no gathered copy of the tokens is ever materialised.  Two LDS stages: the
+// global loads of k-tile i+1 are in flight while the matrix cores work on
+// k-tile i.
 #pragma once
 
 #include "device_common.h"
@@ -27,19 +31,20 @@ namespace gemm {
 
 constexpr int BM = 128;
 constexpr int BN = 128;
-constexpr int KBYTES = 128;              // bytes of k per LDS row per stage
-constexpr int ROW = 144;                 // padded LDS row stride (bytes)
-constexpr int A_BYTES = BM * ROW;
-constexpr int B_BYTES = BN * ROW;
-constexpr int STAGE = A_BYTES + B_BYTES;
+constexpr int KBYTES = 128;              // bytes of k per stage
+constexpr int ROW = KBYTES + 16;         // LDS row stride of a K-rows operand (bytes)
+constexpr int ROWT = 2 * KBYTES + 32;    // LDS row stride of an MN-rows bf16 operand (bytes)
+constexpr int OP_BYTES = BM * ROW;       // one operand, one stage (both layouts fit)
+constexpr int A_BYTES = OP_BYTES;
+constexpr int STAGE = 2 * OP_BYTES;
 constexpr int LDS_BYTES = 2 * STAGE;     // 73,728 bytes
+static_assert((KBYTES / 2) * ROWT <= OP_BYTES, "MN-rows stage must fit");
 
 // One operand of a tile.
-//   direct:     logical row r (0..127) -> source row map(p0 + r), k runs along it;
-//               rows r >= nrows and k >= lim read as zero.
-//   transposed: logical k-row kk -> source row map(p0 + kk), the tile's m/n
-//               columns mn0.. run along it; k-rows kk >= nrows and columns
-//               >= lim read as zero.
+//   K-rows:  logical row r (0..127) -> source row map(p0 + r), k runs along it;
+//            rows r >= nrows and k >= lim read as zero.
+//   MN-rows: logical k-row kk -> source row map(p0 + kk), the tile's m/n columns
+//            mn0.. run along it; k-rows kk >= nrows and columns >= lim read as zero.
 struct Operand {
   const char* base;   // bytes
   long ld;            // source row stride in elements
@@ -55,106 +60,134 @@ __device__ __forceinline__ long map_row(const Operand& o, int p) {
   return o.map ? (long)(o.map[p] / o.div) : (long)p;
 }
 
-template <typename T>
-struct Loader {
-  static constexpr int VEC = 16 / (int)sizeof(T);    // elements per 16 bytes
-  static constexpr int BKE = KBYTES / (int)sizeof(T);  // k elements per stage
-  static constexpr int MBC = 128 / VEC;               // 16-byte column groups per tile row
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
-  // direct operands: source byte offsets of this thread's 4 rows (or -1)
+template <typename T, bool MN>
+struct Stager {
+  static constexpr int VEC = 16 / (int)sizeof(T);      // elements per 16 bytes
+  static constexpr int BKE = KBYTES / (int)sizeof(T);  // k elements per stage
+  static constexpr bool TR_READ = MN && sizeof(T) == 2;  // LDS [k][mn], transpose on read
+
+  // source byte offsets of this thread's 4 rows (-1 = out of range); only
+  // K-rows operands keep them (their rows do not change along k)
   long rowoff[4];
 
-  __device__ __forceinline__ void init_direct(const Operand& o) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void init(const Operand& o) {
+    if constexpr (!MN) {
+      const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      rowoff[i] = (r < o.nrows) ? map_row(o, o.p0 + r) * o.ld * (long)sizeof(T) : -1;
-    }
-  }
-
-  __device__ __forceinline__ void load_direct(const Operand& o, int kt, uint4 (&v)[4]) const {
-    const int c = threadIdx.x & 7;
-    const int col = kt * BKE + c * VEC;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (rowoff[i] >= 0 && col < o.lim)
-        x = *reinterpret_cast<const uint4*>(o.base + rowoff[i] + (long)col * (long)sizeof(T));
-      v[i] = x;
-    }
-  }
-
-  __device__ __forceinline__ static void load_trans(const Operand& o, int kt, uint4 (&v)[4]) {
-    const int tid = threadIdx.x;
-    const int mb = tid % MBC, kb = tid / MBC;
-    const int mn = o.mn0 + mb * VEC;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = kt * BKE + kb * 4 + i;
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (kk < o.nrows && mn < o.lim) {
-        const long row = map_row(o, o.p0 + kk);
-        x = *reinterpret_cast<const uint4*>(o.base + (row * o.ld + mn) * (long)sizeof(T));
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        rowoff[i] = (r < o.nrows) ? map_row(o, o.p0 + r) * o.ld * (long)sizeof(T) : -1;
       }
-      v[i] = x;
     }
   }
 
-  __device__ __forceinline__ static void store_direct(char* lds, const uint4 (&v)[4]) {
+  // Out-of-range elements are loaded from the operand's first element (always
+  // valid when a tile exists) and then zeroed, so every load is issued.
+  __device__ __forceinline__ void load(const Operand& o, int kt, uint4 (&v)[4]) const {
     const int tid = threadIdx.x;
-    const int c = tid & 7;
+    if constexpr (!MN) {
+      const int col = kt * BKE + (tid & 7) * VEC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(lds + r * ROW + c * 16) = v[i];
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = rowoff[i] >= 0 && col < o.lim;
+        uint4 x = *reinterpret_cast<const uint4*>(o.base + (ok ? rowoff[i] + (long)col * (long)sizeof(T) : 0L));
+        if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
+        v[i] = x;
+      }
+    } else if constexpr (TR_READ) {
+      // 64 k-rows x 256 bytes: 16 lanes per row, 16 rows per pass
+      const int mn = o.mn0 + (tid & 15) * VEC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kt * BKE + (tid >> 4) + 16 * i;
+        const bool ok = kk < o.nrows && mn < o.lim;
+        const long off = ok ? (map_row(o, o.p0 + kk) * o.ld + mn) * (long)sizeof(T) : 0L;
+        uint4 x = *reinterpret_cast<const uint4*>(o.base + off);
+        if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
+        v[i] = x;
+      }
+    } else {
+      // fp32: a block of 4 k-rows x 4 columns per thread
+      const int mb = tid & 31, kb = tid >> 5;
+      const int mn = o.mn0 + mb * VEC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kt * BKE + kb * 4 + i;
+        const bool ok = kk < o.nrows && mn < o.lim;
+        const long off = ok ? (map_row(o, o.p0 + kk) * o.ld + mn) * (long)sizeof(T) : 0L;
+        uint4 x = *reinterpret_cast<const uint4*>(o.base + off);
+        if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
+        v[i] = x;
+      }
     }
-  }
-
-  __device__ __forceinline__ static uint32_t half16(const uint4& u, int j) {
-    const uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
-    return (j & 1) ? (w >> 16) : (w & 0xffffu);
   }
 
   __device__ __forceinline__ static uint32_t word32(const uint4& u, int j) {
     return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
   }
 
-  // transposed: thread holds k-rows kb*4..kb*4+3 of columns mb*VEC..+VEC;
-  // writes VEC LDS rows, each with 4 consecutive k values.
-  __device__ __forceinline__ static void store_trans(char* lds, const uint4 (&v)[4]) {
+  __device__ __forceinline__ static void store(char* lds, const uint4 (&v)[4]) {
     const int tid = threadIdx.x;
-    const int mb = tid % MBC, kb = tid / MBC;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (!MN) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint2 w;
-        w.x = half16(v[0], j) | (half16(v[1], j) << 16);
-        w.y = half16(v[2], j) | (half16(v[3], j) << 16);
-        *reinterpret_cast<uint2*>(lds + (mb * 8 + j) * ROW + kb * 8) = w;
-      }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(lds + ((tid >> 3) + 32 * i) * ROW + (tid & 7) * 16) = v[i];
+    } else if constexpr (TR_READ) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(lds + ((tid >> 4) + 16 * i) * ROWT + (tid & 15) * 16) = v[i];
     } else {
+      const int mb = tid & 31, kb = tid >> 5;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint4 w = make_uint4(word32(v[0], j), word32(v[1], j), word32(v[2], j), word32(v[3], j));
+        const uint4 w = make_uint4(word32(v[0], j), word32(v[1], j), word32(v[2], j), word32(v[3], j));
         *reinterpret_cast<uint4*>(lds + (mb * 4 + j) * ROW + kb * 16) = w;
       }
     }
   }
+
+  // The 16-byte MFMA fragment of 32-row block `row0` (m or n), k chunk `chunk`
+  // (32 bytes of k) for this lane: row row0 + lane%32, k elements
+  // chunk*32/sizeof(T) + (lane/32)*VEC .. +VEC.
+  __device__ __forceinline__ static uint4 frag(const char* lds, int row0, int chunk) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (TR_READ) {
+      // lane j of each 16-lane group points at k-row k0 + j/4, columns
+      // c0 + 4*(j%4)..+3; lane i then holds k-rows k0..k0+3 of column c0 + i
+      const int g = lane >> 4, j = lane & 15;
+      const int k0 = chunk * 16 + 8 * (g >> 1);
+      const int c0 = row0 + 16 * (g & 1);
+      const char* p = lds + (k0 + (j >> 2)) * ROWT + (c0 + 4 * (j & 3)) * 2;
+      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p);
+      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(p + 4 * ROWT));
+      uint4 r;
+      r.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+      r.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+      r.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+      r.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+      return r;
+    } else {
+      return *reinterpret_cast<const uint4*>(lds + (row0 + (lane & 31)) * ROW + chunk * 32 + (lane >> 5) * 16);
+    }
+  }
 };
 
-template <typename T>
+template <typename T, bool MN_A, bool MN_B>
 __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16_t (&acc)[2][2]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  using SA = Stager<T, MN_A>;
+  using SB = Stager<T, MN_B>;
+  const int w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
-  const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int chunk = 0; chunk < KBYTES / 32; ++chunk) {
     uint4 a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      a[i] = *reinterpret_cast<const uint4*>(As + (wm * 64 + i * 32 + r32) * ROW + chunk * 32 + half * 16);
-      b[i] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + i * 32 + r32) * ROW + chunk * 32 + half * 16);
+      a[i] = SA::frag(As, wm * 64 + i * 32, chunk);
+      b[i] = SB::frag(Bs, wn * 64 + i * 32, chunk);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -179,12 +212,19 @@ __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16
   }
 }
 
-// Computes one tile and hands every accumulator to epi(row, col, value) with
-// row, col the coordinates inside the 128x128 tile.  Each lane owns 4
-// consecutive rows of one column per 32x32 block.  K is the contraction length.
-template <typename T, bool TRANS_A, bool TRANS_B, class Epi>
+// Computes one tile, then hands it to the epilogue in row-major pieces: the
+// accumulators go through LDS (fp32, 128 x 132) and epi(row, col, v) is called
+// with 8 consecutive columns v[0..7] of one row (col a multiple of 8), so the
+// epilogue's global accesses are 16- or 32-byte vectors and its code exists
+// once instead of once per accumulator.  K is the contraction length; MN_A /
+// MN_B select the MN-rows layout for that operand.
+constexpr int CROW = BN + 4;   // fp32 words per LDS row of the staged tile
+static_assert(BM * CROW * 4 <= LDS_BYTES, "staged tile must fit");
+
+template <typename T, bool MN_A, bool MN_B, class Epi>
 __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi) {
-  using L = Loader<T>;
+  using SA = Stager<T, MN_A>;
+  using SB = Stager<T, MN_B>;
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -193,46 +233,60 @@ __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand&
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  L la, lb;
-  if constexpr (!TRANS_A) la.init_direct(A);
-  if constexpr (!TRANS_B) lb.init_direct(B);
-  const int nk = (K + L::BKE - 1) / L::BKE;
+  SA sa;
+  SB sb;
+  sa.init(A);
+  sb.init(B);
+  const int nk = (K + SA::BKE - 1) / SA::BKE;
   __syncthreads();  // the previous user of this LDS is done
   if (nk > 0) {
     uint4 ra[4], rb[4];
-    if constexpr (TRANS_A) L::load_trans(A, 0, ra); else la.load_direct(A, 0, ra);
-    if constexpr (TRANS_B) L::load_trans(B, 0, rb); else lb.load_direct(B, 0, rb);
-    if constexpr (TRANS_A) L::store_trans(lds, ra); else L::store_direct(lds, ra);
-    if constexpr (TRANS_B) L::store_trans(lds + A_BYTES, rb); else L::store_direct(lds + A_BYTES, rb);
+    sa.load(A, 0, ra);
+    sb.load(B, 0, rb);
+    SA::store(lds, ra);
+    SB::store(lds + A_BYTES, rb);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       char* cur = lds + (kt & 1) * STAGE;
       char* nxt = lds + ((kt + 1) & 1) * STAGE;
       const bool more = kt + 1 < nk;
       if (more) {
-        if constexpr (TRANS_A) L::load_trans(A, kt + 1, ra); else la.load_direct(A, kt + 1, ra);
-        if constexpr (TRANS_B) L::load_trans(B, kt + 1, rb); else lb.load_direct(B, kt + 1, rb);
+        sa.load(A, kt + 1, ra);
+        sb.load(B, kt + 1, rb);
       }
-      mma_stage<T>(cur, cur + A_BYTES, acc);
+      mma_stage<T, MN_A, MN_B>(cur, cur + A_BYTES, acc);
       if (more) {
-        if constexpr (TRANS_A) L::store_trans(nxt, ra); else L::store_direct(nxt, ra);
-        if constexpr (TRANS_B) L::store_trans(nxt + A_BYTES, rb); else L::store_direct(nxt + A_BYTES, rb);
+        SA::store(nxt, ra);
+        SB::store(nxt + A_BYTES, rb);
       }
       __syncthreads();
     }
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w & 1, wn = w >> 1;
+  // stage the accumulators: lane owns 4 consecutive rows of one column per block
+  float* cs = reinterpret_cast<float*>(lds);
+  {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w & 1, wn = w >> 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = wn * 64 + j * 32 + (lane & 31);
-        epi(row, col, acc[i][j][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = wn * 64 + j * 32 + (lane & 31);
+          cs[row * CROW + col] = acc[i][j][r];
+        }
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int it = threadIdx.x; it < BM * (BN / 8); it += kThreads) {
+    const int row = it >> 4, col = (it & 15) * 8;
+    const float4 lo = *reinterpret_cast<const float4*>(cs + row * CROW + col);
+    const float4 hi = *reinterpret_cast<const float4*>(cs + row * CROW + col + 4);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    epi(row, col, v);
+  }
 }
 
 }  // namespace gemm
