@@ -56,6 +56,40 @@ def algorithmic_bytes(cfg) -> dict:
             "per_update": per_mb * cfg.microbatches + adamw, "phases": ph}
 
 
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_sha256() -> str:
+    """Hash of the sources the persistent kernel is built from (the same recipe
+    as the one recorded with the counter profile)."""
+    import glob
+    import hashlib
+    files = sorted(glob.glob(os.path.join(ROOT, "moe_step_megakernel_amd", "csrc", "*.h"))
+                   + [os.path.join(ROOT, "moe_step_megakernel_amd", "csrc", "moe_step.hip"),
+                      os.path.join(ROOT, "include", "moe_step.h")],
+                   key=lambda f: os.path.relpath(f, ROOT))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile of
+    this workload, scaled by the copy calibration; None if there is none or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"moe_step_kernel_{cfg.name}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        doc = json.load(fh)
+    if doc.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return float(doc["hbm_bytes_per_launch"])
+
+
 def gemm_flops(cfg) -> int:
     return 6 * 2 * cfg.tokens * cfg.top_k * cfg.d_model * cfg.d_ff * cfg.microbatches
 
@@ -190,8 +224,9 @@ def main(argv=None):
     avg_launch_s = float(launch_ms.mean()) / 1e3
     bytes_per_launch = ab["per_microbatch"] + ab["adamw"] / M
     achieved = bytes_per_launch / avg_launch_s / 1e9
+    traffic = measured_traffic(cfg)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "moe::moe_step_kernel (persistent, one launch per update)",
                 "algorithmic_bytes_per_launch": int(bytes_per_launch),
                 "avg_launch_us": avg_launch_s * 1e6,

@@ -6,7 +6,7 @@
 // transform (a different stream from the Python generator; timings do not
 // depend on the exact values).  Prints one line per run with ms/update.
 //
-//   moe_step_bench [--config NAME] [--steps K] [--warmup W] [--skip MASK] [--copy-mib N]
+//   moe_step_bench [--config NAME] [--steps K] [--warmup W] [--skip MASK] [--wg-per-cu N] [--copy-mib N]
 //     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024
 //     --skip MASK: after the warm-up, time launches that skip the phases in MASK
 //                  (bit i = phase i), for per-phase counter collection
@@ -102,7 +102,7 @@ int run_copy(int mib, int steps) {
 
 int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024";
-  int steps = 20, warmup = 3, copy_mib = 0;
+  int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
   unsigned skip = 0;
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -118,6 +118,7 @@ int main(int argc, char** argv) {
     else if (a == "--warmup") warmup = std::atoi(next());
     else if (a == "--skip") skip = (unsigned)std::strtoul(next(), nullptr, 0);
     else if (a == "--copy-mib") copy_mib = std::atoi(next());
+    else if (a == "--wg-per-cu") wg_per_cu = std::atoi(next());
     else {
       std::fprintf(stderr, "unknown argument %s\n", a.c_str());
       return 1;
@@ -148,6 +149,7 @@ int main(int argc, char** argv) {
   cfg.adam_eps = 1e-8;
   cfg.weight_decay = 0.01;
   cfg.clip_norm = 1.0;
+  cfg.wg_per_cu = wg_per_cu;
   moe_step_t h = nullptr;
   if (moe_step_create(&cfg, &h) != MOE_OK) {
     std::fprintf(stderr, "moe_step_create: %s\n", moe_step_last_error(nullptr));
@@ -236,8 +238,8 @@ int main(int argc, char** argv) {
   }
   float ms = 0.f;
   CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
-  std::printf("%s skip=0x%02x: %d updates, %.4f ms/update, %.0f tokens/s\n", sh->name, skip, steps, ms / steps,
-              sh->T * steps / (ms * 1e-3));
+  std::printf("%s skip=0x%02x grid=%d: %d updates, %.4f ms/update, %.0f tokens/s\n", sh->name, skip,
+              moe_step_grid_size(h), steps, ms / steps, sh->T * steps / (ms * 1e-3));
   moe_step_destroy(h);
   for (void* p : {dx_in, dt, (void*)params, (void*)grads, (void*)m, (void*)v, (void*)dxg, (void*)stats})
     CHECK_HIP(hipFree(p));

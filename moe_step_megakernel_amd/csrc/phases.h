@@ -860,6 +860,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   const float4* G_ = reinterpret_cast<const float4*>(p.grads);
   float4* M_ = reinterpret_cast<float4*>(p.m);
   float4* V_ = reinterpret_cast<float4*>(p.v);
+  // every parameter, gradient and moment is touched once per update: stream them
+  // with non-temporal loads and stores so they do not evict reused data
+  typedef float nt4 __attribute__((ext_vector_type(4)));
   auto adamw4 = [&](float4& w, const float4& g, float4& m, float4& v) {
     float* wv = &w.x;
     const float* gv = &g.x;
@@ -875,9 +878,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
     }
   };
   auto store4 = [&](long i, const float4& w, const float4& m, const float4& v) {
-    P_[i] = w;
-    M_[i] = m;
-    V_[i] = v;
+    __builtin_nontemporal_store(nt4{w.x, w.y, w.z, w.w}, reinterpret_cast<nt4*>(P_ + i));
+    __builtin_nontemporal_store(nt4{m.x, m.y, m.z, m.w}, reinterpret_cast<nt4*>(M_ + i));
+    __builtin_nontemporal_store(nt4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt4*>(V_ + i));
     if (p.shadow && i >= nr4) {
       uint2 s;
       s.x = pack_bf16x2(w.x, w.y);
@@ -885,17 +888,21 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
       reinterpret_cast<uint2*>(p.shadow)[i - nr4] = s;
     }
   };
-  constexpr int U = 2;
+  constexpr int U = 4;
   const long stride = (long)G * kThreads;
   long i = (long)lwg * kThreads + tid;
   for (; i + (U - 1) * stride < P4; i += U * stride) {
     float4 w[U], g[U], m[U], v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      w[u] = P_[i + u * stride];
-      g[u] = G_[i + u * stride];
-      m[u] = M_[i + u * stride];
-      v[u] = V_[i + u * stride];
+      nt4 a0 = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(P_ + i + u * stride));
+      nt4 a1 = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(G_ + i + u * stride));
+      nt4 a2 = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(M_ + i + u * stride));
+      nt4 a3 = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(V_ + i + u * stride));
+      w[u] = make_float4(a0.x, a0.y, a0.z, a0.w);
+      g[u] = make_float4(a1.x, a1.y, a1.z, a1.w);
+      m[u] = make_float4(a2.x, a2.y, a2.z, a2.w);
+      v[u] = make_float4(a3.x, a3.y, a3.z, a3.w);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

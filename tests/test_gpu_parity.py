@@ -36,7 +36,9 @@ def _check_routing(cfg, inp, out, w_router):
         zr = oracle.router_logits(x, w_router, inp.router_bias)
         assert rel_l2(z, zr) < 1e-5
         diff = int((oracle.token_topk(zr, cfg.top_k) != ref_idx).any(axis=1).sum())
-        say(f"  microbatch {mb}: tokens routed differently by FP64 logits: {diff}")
+        if mb == 0 or mb == cfg.microbatches - 1:
+            say(f"  microbatch {mb}: tokens routed differently by FP64 logits: {diff}; "
+                f"rows per expert min {counts.min()} max {counts.max()}")
 
 
 def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0):
@@ -145,3 +147,25 @@ def test_zero_tokens_only_decays():
         assert rel_l2(run.layer.params.cpu().numpy(), p0 * (1 - cfg.lr * cfg.weight_decay)) < 1e-7
     finally:
         run.close()
+
+
+# ----------------------------------------------------------------------------
+# The full-size workloads, in the launch configuration bench.py times
+# ----------------------------------------------------------------------------
+@pytest.mark.timeout(900)
+def test_bf16_32x1024_full_size():
+    cfg = synth.CONFIGS["bf16_32x1024"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL, steps=1)
+
+
+@pytest.mark.timeout(900)
+def test_top8_4x1024_full_size():
+    cfg = synth.CONFIGS["top8_4x1024"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL, steps=2)
+
+
+@pytest.mark.timeout(1200)
+def test_zipf_16x8x1024_accumulated_full_size():
+    cfg = synth.CONFIGS["zipf_16x8x1024"]
+    inp = synth.make_inputs(cfg, 0)
+    _run_and_compare(cfg, inp, BF16_TOL, steps=1)
