@@ -118,6 +118,8 @@ struct moe_step {
   float* loss_part;
   float* norm_part;
   uint16_t* shadow;
+  void* xs;
+  char* zero;
   unsigned* ctrl;
 };
 
@@ -229,6 +231,8 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const size_t o_loss = take((size_t)h->grid * 4);
   const size_t o_norm = take((size_t)(n10 + n11 + nrr) * 4);
   const size_t o_shadow = cfg->dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
+  const size_t o_xs = cfg->dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
+  const size_t o_zero = take(256);
   h->arena_bytes = off;
 
   he = hipMalloc(reinterpret_cast<void**>(&h->arena), h->arena_bytes);
@@ -256,6 +260,8 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   h->loss_part = reinterpret_cast<float*>(a + o_loss);
   h->norm_part = reinterpret_cast<float*>(a + o_norm);
   h->shadow = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a + o_shadow) : nullptr;
+  h->xs = cfg->dtype == MOE_DTYPE_BF16 ? a + o_xs : nullptr;
+  h->zero = a + o_zero;
 
   // the arena starts zeroed (every stored index is then in range) and so do
   // the barrier words and status (synchronous; not part of any run)
@@ -379,6 +385,8 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
   p.loss_part = h->loss_part;
   p.norm_part = h->norm_part;
   p.shadow = h->shadow;
+  p.xs = h->xs;
+  p.zero = h->zero;
   p.ctrl.gen = h->ctrl;
   p.ctrl.status = h->ctrl + 32;
   p.ctrl.abort = h->ctrl + 64;

@@ -23,7 +23,7 @@ namespace moe {
 
 constexpr int kPhases = 8;
 constexpr int kMetaBytes = 2048;
-constexpr int kScratchBytes = gemm::LDS_BYTES;
+constexpr int kScratchBytes = gemm::LDS_BYTES > gemm::DMA_LDS_BYTES ? gemm::LDS_BYTES : gemm::DMA_LDS_BYTES;
 constexpr int kSmemBytes = kMetaBytes + kScratchBytes;
 constexpr int kRouterTokens = 256;   // tokens per router-gradient partial
 constexpr int kRouterBlockTokens = 32;
@@ -81,6 +81,8 @@ struct KParams {
   float* loss_part;  // [G]
   float* norm_part;  // [n10 + n11 + nr]
   uint16_t* shadow;  // [2*E*d*f] bf16 copy of W1 | W2 (bf16 mode)
+  void* xs;          // [N, d] token rows in expert order (bf16 mode), written by GEMM 1
+  const char* zero;  // 256 zero bytes (source of out-of-range tile elements)
   Ctrl ctrl;
 };
 
@@ -416,7 +418,7 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
     gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1, 0, d, f,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
-    gemm::tile<T, false, true>(lds, A, B, d, [&](int r, int c, const float (&h)[8]) {
+    auto epi = [&](int r, int c, const float (&h)[8]) {
       if (r < mrows && n0 + c < f) {
         F8 a, da;
 #pragma unroll
@@ -425,7 +427,27 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
         st8(act + o, a);
         st8(gp + o, da);
       }
-    });
+    };
+    if constexpr (sizeof(T) == 2) {
+      if (nt == 0) {
+        // the first column block also writes the gathered token rows in expert
+        // order, for the dW1 product (its k runs over these rows)
+        uint16_t* xs = reinterpret_cast<uint16_t*>(p.xs);
+        auto sink = [&](int kt, const char* st) {
+          for (int idx = threadIdx.x; idx < gemm::BM * 8; idx += kThreads) {
+            const int r = idx >> 3, u = idx & 7;
+            const int col = kt * 64 + u * 8;
+            if (r < mrows && col < d)
+              *reinterpret_cast<uint4*>(xs + (long)(p0 + r) * d + col) = gemm::dma_krows_unit(st, r, u);
+          }
+        };
+        gemm::tile<T, false, true>(lds, A, B, d, p.zero, epi, sink);
+      } else {
+        gemm::tile<T, false, true>(lds, A, B, d, p.zero, epi);
+      }
+    } else {
+      gemm::tile<T, false, true>(lds, A, B, d, p.zero, epi);
+    }
   }
 }
 
@@ -449,7 +471,7 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
     gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1, 0, f, d,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
-    gemm::tile<T, false, true>(lds, A, B, f, [&](int r, int c, const float (&v)[8]) {
+    gemm::tile<T, false, true>(lds, A, B, f, p.zero, [&](int r, int c, const float (&v)[8]) {
       if (r < mrows && n0 + c < d) {
         F8 o;
 #pragma unroll
@@ -575,7 +597,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, pe, ce, d, n0};
       float* g = gw2 + (long)e * f * d;
       float sq = 0.f;
-      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, const float (&v)[8]) {
+      gemm::tile<T, true, true>(lds, A, B, ce, p.zero, [&](int r, int c, const float (&v)[8]) {
         if (m0 + r < f && n0 + c < d) {
           float* q = g + (long)(m0 + r) * d + n0 + c;
           F8 nv;
@@ -606,7 +628,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, f - nt * gemm::BN), d, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(lds, A, B, d, [&](int r, int c, const float (&v)[8]) {
+      gemm::tile<T, false, false>(lds, A, B, d, p.zero, [&](int r, int c, const float (&v)[8]) {
         if (r < mrows && n0 + c < f) {
           const long o = (long)(p0 + r) * f + n0 + c;
           F8 g8 = ld8(gp + o);
@@ -696,11 +718,14 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       const int mt = rem / NT11, nt = rem % NT11;
       const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
       const int pe = meta.off[e], ce = meta.cnt[e];
-      gemm::Operand A{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, pe, ce, d, m0};
+      // bf16: the token rows gathered by GEMM 1; fp32: x through perm
+      const gemm::Operand A = (sizeof(T) == 2)
+          ? gemm::Operand{reinterpret_cast<const char*>(p.xs), d, nullptr, 1, pe, ce, d, m0}
+          : gemm::Operand{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, pe, ce, d, m0};
       gemm::Operand B{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, pe, ce, f, n0};
       float* g = gw1 + (long)e * d * f;
       float sq = 0.f;
-      gemm::tile<T, true, true>(lds, A, B, ce, [&](int r, int c, const float (&v)[8]) {
+      gemm::tile<T, true, true>(lds, A, B, ce, p.zero, [&](int r, int c, const float (&v)[8]) {
         if (m0 + r < d && n0 + c < f) {
           float* q = g + (long)(m0 + r) * f + n0 + c;
           F8 nv;
@@ -731,7 +756,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, d - nt * gemm::BN), f, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(lds, A, B, f, [&](int r, int c, const float (&v)[8]) {
+      gemm::tile<T, false, false>(lds, A, B, f, p.zero, [&](int r, int c, const float (&v)[8]) {
         if (r < mrows && n0 + c < d) {
           F8 o;
 #pragma unroll

@@ -60,6 +60,9 @@ __device__ __forceinline__ long map_row(const Operand& o, int p) {
   return o.map ? (long)(o.map[p] / o.div) : (long)p;
 }
 
+constexpr int CROW = BN + 4;   // fp32 words per LDS row of the staged tile
+static_assert(BM * CROW * 4 <= LDS_BYTES, "staged tile must fit");
+
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
@@ -218,11 +221,39 @@ __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16
 // epilogue's global accesses are 16- or 32-byte vectors and its code exists
 // once instead of once per accumulator.  K is the contraction length; MN_A /
 // MN_B select the MN-rows layout for that operand.
-constexpr int CROW = BN + 4;   // fp32 words per LDS row of the staged tile
-static_assert(BM * CROW * 4 <= LDS_BYTES, "staged tile must fit");
+
+// Stages the accumulators through LDS (fp32, 128 x CROW) and calls epi(row,
+// col, v) on 8-column row pieces.  The caller has made the LDS free.
+template <class Epi>
+__device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2], Epi&& epi) {
+  float* cs = reinterpret_cast<float*>(lds);
+  {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w & 1, wn = w >> 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = wn * 64 + j * 32 + (lane & 31);
+          cs[row * CROW + col] = acc[i][j][r];
+        }
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int it = threadIdx.x; it < BM * (BN / 8); it += kThreads) {
+    const int row = it >> 4, col = (it & 15) * 8;
+    const float4 lo = *reinterpret_cast<const float4*>(cs + row * CROW + col);
+    const float4 hi = *reinterpret_cast<const float4*>(cs + row * CROW + col + 4);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    epi(row, col, v);
+  }
+}
 
 template <typename T, bool MN_A, bool MN_B, class Epi>
-__device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi) {
+__device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi) {
   using SA = Stager<T, MN_A>;
   using SB = Stager<T, MN_B>;
   f32x16_t acc[2][2];
@@ -262,31 +293,243 @@ __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand&
       __syncthreads();
     }
   }
-  // stage the accumulators: lane owns 4 consecutive rows of one column per block
-  float* cs = reinterpret_cast<float*>(lds);
-  {
+  epilogue(lds, acc, epi);
+}
+
+
+// ---------------------------------------------------------------------------
+// bf16 tiles: direct-to-LDS loads (global_load_lds_dwordx4), four LDS stages,
+// so the loads of three k-tiles are in flight while the matrix cores work on
+// the fourth, at no register cost.  Each wave instruction fills 1 KB of LDS
+// contiguously (lane l -> bytes 16l..16l+15), so bank conflicts on the MFMA
+// reads are avoided by an XOR swizzle of 16-byte units instead of padding:
+//  * K-rows operand, LDS [128 rows][128 B]: logical k-unit u of row r sits in
+//    physical unit u ^ ((r >> 1) & 7);
+//  * MN-rows operand, LDS [64 k-rows][256 B]: logical 16-byte column slot s of
+//    k-row r sits in physical slot s ^ (2 * (r & 3)).
+// Lanes whose element is out of range load from a zero page instead.  The
+// loop waits on the vector-memory counter itself and synchronises with a bare
+// s_barrier, so the loads of later k-tiles stay in flight across it.
+// ---------------------------------------------------------------------------
+constexpr int DMA_STAGES = 4;
+constexpr int DMA_OP = 16384;                  // bytes per operand per stage
+constexpr int DMA_STAGE = 2 * DMA_OP;
+constexpr int DMA_LDS_BYTES = DMA_STAGES * DMA_STAGE;   // 131,072 bytes
+static_assert(BM * CROW * 4 <= DMA_LDS_BYTES, "staged tile must fit");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) for n in {0, 8, 16}; expcnt and lgkmcnt left alone
+__device__ __forceinline__ void wait_vm(int outstanding_tiles) {
+  if (outstanding_tiles >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);
+  else if (outstanding_tiles == 1) __builtin_amdgcn_s_waitcnt(0x0F78);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+template <bool MN>
+struct DmaOp {
+  // per lane and instruction i (0..3): K-rows -> source row start (bytes) or
+  // -1, and the logical k-unit this lane carries; MN-rows -> k-row within the
+  // stage and the column byte offset (or -1)
+  long rowbase[4];
+  int unit[4];
+  long coloff;
+  int krow0;
+
+  __device__ __forceinline__ void init(const Operand& o) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w & 1, wn = w >> 1;
+    if constexpr (!MN) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = wn * 64 + j * 32 + (lane & 31);
-          cs[row * CROW + col] = acc[i][j][r];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * w + i) + (lane >> 3);
+        unit[i] = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
+        rowbase[i] = (row < o.nrows) ? map_row(o, o.p0 + row) * o.ld * 2 + unit[i] * 16 : -1;
+      }
+    } else {
+      const int slot = (lane & 15) ^ (2 * ((lane >> 4) & 3));
+      const int mn = o.mn0 + slot * 8;
+      coloff = (mn < o.lim) ? (long)mn * 2 : -1;
+      krow0 = 16 * w + (lane >> 4);   // + 4 i
+    }
   }
-  __syncthreads();
-#pragma unroll 1
-  for (int it = threadIdx.x; it < BM * (BN / 8); it += kThreads) {
-    const int row = it >> 4, col = (it & 15) * 8;
-    const float4 lo = *reinterpret_cast<const float4*>(cs + row * CROW + col);
-    const float4 hi = *reinterpret_cast<const float4*>(cs + row * CROW + col + 4);
-    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    epi(row, col, v);
+
+  __device__ __forceinline__ void issue(const Operand& o, int kt, char* st, const char* zero) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* src = zero;
+      if constexpr (!MN) {
+        if (rowbase[i] >= 0 && kt * 64 + unit[i] * 8 < o.lim) src = o.base + rowbase[i] + (long)kt * 128;
+      } else {
+        const int kk = kt * 64 + krow0 + 4 * i;
+        if (coloff >= 0 && kk < o.nrows) src = o.base + (long)(o.p0 + kk) * o.ld * 2 + coloff;
+      }
+      dma16(src, st + (4 * w + i) * 1024);
+    }
   }
+
+};
+
+// LDS reads of data written by the direct-to-LDS loads are issued as inline
+// assembly that ends in its own lgkmcnt wait: the compiler cannot tell that
+// they read a different stage than the loads still in flight and would
+// otherwise drain every outstanding load before each read.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// Reads logical 16-byte unit u of row r from a K-rows DMA stage.
+__device__ __forceinline__ uint4 dma_krows_unit(const char* st, int r, int u) {
+  const uint32_t a = lds_addr(st + r * 128 + ((u ^ ((r >> 1) & 7)) << 4));
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// LDS byte address of this lane's fragment (K-rows: the b128 read; MN-rows:
+// the first of the two transpose reads, the second is 1024 bytes further)
+template <bool MN>
+__device__ __forceinline__ uint32_t dma_frag_addr(const char* st, int row0, int chunk) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (!MN) {
+    const int r = row0 + (lane & 31);
+    const int u = chunk * 2 + (lane >> 5);
+    return lds_addr(st + r * 128 + ((u ^ ((r >> 1) & 7)) << 4));
+  } else {
+    const int g = lane >> 4, j = lane & 15;
+    const int r = chunk * 16 + 8 * (g >> 1) + (j >> 2);
+    const int c = row0 + 16 * (g & 1) + 4 * (j & 3);
+    return lds_addr(st + r * 256 + (((c >> 3) ^ (2 * (r & 3))) << 4) + (c & 7) * 2);
+  }
+}
+
+__device__ __forceinline__ uint4 join(const u32x2_t& lo, const u32x2_t& hi) {
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// The four fragments (2 of A, 2 of B) of one 16-element k chunk.
+template <bool MN_A, bool MN_B>
+__device__ __forceinline__ void dma_frags(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, uint4 (&a)[2],
+                                          uint4 (&b)[2]) {
+  if constexpr (!MN_A && !MN_B) {
+    u32x4_t x0, x1, y0, y1;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
+    a[0] = make_uint4(x0.x, x0.y, x0.z, x0.w);
+    a[1] = make_uint4(x1.x, x1.y, x1.z, x1.w);
+    b[0] = make_uint4(y0.x, y0.y, y0.z, y0.w);
+    b[1] = make_uint4(y1.x, y1.y, y1.z, y1.w);
+  } else if constexpr (!MN_A && MN_B) {
+    u32x4_t x0, x1;
+    u32x2_t y0l, y0h, y1l, y1h;
+    asm volatile(
+        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\t"
+        "ds_read_b64_tr_b16 %2, %8\n\tds_read_b64_tr_b16 %3, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %9\n\tds_read_b64_tr_b16 %5, %9 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(y0l), "=&v"(y0h), "=&v"(y1l), "=&v"(y1h)
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
+    a[0] = make_uint4(x0.x, x0.y, x0.z, x0.w);
+    a[1] = make_uint4(x1.x, x1.y, x1.z, x1.w);
+    b[0] = join(y0l, y0h);
+    b[1] = join(y1l, y1h);
+  } else {
+    static_assert(MN_A && MN_B, "layout combination not used");
+    u32x2_t x0l, x0h, x1l, x1h, y0l, y0h, y1l, y1h;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\tds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\tds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\tds_read_b64_tr_b16 %7, %11 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x0l), "=&v"(x0h), "=&v"(x1l), "=&v"(x1h), "=&v"(y0l), "=&v"(y0h), "=&v"(y1l), "=&v"(y1h)
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
+    a[0] = join(x0l, x0h);
+    a[1] = join(x1l, x1h);
+    b[0] = join(y0l, y0h);
+    b[1] = join(y1l, y1h);
+  }
+}
+
+// bf16 tile through the DMA pipeline.  sink(kt, stageA) runs once per k-tile
+// after its data landed (all waves), before any wave reads it for the MFMAs.
+template <bool MN_A, bool MN_B, class Epi, class Sink>
+__device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
+                                         Epi&& epi, Sink&& sink) {
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  DmaOp<MN_A> da;
+  DmaOp<MN_B> db;
+  da.init(A);
+  db.init(B);
+  const int nk = (K + 63) / 64;
+  __syncthreads();  // the previous user of this LDS is done
+  for (int j = 0; j < DMA_STAGES - 1 && j < nk; ++j) {
+    char* st = lds + j * DMA_STAGE;
+    da.issue(A, j, st, zero);
+    db.issue(B, j, st + DMA_OP, zero);
+  }
+  const int w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm(min(DMA_STAGES - 2, nk - 1 - kt));
+    lds_barrier();
+    const char* st = lds + (kt % DMA_STAGES) * DMA_STAGE;
+    sink(kt, st);
+    if (kt + DMA_STAGES - 1 < nk) {
+      char* nx = lds + ((kt + DMA_STAGES - 1) % DMA_STAGES) * DMA_STAGE;
+      da.issue(A, kt + DMA_STAGES - 1, nx, zero);
+      db.issue(B, kt + DMA_STAGES - 1, nx + DMA_OP, zero);
+    }
+#pragma unroll
+    for (int chunk = 0; chunk < 4; ++chunk) {
+      uint4 a[2], b[2];
+      dma_frags<MN_A, MN_B>(dma_frag_addr<MN_A>(st, wm * 64, chunk), dma_frag_addr<MN_A>(st, wm * 64 + 32, chunk),
+                            dma_frag_addr<MN_B>(st + DMA_OP, wn * 64, chunk),
+                            dma_frag_addr<MN_B>(st + DMA_OP, wn * 64 + 32, chunk), a, b);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                             __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();  // every wave is done with the stages
+  epilogue(lds, acc, epi);
+}
+
+struct NoSink {
+  __device__ __forceinline__ void operator()(int, const char*) const {}
+};
+
+// One tile: bf16 through the DMA pipeline, fp32 through register staging.
+template <typename T, bool MN_A, bool MN_B, class Epi, class Sink = NoSink>
+__device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
+                                     Epi&& epi, Sink&& sink = Sink()) {
+  if constexpr (sizeof(T) == 2) tile_dma<MN_A, MN_B>(lds, A, B, K, zero, epi, sink);
+  else tile_reg<T, MN_A, MN_B>(lds, A, B, K, epi);
 }
 
 }  // namespace gemm
