@@ -58,6 +58,39 @@ __device__ __forceinline__ F8 ld8(const float* p) {
   return r;
 }
 
+// 8 consecutive elements as loaded (16 bytes of bf16, 32 of fp32), converted
+// to F8 only where they are used
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  uint4 u;
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+};
+
+__device__ __forceinline__ Raw8<uint16_t> ldr8(const uint16_t* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+__device__ __forceinline__ Raw8<float> ldr8(const float* p) {
+  return {reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+}
+
+__device__ __forceinline__ F8 cvt8(const Raw8<uint16_t>& r) {
+  F8 f;
+  f.v[0] = bf16_to_f32(r.u.x & 0xffffu); f.v[1] = bf16_to_f32(r.u.x >> 16);
+  f.v[2] = bf16_to_f32(r.u.y & 0xffffu); f.v[3] = bf16_to_f32(r.u.y >> 16);
+  f.v[4] = bf16_to_f32(r.u.z & 0xffffu); f.v[5] = bf16_to_f32(r.u.z >> 16);
+  f.v[6] = bf16_to_f32(r.u.w & 0xffffu); f.v[7] = bf16_to_f32(r.u.w >> 16);
+  return f;
+}
+__device__ __forceinline__ F8 cvt8(const Raw8<float>& r) {
+  F8 f;
+  f.v[0] = r.a.x; f.v[1] = r.a.y; f.v[2] = r.a.z; f.v[3] = r.a.w;
+  f.v[4] = r.b.x; f.v[5] = r.b.y; f.v[6] = r.b.z; f.v[7] = r.b.w;
+  return f;
+}
+
 __device__ __forceinline__ void st8(uint16_t* p, const F8& f) {
   uint4 u;
   u.x = pack_bf16x2(f.v[0], f.v[1]);
@@ -101,16 +134,26 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// tanh-form GELU and its derivative (fp32), with the device tanhf.
+// tanh-form GELU and its derivative (fp32).  With u = sqrt(2/pi) (h + 0.044715
+// h^3) and r = 1 / (1 + e^{2u}), the identity tanh(u) = 1 - 2r gives
+//   gelu(h)  = h (1 - r)
+//   gelu'(h) = (1 - r) + 2 h r (1 - r) sqrt(2/pi) (1 + 3 * 0.044715 h^2)
+// and 1 - r = e^{2u} r keeps full relative precision where e^{2u} is small.
+// e^{2u} comes from the hardware base-2 exponential and r from the hardware
+// reciprocal (about 1 ulp each); the exponent is capped at 2^64 so that
+// e^{2u} r stays finite.
 constexpr float kSqrt2OverPi = 0.7978845608028654f;
 constexpr float kGeluCubic = 0.044715f;
+constexpr float kTwoLog2e = 2.8853900817779268f;   // 2 / ln 2
 
 __device__ __forceinline__ void gelu_and_grad(float h, float& a, float& da) {
   const float h2 = h * h;
-  const float u = kSqrt2OverPi * (h + kGeluCubic * h2 * h);
-  const float th = tanhf(u);
-  a = 0.5f * h * (1.f + th);
-  da = 0.5f * (1.f + th) + 0.5f * h * (1.f - th * th) * kSqrt2OverPi * (1.f + 3.f * kGeluCubic * h2);
+  const float t = fminf(kTwoLog2e * kSqrt2OverPi * h * (1.f + kGeluCubic * h2), 64.f);   // 2u log2(e)
+  const float e = __builtin_amdgcn_exp2f(t);
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  const float s = e * r;   // 1 - r
+  a = h * s;
+  da = s + 2.f * kSqrt2OverPi * h * r * s * (1.f + 3.f * kGeluCubic * h2);
 }
 
 // ---------------------------------------------------------------------------
@@ -149,19 +192,25 @@ __device__ __forceinline__ bool wait_for(const Ctrl& c, const unsigned* p, unsig
   return true;
 }
 
-// Grid-wide barrier.  Every wave first releases its own global writes at agent
-// scope (waits for its stores and writes dirty L2 lines back, so the other XCDs
-// see them).  A workgroup other than 0 then stores `target` into its arrival
-// slot and polls the generation word; workgroup 0 polls all arrival slots in
-// parallel (one per thread), acquires, and stores `target` into the generation
-// word.  Polling uses plain relaxed loads with a sleep in between, and each
-// poller acquires once afterwards, so waiting does not keep invalidating the
-// caches under the workgroups still working.  Returns false if a wait timed out
-// or another workgroup already gave up; the caller then skips all further
-// phases so that every workgroup still exits.
+// Grid-wide barrier.  Every wave first waits until its own stores have
+// reached L2; after a workgroup barrier one wave releases at agent scope for
+// the whole workgroup (writes the XCD's dirty L2 lines back, so the other XCDs
+// see them) -- one L2 write-back per workgroup instead of one per wave.  A
+// workgroup other than 0 then stores `target` into its arrival slot (relaxed:
+// the fence before it orders the data) and polls the generation word;
+// workgroup 0 polls all arrival slots in parallel (one per thread), acquires,
+// and stores `target` into the generation word.  Polling uses plain relaxed
+// loads with a sleep in between, and each poller acquires once afterwards, so
+// waiting does not keep invalidating the caches under the workgroups still
+// working.  Returns false if a wait timed out or another workgroup already
+// gave up; the caller then skips all further phases so that every workgroup
+// still exits.
 __device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, unsigned* lds_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // release once per workgroup: every wave's stores have reached L2 before the
+  // barrier; one wave then writes the XCD's dirty L2 lines back
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
+  if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   if (threadIdx.x == 0) *lds_flag = 1u;
   __syncthreads();
   if (blockIdx.x == 0) {
@@ -177,7 +226,7 @@ __device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, uns
     if (threadIdx.x == 0 && *lds_flag != 0u)
       __hip_atomic_store(c.gen, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   } else if (threadIdx.x == 0) {
-    __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!wait_for(c, c.gen, target)) *lds_flag = 0u;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }

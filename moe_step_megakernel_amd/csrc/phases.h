@@ -25,7 +25,7 @@ constexpr int kPhases = 8;
 constexpr int kMetaBytes = 2048;
 constexpr int kScratchBytes = gemm::LDS_BYTES > gemm::DMA_LDS_BYTES ? gemm::LDS_BYTES : gemm::DMA_LDS_BYTES;
 constexpr int kSmemBytes = kMetaBytes + kScratchBytes;
-constexpr int kRouterTokens = 256;   // tokens per router-gradient partial
+constexpr int kRouterTokens = 128;   // tokens per router-gradient partial
 constexpr int kRouterBlockTokens = 32;
 
 // Routing metadata kept in LDS for the whole launch (every workgroup computes
@@ -106,6 +106,19 @@ __device__ __forceinline__ Span xcd_span(int n) {
   const int G = gridDim.x;
   if ((G & 7) != 0) return {(int)blockIdx.x, n, G};
   const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per = G >> 3;
+  const int chunk = (n + 7) >> 3;
+  const int lo = min(n, x * chunk);
+  const int hi = min(n, lo + chunk);
+  return {lo + j, hi, per};
+}
+
+// As xcd_span, but the XCD's items go to its workgroups from the last one
+// down: a phase that deals several kinds of work gives its small trailing
+// kind to the workgroups that got the fewest items of the kinds before it.
+__device__ __forceinline__ Span xcd_span_last(int n) {
+  const int G = gridDim.x;
+  if ((G & 7) != 0) return {G - 1 - (int)blockIdx.x, n, G};
+  const int x = blockIdx.x & 7, per = G >> 3, j = per - 1 - (int)(blockIdx.x >> 3);
   const int chunk = (n + 7) >> 3;
   const int lo = min(n, x * chunk);
   const int hi = min(n, lo + chunk);
@@ -579,7 +592,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 
   // each kind of work is dealt over the XCDs on its own, so every XCD gets the
   // same mix (the kinds differ a lot in cost)
-  const Span s10 = xcd_span(n10), s9 = xcd_span(n9), sr = xcd_span(nr);
+  const Span s10 = xcd_span(n10), s9 = xcd_span(n9), sr = xcd_span_last(nr);
   const int c10 = max(0, ceil_div(s10.end - s10.begin, s10.step));
   const int c9 = max(0, ceil_div(s9.end - s9.begin, s9.step));
   const int cr = max(0, ceil_div(sr.end - sr.begin, sr.step));
@@ -597,23 +610,24 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, pe, ce, d, n0};
       float* g = gw2 + (long)e * f * d;
       float sq = 0.f;
-      gemm::tile<T, true, true>(lds, A, B, ce, p.zero, [&](int r, int c, const float (&v)[8]) {
-        if (m0 + r < f && n0 + c < d) {
-          float* q = g + (long)(m0 + r) * d + n0 + c;
-          F8 nv;
-          if (zero_grad) {
+      gemm::tile<T, true, true>(
+          lds, A, B, ce, p.zero,
+          [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
+            if (m0 + r < f && n0 + c < d) {
+              F8 nv = cvt8(old);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) nv.v[u] = v[u];
-          } else {
-            nv = ld8(q);
+              for (int u = 0; u < 8; ++u) nv.v[u] = zero_grad ? v[u] : nv.v[u] + v[u];
+              st8(g + (long)(m0 + r) * d + n0 + c, nv);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) nv.v[u] += v[u];
-          }
-          st8(q, nv);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
-        }
-      });
+              for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
+            }
+          },
+          gemm::NoSink(),
+          [&](int r, int c) {
+            Raw8<float> old{};
+            if (!zero_grad && m0 + r < f && n0 + c < d) old = ldr8(g + (long)(m0 + r) * d + n0 + c);
+            return old;
+          });
       const float s = block_sum(sq, meta.red);
       if (tid == 0) p.norm_part[item] = s;
     } else if (item < n10 + n9) {
@@ -628,17 +642,24 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, f - nt * gemm::BN), d, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(lds, A, B, d, p.zero, [&](int r, int c, const float (&v)[8]) {
-        if (r < mrows && n0 + c < f) {
-          const long o = (long)(p0 + r) * f + n0 + c;
-          F8 g8 = ld8(gp + o);
+      gemm::tile<T, false, false>(
+          lds, A, B, d, p.zero,
+          [&](int r, int c, const float (&v)[8], const Raw8<T>& graw) {
+            if (r < mrows && n0 + c < f) {
+              F8 g8 = cvt8(graw);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) g8.v[u] *= v[u];
-          st8(dh + o, g8);
-        }
-      });
+              for (int u = 0; u < 8; ++u) g8.v[u] *= v[u];
+              st8(dh + (long)(p0 + r) * f + n0 + c, g8);
+            }
+          },
+          gemm::NoSink(),
+          [&](int r, int c) {
+            Raw8<T> graw{};
+            if (r < mrows && n0 + c < f) graw = ldr8(gp + (long)(p0 + r) * f + n0 + c);
+            return graw;
+          });
     } else {
-      // router-gradient partial: tokens [rc*256, +256) x columns [cc*256, +256)
+      // router-gradient partial: tokens [rc*kRouterTokens, +kRouterTokens) x columns [cc*256, +256)
       const int ir = item - n10 - n9;
       const int rc = ir / CCH, cc = ir % CCH;
       float* acc = reinterpret_cast<float*>(lds);                      // [E][256]
@@ -704,7 +725,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
-  const Span s11 = xcd_span(n11), s12 = xcd_span(n12), srr = xcd_span(nrr);
+  const Span s11 = xcd_span(n11), s12 = xcd_span(n12), srr = xcd_span_last(nrr);
   const int c11 = max(0, ceil_div(s11.end - s11.begin, s11.step));
   const int c12 = max(0, ceil_div(s12.end - s12.begin, s12.step));
   const int crr = max(0, ceil_div(srr.end - srr.begin, srr.step));
@@ -725,23 +746,24 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, pe, ce, f, n0};
       float* g = gw1 + (long)e * d * f;
       float sq = 0.f;
-      gemm::tile<T, true, true>(lds, A, B, ce, p.zero, [&](int r, int c, const float (&v)[8]) {
-        if (m0 + r < d && n0 + c < f) {
-          float* q = g + (long)(m0 + r) * f + n0 + c;
-          F8 nv;
-          if (zero_grad) {
+      gemm::tile<T, true, true>(
+          lds, A, B, ce, p.zero,
+          [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
+            if (m0 + r < d && n0 + c < f) {
+              F8 nv = cvt8(old);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) nv.v[u] = v[u];
-          } else {
-            nv = ld8(q);
+              for (int u = 0; u < 8; ++u) nv.v[u] = zero_grad ? v[u] : nv.v[u] + v[u];
+              st8(g + (long)(m0 + r) * f + n0 + c, nv);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) nv.v[u] += v[u];
-          }
-          st8(q, nv);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
-        }
-      });
+              for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
+            }
+          },
+          gemm::NoSink(),
+          [&](int r, int c) {
+            Raw8<float> old{};
+            if (!zero_grad && m0 + r < d && n0 + c < f) old = ldr8(g + (long)(m0 + r) * f + n0 + c);
+            return old;
+          });
       const float s = block_sum(sq, meta.red);
       if (tid == 0) p.norm_part[n10 + item] = s;
     } else if (item < n11 + n12) {
@@ -756,14 +778,17 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, d - nt * gemm::BN), f, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(lds, A, B, f, p.zero, [&](int r, int c, const float (&v)[8]) {
-        if (r < mrows && n0 + c < d) {
-          F8 o;
+      gemm::tile<T, false, false>(
+          lds, A, B, f, p.zero,
+          [&](int r, int c, const float (&v)[8], int slot) {
+            if (r < mrows && n0 + c < d) {
+              F8 o;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) o.v[u] = v[u];
-          st8(dxs + (long)p.perm[p0 + r] * d + n0 + c, o);
-        }
-      });
+              for (int u = 0; u < 8; ++u) o.v[u] = v[u];
+              st8(dxs + (long)slot * d + n0 + c, o);
+            }
+          },
+          gemm::NoSink(), [&](int r, int c) { return (r < mrows && n0 + c < d) ? p.perm[p0 + r] : 0; });
     } else {
       // dW_r[c][e] = sum over token chunks (ascending) of the partials
       const int ir = item - n11 - n12;

@@ -222,10 +222,29 @@ __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16
 // once instead of once per accumulator.  K is the contraction length; MN_A /
 // MN_B select the MN-rows layout for that operand.
 
+// No per-piece inputs for the epilogue.
+struct NoPre {
+  __device__ __forceinline__ int operator()(int, int) const { return 0; }
+};
+
 // Stages the accumulators through LDS (fp32, 128 x CROW) and calls epi(row,
-// col, v) on 8-column row pieces.  The caller has made the LDS free.
-template <class Epi>
-__device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2], Epi&& epi) {
+// col, v) on 8-column row pieces.  The caller has made the LDS free.  With a
+// `pre` functor, pre(row, col) is called for all of this thread's pieces
+// first, so the global loads it makes (inputs of the epilogue) are all in
+// flight together, and epi(row, col, v, pre_value) gets its result.
+template <class Epi, class Pre>
+__device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2], Epi&& epi, Pre&& pre) {
+  constexpr int kIt = BM * (BN / 8) / kThreads;
+  constexpr bool kPre = !__is_same(__remove_cvref(Pre), NoPre);
+  using PV = decltype(pre(0, 0));
+  PV pv[kPre ? kIt : 1];
+  if constexpr (kPre) {
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) {
+      const int it = threadIdx.x + j * kThreads;
+      pv[j] = pre(it >> 4, (it & 15) * 8);
+    }
+  }
   float* cs = reinterpret_cast<float*>(lds);
   {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -242,18 +261,30 @@ __device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2],
         }
   }
   __syncthreads();
+  if constexpr (kPre) {
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) {
+      const int it = threadIdx.x + j * kThreads;
+      const int row = it >> 4, col = (it & 15) * 8;
+      const float4 lo = *reinterpret_cast<const float4*>(cs + row * CROW + col);
+      const float4 hi = *reinterpret_cast<const float4*>(cs + row * CROW + col + 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      epi(row, col, v, pv[j]);
+    }
+  } else {
 #pragma unroll 1
-  for (int it = threadIdx.x; it < BM * (BN / 8); it += kThreads) {
-    const int row = it >> 4, col = (it & 15) * 8;
-    const float4 lo = *reinterpret_cast<const float4*>(cs + row * CROW + col);
-    const float4 hi = *reinterpret_cast<const float4*>(cs + row * CROW + col + 4);
-    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    epi(row, col, v);
+    for (int it = threadIdx.x; it < BM * (BN / 8); it += kThreads) {
+      const int row = it >> 4, col = (it & 15) * 8;
+      const float4 lo = *reinterpret_cast<const float4*>(cs + row * CROW + col);
+      const float4 hi = *reinterpret_cast<const float4*>(cs + row * CROW + col + 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      epi(row, col, v);
+    }
   }
 }
 
-template <typename T, bool MN_A, bool MN_B, class Epi>
-__device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi) {
+template <typename T, bool MN_A, bool MN_B, class Epi, class Pre>
+__device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi, Pre&& pre) {
   using SA = Stager<T, MN_A>;
   using SB = Stager<T, MN_B>;
   f32x16_t acc[2][2];
@@ -293,7 +324,7 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
       __syncthreads();
     }
   }
-  epilogue(lds, acc, epi);
+  epilogue(lds, acc, epi, pre);
 }
 
 
@@ -417,60 +448,133 @@ __device__ __forceinline__ uint32_t dma_frag_addr(const char* st, int row0, int 
   }
 }
 
-__device__ __forceinline__ uint4 join(const u32x2_t& lo, const u32x2_t& hi) {
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+// The fragments of one 16-element k chunk: a0/a1 for the two 32-row blocks of
+// A (m), b0/b1 for those of B (n), 8 bf16 per lane each.
+struct Frags {
+  u32x4_t a0, a1, b0, b1;
+};
+
+__device__ __forceinline__ u32x4_t join(const u32x2_t& lo, const u32x2_t& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
 }
 
-// The four fragments (2 of A, 2 of B) of one 16-element k chunk.
+// The k loop is software-pipelined by hand, two chunks deep: one asm block
+// issues the LDS reads of chunk c+2, runs the four MFMAs of chunk c, and then
+// waits only for the reads of chunk c+1 (issued one block earlier), so every
+// read has two blocks of matrix work to land.  Reads, MFMAs and the wait share
+// one block, and the fragments of chunk c+2 are next touched two blocks later,
+// after the wait that completes them; the compiler is never handed a register
+// whose read it could observe early.  Accumulators live in AGPRs.
+//   WAIT = 0: wait for every read; 1: leave this block's reads outstanding;
+//   -1: no wait.
+#define MOE_RD_K(d, a) "ds_read_b128 %[" d "], %[" a "]\n\t"
+#define MOE_RD_MN(d, a) "ds_read_b64_tr_b16 %[" d "l], %[" a "]\n\tds_read_b64_tr_b16 %[" d "h], %[" a "] offset:1024\n\t"
+#define MOE_MFMA4                                                   \
+  "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"      \
+  "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"      \
+  "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"      \
+  "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+#define MOE_ACC_OUT [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1])
+#define MOE_CUR_IN [a0] "v"(c.a0), [a1] "v"(c.a1), [b0] "v"(c.b0), [b1] "v"(c.b1)
+#define MOE_ADDR_IN [pa0] "v"(pa0), [pa1] "v"(pa1), [pb0] "v"(pb0), [pb1] "v"(pb1)
+// one pipeline block for a layout pair: READS issues the reads into the
+// output operands OUTS; NREAD is the number of LDS instructions in READS
+#define MOE_PIPE_BODY(READS, OUTS, NREAD, FINISH)                                                         \
+  if constexpr (MMA && WAIT == 0) {                                                                      \
+    asm volatile(READS MOE_MFMA4 "s_waitcnt lgkmcnt(0)" : OUTS, MOE_ACC_OUT : MOE_CUR_IN, MOE_ADDR_IN : "memory"); \
+  } else if constexpr (MMA && WAIT == 1) {                                                               \
+    asm volatile(READS MOE_MFMA4 "s_waitcnt lgkmcnt(" #NREAD ")"                                          \
+                 : OUTS, MOE_ACC_OUT : MOE_CUR_IN, MOE_ADDR_IN : "memory");                              \
+  } else if constexpr (MMA) {                                                                            \
+    asm volatile(READS MOE_MFMA4 : OUTS, MOE_ACC_OUT : MOE_CUR_IN, MOE_ADDR_IN : "memory");              \
+  } else if constexpr (WAIT == 0) {                                                                      \
+    asm volatile(READS "s_waitcnt lgkmcnt(0)" : OUTS : MOE_ADDR_IN : "memory");                           \
+  } else {                                                                                               \
+    asm volatile(READS : OUTS : MOE_ADDR_IN : "memory");                                                 \
+  }                                                                                                      \
+  FINISH
+
+#define MOE_PIPE_OUTS_KM [x0] "=&v"(x0), [x1] "=&v"(x1), [y0l] "=&v"(y0l), [y0h] "=&v"(y0h), [y1l] "=&v"(y1l), [y1h] "=&v"(y1h)
+#define MOE_PIPE_OUTS_KK [x0] "=&v"(x0), [x1] "=&v"(x1), [y0] "=&v"(y0), [y1] "=&v"(y1)
+#define MOE_PIPE_OUTS_MM [x0l] "=&v"(x0l), [x0h] "=&v"(x0h), [x1l] "=&v"(x1l), [x1h] "=&v"(x1h), [y0l] "=&v"(y0l), [y0h] "=&v"(y0h), [y1l] "=&v"(y1l), [y1h] "=&v"(y1h)
+
 template <bool MN_A, bool MN_B>
-__device__ __forceinline__ void dma_frags(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, uint4 (&a)[2],
-                                          uint4 (&b)[2]) {
-  if constexpr (!MN_A && !MN_B) {
-    u32x4_t x0, x1, y0, y1;
-    asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
-    a[0] = make_uint4(x0.x, x0.y, x0.z, x0.w);
-    a[1] = make_uint4(x1.x, x1.y, x1.z, x1.w);
-    b[0] = make_uint4(y0.x, y0.y, y0.z, y0.w);
-    b[1] = make_uint4(y1.x, y1.y, y1.z, y1.w);
-  } else if constexpr (!MN_A && MN_B) {
+struct Pipe;
+
+// A K-rows, B MN-rows (forward products)
+template <>
+struct Pipe<false, true> {
+  template <bool MMA, int WAIT>
+  __device__ __forceinline__ static void step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], uint32_t pa0,
+                                              uint32_t pa1, uint32_t pb0, uint32_t pb1) {
     u32x4_t x0, x1;
     u32x2_t y0l, y0h, y1l, y1h;
-    asm volatile(
-        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\t"
-        "ds_read_b64_tr_b16 %2, %8\n\tds_read_b64_tr_b16 %3, %8 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %4, %9\n\tds_read_b64_tr_b16 %5, %9 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(x0), "=&v"(x1), "=&v"(y0l), "=&v"(y0h), "=&v"(y1l), "=&v"(y1h)
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
-    a[0] = make_uint4(x0.x, x0.y, x0.z, x0.w);
-    a[1] = make_uint4(x1.x, x1.y, x1.z, x1.w);
-    b[0] = join(y0l, y0h);
-    b[1] = join(y1l, y1h);
-  } else {
-    static_assert(MN_A && MN_B, "layout combination not used");
-    u32x2_t x0l, x0h, x1l, x1h, y0l, y0h, y1l, y1h;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\tds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\tds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %6, %11\n\tds_read_b64_tr_b16 %7, %11 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(x0l), "=&v"(x0h), "=&v"(x1l), "=&v"(x1h), "=&v"(y0l), "=&v"(y0h), "=&v"(y1l), "=&v"(y1h)
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
-    a[0] = join(x0l, x0h);
-    a[1] = join(x1l, x1h);
-    b[0] = join(y0l, y0h);
-    b[1] = join(y1l, y1h);
+    MOE_PIPE_BODY(MOE_RD_K("x0", "pa0") MOE_RD_K("x1", "pa1") MOE_RD_MN("y0", "pb0") MOE_RD_MN("y1", "pb1"),
+                  MOE_PIPE_OUTS_KM, 6,
+                  n.a0 = x0; n.a1 = x1; n.b0 = join(y0l, y0h); n.b1 = join(y1l, y1h);)
   }
+};
+
+// both K-rows (dH = dO W2^T, dXs = dA W1^T)
+template <>
+struct Pipe<false, false> {
+  template <bool MMA, int WAIT>
+  __device__ __forceinline__ static void step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], uint32_t pa0,
+                                              uint32_t pa1, uint32_t pb0, uint32_t pb1) {
+    u32x4_t x0, x1, y0, y1;
+    MOE_PIPE_BODY(MOE_RD_K("x0", "pa0") MOE_RD_K("x1", "pa1") MOE_RD_K("y0", "pb0") MOE_RD_K("y1", "pb1"),
+                  MOE_PIPE_OUTS_KK, 4,
+                  n.a0 = x0; n.a1 = x1; n.b0 = y0; n.b1 = y1;)
+  }
+};
+
+// both MN-rows (weight gradients: k runs over the routed tokens)
+template <>
+struct Pipe<true, true> {
+  template <bool MMA, int WAIT>
+  __device__ __forceinline__ static void step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], uint32_t pa0,
+                                              uint32_t pa1, uint32_t pb0, uint32_t pb1) {
+    u32x2_t x0l, x0h, x1l, x1h, y0l, y0h, y1l, y1h;
+    MOE_PIPE_BODY(MOE_RD_MN("x0", "pa0") MOE_RD_MN("x1", "pa1") MOE_RD_MN("y0", "pb0") MOE_RD_MN("y1", "pb1"),
+                  MOE_PIPE_OUTS_MM, 8,
+                  n.a0 = join(x0l, x0h); n.a1 = join(x1l, x1h); n.b0 = join(y0l, y0h); n.b1 = join(y1l, y1h);)
+  }
+};
+
+// MFMAs of one chunk, no reads
+template <bool MN_A, bool MN_B>
+__device__ __forceinline__ void pipe_mma(const Frags& c, f32x16_t (&acc)[2][2]) {
+  asm volatile(MOE_MFMA4 : MOE_ACC_OUT : MOE_CUR_IN);
 }
 
-// bf16 tile through the DMA pipeline.  sink(kt, stageA) runs once per k-tile
+#undef MOE_RD_K
+#undef MOE_RD_MN
+#undef MOE_MFMA4
+#undef MOE_ACC_OUT
+#undef MOE_CUR_IN
+#undef MOE_ADDR_IN
+#undef MOE_PIPE_BODY
+#undef MOE_PIPE_OUTS_KM
+#undef MOE_PIPE_OUTS_KK
+#undef MOE_PIPE_OUTS_MM
+
+// bf16 tile through the DMA pipeline.  sink(kt, stage) runs once per k-tile
 // after its data landed (all waves), before any wave reads it for the MFMAs.
-template <bool MN_A, bool MN_B, class Epi, class Sink>
+//
+// Schedule of k-tile kt (stage slot kt % 4; the fragments of chunks 0 and 1
+// are already read, F[c] holds chunk c):
+//   MFMAs of chunk 0 | reads of chunk 2 -> F2 | wait for F1
+//   MFMAs of chunk 1 | reads of chunk 3 -> F3 | wait for all: stage kt is in registers
+//   wait for the loads of stage kt+1, barrier, sink, issue the loads of stage
+//   kt+4 into slot kt % 4 (every wave is past its reads of it)
+//   MFMAs of chunk 2 | reads of chunk 0 of stage kt+1 -> F0
+//   MFMAs of chunk 3 | reads of chunk 1 of stage kt+1 -> F1 | wait for F0
+// so three k-tiles of loads are in flight while one is computed, and each LDS
+// read has at least one block of matrix work to hide behind.
+template <bool MN_A, bool MN_B, class Epi, class Sink, class Pre>
 __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
-                                         Epi&& epi, Sink&& sink) {
+                                         Epi&& epi, Sink&& sink, Pre&& pre) {
+  using P = Pipe<MN_A, MN_B>;
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -489,35 +593,62 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
     da.issue(A, j, st, zero);
     db.issue(B, j, st + DMA_OP, zero);
   }
-  const int w = threadIdx.x >> 6;
-  const int wm = w & 1, wn = w >> 1;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vm(min(DMA_STAGES - 2, nk - 1 - kt));
+  if (nk > 0) {
+    const int w = threadIdx.x >> 6;
+    const int wm = w & 1, wn = w >> 1;
+    // this lane's fragment addresses in slot 0, per chunk
+    uint32_t fa0[4], fa1[4], fb0[4], fb1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      fa0[c] = dma_frag_addr<MN_A>(lds, wm * 64, c);
+      fa1[c] = dma_frag_addr<MN_A>(lds, wm * 64 + 32, c);
+      fb0[c] = dma_frag_addr<MN_B>(lds + DMA_OP, wn * 64, c);
+      fb1[c] = dma_frag_addr<MN_B>(lds + DMA_OP, wn * 64 + 32, c);
+    }
+    wait_vm(min(DMA_STAGES - 2, nk - 1));
     lds_barrier();
-    const char* st = lds + (kt % DMA_STAGES) * DMA_STAGE;
-    sink(kt, st);
-    if (kt + DMA_STAGES - 1 < nk) {
-      char* nx = lds + ((kt + DMA_STAGES - 1) % DMA_STAGES) * DMA_STAGE;
-      da.issue(A, kt + DMA_STAGES - 1, nx, zero);
-      db.issue(B, kt + DMA_STAGES - 1, nx + DMA_OP, zero);
+    sink(0, lds);
+    if (DMA_STAGES - 1 < nk) {
+      char* nx = lds + (DMA_STAGES - 1) * DMA_STAGE;
+      da.issue(A, DMA_STAGES - 1, nx, zero);
+      db.issue(B, DMA_STAGES - 1, nx + DMA_OP, zero);
     }
-#pragma unroll
-    for (int chunk = 0; chunk < 4; ++chunk) {
-      uint4 a[2], b[2];
-      dma_frags<MN_A, MN_B>(dma_frag_addr<MN_A>(st, wm * 64, chunk), dma_frag_addr<MN_A>(st, wm * 64 + 32, chunk),
-                            dma_frag_addr<MN_B>(st + DMA_OP, wn * 64, chunk),
-                            dma_frag_addr<MN_B>(st + DMA_OP, wn * 64 + 32, chunk), a, b);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
-                                                             __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0, 0);
+    Frags F0, F1, F2, F3;
+    P::template step<false, -1>(F0, F0, acc, fa0[0], fa1[0], fb0[0], fb1[0]);
+    P::template step<false, 0>(F1, F1, acc, fa0[1], fa1[1], fb0[1], fb1[1]);
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      const uint32_t so = (uint32_t)(kt % DMA_STAGES) * DMA_STAGE;
+      const uint32_t sn = (uint32_t)((kt + 1) % DMA_STAGES) * DMA_STAGE;
+      P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
+      P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
+      // every stage up to min(kt + 3, nk - 1) has all its loads issued
+      wait_vm(min(DMA_STAGES - 2, nk - 2 - kt));
+      lds_barrier();
+      sink(kt + 1, lds + sn);
+      if (kt + DMA_STAGES < nk) {
+        char* nx = lds + so;
+        da.issue(A, kt + DMA_STAGES, nx, zero);
+        db.issue(B, kt + DMA_STAGES, nx + DMA_OP, zero);
+      }
+      P::template step<true, -1>(F0, F2, acc, fa0[0] + sn, fa1[0] + sn, fb0[0] + sn, fb1[0] + sn);
+      P::template step<true, 1>(F1, F3, acc, fa0[1] + sn, fa1[1] + sn, fb0[1] + sn, fb1[1] + sn);
     }
+    {
+      // last k-tile: its chunks 0 and 1 are in flight or landed
+      const uint32_t so = (uint32_t)((nk - 1) % DMA_STAGES) * DMA_STAGE;
+      P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
+      P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
+      pipe_mma<MN_A, MN_B>(F2, acc);
+      pipe_mma<MN_A, MN_B>(F3, acc);
+    }
+    // the MFMA results are read by ordinary code below: cover the
+    // write-to-read distance the hardware requires after the last MFMA
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]));
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();  // every wave is done with the stages
-  epilogue(lds, acc, epi);
+  epilogue(lds, acc, epi, pre);
 }
 
 struct NoSink {
@@ -525,11 +656,11 @@ struct NoSink {
 };
 
 // One tile: bf16 through the DMA pipeline, fp32 through register staging.
-template <typename T, bool MN_A, bool MN_B, class Epi, class Sink = NoSink>
+template <typename T, bool MN_A, bool MN_B, class Epi, class Sink = NoSink, class Pre = NoPre>
 __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
-                                     Epi&& epi, Sink&& sink = Sink()) {
-  if constexpr (sizeof(T) == 2) tile_dma<MN_A, MN_B>(lds, A, B, K, zero, epi, sink);
-  else tile_reg<T, MN_A, MN_B>(lds, A, B, K, epi);
+                                     Epi&& epi, Sink&& sink = Sink(), Pre&& pre = Pre()) {
+  if constexpr (sizeof(T) == 2) tile_dma<MN_A, MN_B>(lds, A, B, K, zero, epi, sink, pre);
+  else tile_reg<T, MN_A, MN_B>(lds, A, B, K, epi, pre);
 }
 
 }  // namespace gemm
