@@ -498,59 +498,97 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
 // ===========================================================================
 // P4: combine, loss, dL/dO, dL/dgate -> dL/dlogit (one wave per token)
 // ===========================================================================
-template <typename T>
-__device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One token per half-wave: lane h of the half owns columns 8h.. of every
+// 256-column chunk.  CP chunks of the token are loaded at once (CP * k <= 8
+// row pieces of `out`), and the gates and slots of the half-wave's next token
+// are loaded one token ahead, so every lane keeps several loads in flight.
+template <typename T, int CP>
+__device__ __forceinline__ float combine_tokens(const KParams& p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, hl = lane & 31;
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, k = p.k;
   const T* tg = reinterpret_cast<const T*>(p.t);
   T* dout = reinterpret_cast<T*>(p.dout);
+  const int stride = G * kWaves * 2;
   float lsum = 0.f;
-  for (int tok = lwg * kWaves + wave; tok < p.T; tok += G * kWaves) {
-    float g[kMaxTopK], dg[kMaxTopK];
-    int pos[kMaxTopK];
+  float g[kMaxTopK], gn[kMaxTopK];
+  int pos[kMaxTopK], pn[kMaxTopK];
+  auto load_idx = [&](int tok, float (&gg)[kMaxTopK], int (&pp)[kMaxTopK]) {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      g[j] = 0.f;
-      dg[j] = 0.f;
-      pos[j] = 0;
-      if (j < k) {
-        g[j] = p.gate[tok * k + j];
-        pos[j] = p.inv[tok * k + j];
+      gg[j] = 0.f;
+      pp[j] = 0;
+      if (j < k && tok < p.T) {
+        gg[j] = p.gate[tok * k + j];
+        pp[j] = p.inv[tok * k + j];
       }
     }
-    for (int c = lane * 8; c < d; c += 64 * 8) {
-      const F8 tv = ld8(tg + (long)tok * d + c);
-      F8 o[kMaxTopK];
-      F8 y;
+  };
+  int base = (lwg * kWaves + wave) * 2;
+  load_idx(base + half, g, pos);
+  // the loop bound is uniform over the wave (the half-wave sums need both halves)
+  for (; base < p.T; base += stride) {
+    const int tok = base + half;
+    const bool live = tok < p.T;
+    load_idx(tok + stride, gn, pn);
+    float dg[kMaxTopK];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) y.v[q] = 0.f;
+    for (int j = 0; j < kMaxTopK; ++j) dg[j] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += 256 * CP) {
+      Raw8<T> tr[CP];
+      Raw8<float> o[CP * kMaxTopK > 8 ? 8 : CP * kMaxTopK];
+      constexpr int NS = CP * kMaxTopK > 8 ? 8 : CP * kMaxTopK;
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-          o[j] = ld8(p.out + (long)pos[j] * d + c);
+      for (int ch = 0; ch < CP; ++ch) {
+        const int c = c0 + ch * 256 + hl * 8;
+        tr[ch] = Raw8<T>{};
+        if (live && c < d) tr[ch] = ldr8(tg + (long)tok * d + c);
+      }
 #pragma unroll
-          for (int q = 0; q < 8; ++q) y.v[q] += g[j] * o[j].v[q];
+      for (int s = 0; s < NS; ++s) {
+        const int j = s / CP, ch = s % CP;
+        const int c = c0 + ch * 256 + hl * 8;
+        o[s] = Raw8<float>{};
+        if (live && j < k && c < d) o[s] = ldr8(p.out + (long)pos[j] * d + c);
+      }
+      F8 y[CP];
+#pragma unroll
+      for (int ch = 0; ch < CP; ++ch)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[ch].v[q] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = s / CP, ch = s % CP;
+        const F8 ov = cvt8(o[s]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[ch].v[q] += g[j] * ov.v[q];
+      }
+#pragma unroll
+      for (int ch = 0; ch < CP; ++ch) {
+        const F8 tv = cvt8(tr[ch]);
+        const int c = c0 + ch * 256 + hl * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float r = y[ch].v[q] - tv.v[q];
+          if (live && c < d) lsum += r * r;
+          y[ch].v[q] = r * p.inv_tupd;   // now dL/dy
         }
       }
-      F8 dy;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float r = y.v[q] - tv.v[q];
-        lsum += r * r;
-        dy.v[q] = r * p.inv_tupd;
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
+      for (int s = 0; s < NS; ++s) {
+        const int j = s / CP, ch = s % CP;
+        const int c = c0 + ch * 256 + hl * 8;
+        if (live && j < k && c < d) {
+          const F8 ov = cvt8(o[s]);
           F8 w;
-          float s = 0.f;
+          float sdot = 0.f;
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            w.v[q] = g[j] * dy.v[q];
-            s += dy.v[q] * o[j].v[q];
+            w.v[q] = g[j] * y[ch].v[q];
+            sdot += y[ch].v[q] * ov.v[q];
           }
-          dg[j] += s;
+          dg[j] += sdot;
           st8(dout + (long)pos[j] * d + c, w);
         }
       }
@@ -559,16 +597,28 @@ __device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k) {
-        dg[j] = wave_sum(dg[j]);
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) dg[j] += __shfl_xor(dg[j], m, 64);
         sg += g[j] * dg[j];
       }
     }
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
-      if (j < k && lane == j) p.dzsel[tok * k + j] = g[j] * (dg[j] - sg);
+      if (live && j < k && hl == j) p.dzsel[tok * k + j] = g[j] * (dg[j] - sg);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      g[j] = gn[j];
+      pos[j] = pn[j];
+    }
   }
+  return lsum;
+}
+
+template <typename T>
+__device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
+  const float lsum = p.k <= 2 ? combine_tokens<T, 4>(p) : combine_tokens<T, 1>(p);
   const float s = block_sum(lsum, meta.red);
-  if (tid == 0) p.loss_part[lwg] = s;
+  if (threadIdx.x == 0) p.loss_part[logical_wg()] = s;
 }
 
 // ===========================================================================
