@@ -130,6 +130,80 @@ __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot
     p.trace[((size_t)blockIdx.x * kPhases + phase) * 3 + slot] = wall_clock64();
 }
 
+// Partial router logits of one token over one column segment (see the
+// router phase): acc[e] = sum over the segment's columns c of x[tok][c] W_r[c][e],
+// for EGT groups of 4 experts (E <= 4 EGT; padded experts read zero weights).
+// W_r goes through LDS chunk by chunk; the token's 8-column pieces are loaded
+// four at a time, one group ahead of the group being multiplied.
+template <typename T, int EGT>
+__device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x, float4* wl, float (&acc)[kMaxExperts],
+                                                    int tok, bool mine, int s_me, int S, int DC, int EG) {
+  const int tid = threadIdx.x, d = p.d, E = p.E;
+#pragma unroll
+  for (int e = 0; e < kMaxExperts; ++e) acc[e] = 0.f;
+  for (int c0 = 0; c0 < d; c0 += DC) {
+    const int dc = min(DC, ceil_div(d - c0, 8 * S) * (8 * S));
+    __syncthreads();
+    // all of a thread's loads are issued before its LDS stores (16 per batch)
+#pragma unroll 16
+    for (int q = tid; q < dc * EG; q += kThreads) {
+      const int cl = q / EG, eg = q % EG;
+      const int i = cl / (8 * S), rem = cl % (8 * S), s = rem >> 3, j = rem & 7;
+      const int c = c0 + cl;
+      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+      if ((E & 3) == 0) {
+        if (c < d) w = *reinterpret_cast<const float4*>(p.params + (long)c * E + eg * 4);
+      } else {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = eg * 4 + u;
+          v[u] = (c < d && e < E) ? p.params[(long)c * E + e] : 0.f;
+        }
+        w = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      wl[((i * 8 + j) * EG + eg) * S + s] = w;
+    }
+    __syncthreads();
+    const int ni = dc / (8 * S);
+    auto load_group = [&](int i0, Raw8<T> (&xr)[4]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + (i0 + u) * 8 * S + 8 * s_me;
+        xr[u] = Raw8<T>{};
+        if (mine && i0 + u < ni && c < d) xr[u] = ldr8(x + (long)tok * d + c);
+      }
+    };
+    Raw8<T> xa[4], xb[4];
+    load_group(0, xa);
+    for (int i0 = 0; i0 < ni; i0 += 4) {
+      load_group(i0 + 4, xb);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u < ni) {
+          const F8 xv = cvt8(xa[u]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float4* wr = wl + ((i0 + u) * 8 + j) * EG * S + s_me;
+            float4 w[EGT];
+#pragma unroll
+            for (int eg = 0; eg < EGT; ++eg) w[eg] = eg < EG ? wr[eg * S] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int eg = 0; eg < EGT; ++eg) {
+              acc[eg * 4 + 0] += xv.v[j] * w[eg].x;
+              acc[eg * 4 + 1] += xv.v[j] * w[eg].y;
+              acc[eg * 4 + 2] += xv.v[j] * w[eg].z;
+              acc[eg * 4 + 3] += xv.v[j] * w[eg].w;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xa[u] = xb[u];
+    }
+  }
+}
+
 // ===========================================================================
 // P0: weight-copy refresh, W_r^T, router logits + token_topk + gates + histogram
 // ===========================================================================
@@ -152,78 +226,54 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
     p.wrt[(long)e * d + c] = p.params[i];
   }
 
-  int* hist = reinterpret_cast<int*>(smem);                  // [E]
-  float* zacc = reinterpret_cast<float*>(smem + 256);        // [32][EP]
+  int* hist = reinterpret_cast<int*>(smem);                  // [64]
   int EP = 1;
   while (EP < E) EP <<= 1;
-  const int TPI = kThreads / EP;          // tokens per pass
-  // chunk of d so that the padded W_r^T and x chunks each fit in 32 KB
-  int DC = min(d, min(8192 / E - 4, 32 * EP - 4));
-  DC &= ~7;
-  const int LDW = DC + 4;
-  float* ws = reinterpret_cast<float*>(smem + 256 + kRouterBlockTokens * kMaxExperts * 4);  // [E][LDW]
-  float* xs = ws + E * LDW;                                                               // [TPI][LDW]
-
+  const int TPI = kThreads / EP;          // tokens per top-k pass
   const int per = ceil_div(p.T, G);
   const int t_lo = min(p.T, lwg * per), t_hi = min(p.T, t_lo + per);
   if (tid < kMaxExperts) hist[tid] = 0;
   const int e_me = tid % EP, slot = tid / EP;
   const T* x = reinterpret_cast<const T*>(p.x);
 
-  for (int b0 = t_lo; b0 < t_hi; b0 += kRouterBlockTokens) {
-    const int nb = min(kRouterBlockTokens, t_hi - b0);
+  // Router logits, TP tokens per pass, each split over S column segments
+  // (TP * S <= 256 threads, S a power of two <= 64 so a token's segments are
+  // adjacent lanes of one wave).  Segment s of a token owns the 8-column
+  // pieces 8s, 8s + 8S, 8s + 16S, ... and keeps all E partial sums in
+  // registers; W_r is staged in LDS in the order the segments read it (for
+  // each piece index i, row j of the piece and 4-expert group eg, the S
+  // segments' float4s side by side), so the reads of one wave are either
+  // distinct consecutive 16-byte words or broadcasts.
+  int TP = 1;
+  while (TP < min(t_hi - t_lo, kThreads)) TP <<= 1;
+  int S = min(64, kThreads / TP);
+  while (S > 1 && 8 * S > d) S >>= 1;
+  const int EG = (E + 3) / 4;
+  float* zacc = reinterpret_cast<float*>(smem + 256);                          // [TP][EP]
+  float4* wl = reinterpret_cast<float4*>(smem + 256 + TP * EP * 4);           // staged W_r chunk
+  // (the reads of padded expert groups may run up to 16 * S float4 past the chunk)
+  const int wbudget = kScratchBytes - 256 - TP * EP * 4 - 16 * 64 * 16;
+  int DC = (wbudget / (EG * 16)) / (8 * S) * (8 * S);                           // columns per chunk
+  DC = min(DC, ceil_div(d, 8 * S) * (8 * S));
+  const int t_me = tid / S, s_me = tid % S;
+
+  for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
+    const int nb = min(TP, t_hi - b0);
+    float acc[kMaxExperts];
+    if (EG <= 4) router_segment_sums<T, 4>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+    else router_segment_sums<T, 16>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+    // sum the S segments of each token (adjacent lanes), fixed order
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+      if (e < E) {
+        for (int m = S >> 1; m >= 1; m >>= 1) acc[e] += __shfl_xor(acc[e], m, 64);
+      }
+    }
     __syncthreads();
-    for (int i = tid; i < kRouterBlockTokens * EP; i += kThreads) zacc[i] = 0.f;
-    for (int c0 = 0; c0 < d; c0 += DC) {
-      const int dc = min(DC, d - c0);
-      __syncthreads();
-      {
-        // rows c0..c0+dc of W_r are contiguous: float4 loads, all issued first
-        const float4* src = reinterpret_cast<const float4*>(p.params + (long)c0 * E);
-        const int n4 = E * dc / 4;
-        for (int i0 = tid; i0 < n4; i0 += kThreads * 8) {
-          float4 v[8];
+    if (t_me < nb && s_me == 0) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (i0 + u * kThreads < n4) v[u] = src[i0 + u * kThreads];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i4 = i0 + u * kThreads;
-            if (i4 < n4) {
-              const float* vv = &v[u].x;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int i = i4 * 4 + q;
-                ws[(i % E) * LDW + i / E] = vv[q];
-              }
-            }
-          }
-        }
-      }
-      for (int g0 = 0; g0 < nb; g0 += TPI) {
-        __syncthreads();
-        const int ng = min(TPI, nb - g0);
-        for (int i = tid * 8; i < ng * dc; i += kThreads * 8) {
-          const int tk = i / dc, c = i % dc;
-          F8 v = ld8(x + (long)(b0 + g0 + tk) * d + c0 + c);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) xs[tk * LDW + c + q] = v.v[q];
-        }
-        __syncthreads();
-        if (slot < ng && e_me < E) {
-          float s = 0.f;
-          const float4* wr = reinterpret_cast<const float4*>(ws + e_me * LDW);
-          const float4* xr = reinterpret_cast<const float4*>(xs + slot * LDW);
-          for (int c = 0; c < dc / 4; ++c) {
-            const float4 a = wr[c], b = xr[c];
-            s += a.x * b.x;
-            s += a.y * b.y;
-            s += a.z * b.z;
-            s += a.w * b.w;
-          }
-          zacc[(g0 + slot) * EP + e_me] += s;
-        }
-      }
+      for (int e = 0; e < kMaxExperts; ++e)
+        if (e < E) zacc[t_me * EP + e] = acc[e];
     }
     __syncthreads();
     // token_topk over each group of EP lanes (the group never crosses a wave)
