@@ -911,6 +911,89 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
 // ===========================================================================
 // P7: dx row sums; global norm; clip + AdamW (+ bf16 weight copy)
 // ===========================================================================
+// dx of each token = router part sum_j dz_j W_r[:, e_j] + the token's k slot
+// rows of dXs, summed in slot order.  One token per half-wave as in the
+// combine phase: lane h owns columns 8h.. of each 256-column chunk, CP chunks
+// are loaded at once, and the next token's dz / experts are loaded one token
+// ahead.
+template <typename T, int CP>
+__device__ __forceinline__ void dx_tokens(const KParams& p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, hl = lane & 31;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, k = p.k;
+  const T* dxs = reinterpret_cast<const T*>(p.dxs);
+  const int stride = G * kWaves * 2;
+  constexpr int NS = CP * kMaxTopK > 8 ? 8 : CP * kMaxTopK;
+  float dz[kMaxTopK], dzn[kMaxTopK];
+  int ev[kMaxTopK], evn[kMaxTopK];
+  auto load_idx = [&](int tok, float (&zz)[kMaxTopK], int (&ee)[kMaxTopK]) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      zz[j] = 0.f;
+      ee[j] = 0;
+      if (j < k && tok < p.T) {
+        zz[j] = p.dzsel[tok * k + j];
+        ee[j] = p.idx[tok * k + j];
+      }
+    }
+  };
+  int base = (lwg * kWaves + wave) * 2;
+  load_idx(base + half, dz, ev);
+  for (; base < p.T; base += stride) {
+    const int tok = base + half;
+    const bool live = tok < p.T;
+    load_idx(tok + stride, dzn, evn);
+    for (int c0 = 0; c0 < d; c0 += 256 * CP) {
+      Raw8<float> w[NS];
+      Raw8<T> v[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = s / CP, ch = s % CP;
+        const int c = c0 + ch * 256 + hl * 8;
+        w[s] = Raw8<float>{};
+        v[s] = Raw8<T>{};
+        if (live && j < k && c < d) {
+          w[s] = ldr8(p.wrt + (long)ev[j] * d + c);
+          v[s] = ldr8(dxs + ((long)tok * k + j) * d + c);
+        }
+      }
+      F8 acc[CP];
+#pragma unroll
+      for (int ch = 0; ch < CP; ++ch)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[ch].v[q] = 0.f;
+      // router part first, then the slot rows, each in slot order
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = s / CP, ch = s % CP;
+        const F8 wf = cvt8(w[s]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[ch].v[q] += dz[j] * wf.v[q];
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = s / CP, ch = s % CP;
+        if (j < k) {
+          const F8 vf = cvt8(v[s]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[ch].v[q] += vf.v[q];
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < CP; ++ch) {
+        const int c = c0 + ch * 256 + hl * 8;
+        if (live && c < d) st8(p.dx + (long)tok * d + c, acc[ch]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      dz[j] = dzn[j];
+      ev[j] = evn[j];
+    }
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& meta, bool zero_grad, bool apply,
                             bool want_dx) {
@@ -918,44 +1001,7 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E, k = p.k;
 
-  if (want_dx) {
-    const T* dxs = reinterpret_cast<const T*>(p.dxs);
-    for (int tok = lwg * kWaves + wave; tok < p.T; tok += G * kWaves) {
-      float dzv[kMaxTopK];
-      int ev[kMaxTopK];
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        dzv[j] = 0.f;
-        ev[j] = 0;
-        if (j < k) {
-          dzv[j] = p.dzsel[tok * k + j];
-          ev[j] = p.idx[tok * k + j];
-        }
-      }
-      for (int c = lane * 8; c < d; c += 64 * 8) {
-        F8 s;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s.v[q] = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-          if (j < k) {
-            const F8 w = ld8(p.wrt + (long)ev[j] * d + c);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) s.v[q] += dzv[j] * w.v[q];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-          if (j < k) {
-            const F8 v = ld8(dxs + ((long)tok * k + j) * d + c);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) s.v[q] += v.v[q];
-          }
-        }
-        st8(p.dx + (long)tok * d + c, s);
-      }
-    }
-  }
+  if (want_dx) p.k <= 2 ? dx_tokens<T, 4>(p) : dx_tokens<T, 1>(p);
 
   // loss of this launch, summed over workgroups in index order
   if (lwg == 0 && p.stats) {
