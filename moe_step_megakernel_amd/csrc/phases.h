@@ -132,15 +132,16 @@ __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot
 
 // Partial router logits of one token over one column segment (see the
 // router phase): acc[e] = sum over the segment's columns c of x[tok][c] W_r[c][e],
-// for EGT groups of 4 experts (E <= 4 EGT; padded experts read zero weights).
+// for the EGT groups of 4 experts from group EG0 on (padded experts read zero
+// weights).
 // W_r goes through LDS chunk by chunk; the token's 8-column pieces are loaded
 // four at a time, one group ahead of the group being multiplied.
-template <typename T, int EGT>
+template <typename T, int EGT, int EG0>
 __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x, float4* wl, float (&acc)[kMaxExperts],
                                                     int tok, bool mine, int s_me, int S, int DC, int EG) {
   const int tid = threadIdx.x, d = p.d, E = p.E;
 #pragma unroll
-  for (int e = 0; e < kMaxExperts; ++e) acc[e] = 0.f;
+  for (int e = 4 * EG0; e < 4 * (EG0 + EGT); ++e) acc[e] = 0.f;
   for (int c0 = 0; c0 < d; c0 += DC) {
     const int dc = min(DC, ceil_div(d - c0, 8 * S) * (8 * S));
     __syncthreads();
@@ -187,13 +188,14 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
             const float4* wr = wl + ((i0 + u) * 8 + j) * EG * S + s_me;
             float4 w[EGT];
 #pragma unroll
-            for (int eg = 0; eg < EGT; ++eg) w[eg] = eg < EG ? wr[eg * S] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int eg = 0; eg < EGT; ++eg)
+              w[eg] = EG0 + eg < EG ? wr[(EG0 + eg) * S] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int eg = 0; eg < EGT; ++eg) {
-              acc[eg * 4 + 0] += xv.v[j] * w[eg].x;
-              acc[eg * 4 + 1] += xv.v[j] * w[eg].y;
-              acc[eg * 4 + 2] += xv.v[j] * w[eg].z;
-              acc[eg * 4 + 3] += xv.v[j] * w[eg].w;
+              acc[(EG0 + eg) * 4 + 0] += xv.v[j] * w[eg].x;
+              acc[(EG0 + eg) * 4 + 1] += xv.v[j] * w[eg].y;
+              acc[(EG0 + eg) * 4 + 2] += xv.v[j] * w[eg].z;
+              acc[(EG0 + eg) * 4 + 3] += xv.v[j] * w[eg].w;
             }
           }
         }
@@ -260,8 +262,14 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
     const int nb = min(TP, t_hi - b0);
     float acc[kMaxExperts];
-    if (EG <= 4) router_segment_sums<T, 4>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-    else router_segment_sums<T, 16>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+    // more than 16 experts: two passes over the columns, 8 expert groups each
+    // (one pass over all 64 would not fit the register file)
+    if (EG <= 4) {
+      router_segment_sums<T, 4, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+    } else {
+      router_segment_sums<T, 8, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+      router_segment_sums<T, 8, 8>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+    }
     // sum the S segments of each token (adjacent lanes), fixed order
 #pragma unroll
     for (int e = 0; e < kMaxExperts; ++e) {

@@ -337,7 +337,9 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
 //  * K-rows operand, LDS [128 rows][128 B]: logical k-unit u of row r sits in
 //    physical unit u ^ ((r >> 1) & 7);
 //  * MN-rows operand, LDS [64 k-rows][256 B]: logical 16-byte column slot s of
-//    k-row r sits in physical slot s ^ (2 * (r & 3)).
+//    k-row r sits in physical slot s ^ (4 * (r & 3)).  Half a transpose read
+//    (32 lanes) covers 4 k-rows x 64 bytes; the XOR puts the 4 rows' 64-byte
+//    pieces in the 4 distinct quarters of the 64 banks.
 // Lanes whose element is out of range load from a zero page instead.  The
 // loop waits on the vector-memory counter itself and synchronises with a bare
 // s_barrier, so the loads of later k-tiles stay in flight across it.
@@ -388,7 +390,7 @@ struct DmaOp {
         rowbase[i] = (row < o.nrows) ? map_row(o, o.p0 + row) * o.ld * 2 + unit[i] * 16 : -1;
       }
     } else {
-      const int slot = (lane & 15) ^ (2 * ((lane >> 4) & 3));
+      const int slot = (lane & 15) ^ (4 * ((lane >> 4) & 3));
       const int mn = o.mn0 + slot * 8;
       coloff = (mn < o.lim) ? (long)mn * 2 : -1;
       krow0 = 16 * w + (lane >> 4);   // + 4 i
@@ -444,7 +446,7 @@ __device__ __forceinline__ uint32_t dma_frag_addr(const char* st, int row0, int 
     const int g = lane >> 4, j = lane & 15;
     const int r = chunk * 16 + 8 * (g >> 1) + (j >> 2);
     const int c = row0 + 16 * (g & 1) + 4 * (j & 3);
-    return lds_addr(st + r * 256 + (((c >> 3) ^ (2 * (r & 3))) << 4) + (c & 7) * 2);
+    return lds_addr(st + r * 256 + (((c >> 3) ^ (4 * (r & 3))) << 4) + (c & 7) * 2);
   }
 }
 
