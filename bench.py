@@ -94,9 +94,10 @@ def gemm_flops(cfg) -> int:
     return 6 * 2 * cfg.tokens * cfg.top_k * cfg.d_model * cfg.d_ff * cfg.microbatches
 
 
-def cpu_baseline(cfg, inp, budget_s: float) -> dict:
+def cpu_baseline(cfg, inp, budget_s: float, one_thread: bool = True) -> dict:
     """The oracle as it stands, on this host's cores, repeated over the same batch
-    until about ``budget_s`` seconds of work (at least one update)."""
+    until about ``budget_s`` seconds of work (at least one update); then, for
+    scale, one more update on a single BLAS thread."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -119,15 +120,30 @@ def cpu_baseline(cfg, inp, budget_s: float) -> dict:
         if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
             break
     tok = cfg.tokens_in_update * reps
-    return {"value": tok / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} full FP64 update(s) of the {cfg.name} layer ({cfg.tokens_in_update} tokens each), "
-                      f"{el:.1f} s", "ms_per_update": 1e3 * el / reps}
+    res = {"value": tok / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{reps} full FP64 update(s) of the {cfg.name} layer ({cfg.tokens_in_update} tokens each), "
+                     f"{el:.1f} s", "ms_per_update": 1e3 * el / reps}
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        res["blas"] = ",".join(sorted({str(i.get("internal_api")) for i in threadpool_info()
+                                       if i.get("user_api") == "blas"})) or None
+        # one update on a single BLAS thread, for scale
+        if one_thread:
+            with threadpool_limits(limits=1, user_api="blas"):
+                t1 = time.perf_counter()
+                oracle.step(xs, ts, params, m, v, reps + 1, d=cfg.d_model, f=cfg.d_ff, E=cfg.n_experts,
+                            top_k=cfg.top_k, lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
+                            weight_decay=cfg.weight_decay, clip_norm=cfg.clip_norm, bias=inp.router_bias)
+                res["ms_per_update_1_thread"] = 1e3 * (time.perf_counter() - t1)
+    except Exception:  # pragma: no cover - threadpoolctl missing or refusing
+        pass
+    return res
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="bf16_2x1024")
     ap.add_argument("--wg-per-cu", type=int, default=0)
@@ -207,15 +223,21 @@ def main(argv=None):
     if not args.no_trace:
         words = layer.trace_words()
         tr = torch.zeros(words, dtype=torch.int64, device=dev)
-        ev_tr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(M)]
-        one_update(ev_tr, trace=tr)
-        torch.cuda.synchronize()
+        # a few traced updates: the overhead figure is their median launch time
+        # against the untraced median; the clocks decoded are the last one's
+        traced_ms = []
+        for _ in range(5):
+            ev_tr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(M)]
+            one_update(ev_tr, trace=tr)
+            torch.cuda.synchronize()
+            traced_ms.append(float(ev_tr[-1][0].elapsed_time(ev_tr[-1][1])))
         layer.status()
         raw = tr.cpu().numpy()
         if args.dump_trace:
             np.save(args.dump_trace, raw.reshape(layer.grid, -1, 3))
         phases = trace_mod.decode(raw, layer.grid)
-        phases["traced_launch_ms"] = float(ev_tr[-1][0].elapsed_time(ev_tr[-1][1]))
+        phases["traced_launch_ms"] = float(np.median(traced_ms))
+        phases["trace_overhead_frac"] = phases["traced_launch_ms"] / float(np.median(launch_ms[:, -1])) - 1.0
         print("# phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in phases["phase_us"].items())
               + f"  barrier idle mean {phases['barrier_idle_frac_mean']:.3f}", file=sys.stderr, flush=True)
 

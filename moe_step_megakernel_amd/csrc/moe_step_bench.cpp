@@ -6,10 +6,11 @@
 // transform (a different stream from the Python generator; timings do not
 // depend on the exact values).  Prints one line per run with ms/update.
 //
-//   moe_step_bench [--config NAME] [--steps K] [--warmup W] [--skip MASK] [--wg-per-cu N] [--copy-mib N]
+//   moe_step_bench [--config NAME] [--steps K] [--warmup W] [--skip MASK[,MASK...]] [--wg-per-cu N] [--copy-mib N]
 //     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024
-//     --skip MASK: after the warm-up, time launches that skip the phases in MASK
-//                  (bit i = phase i), for per-phase counter collection
+//     --skip MASK: after the warm-up, time K launches that skip the phases in MASK
+//                  (bit i = phase i), for per-phase timing and counter collection;
+//                  a comma-separated list times K launches per mask, in order
 //     --copy-mib N: instead, time a plain device copy of N MiB (read N, write N),
 //                  the reference for scaling memory counters
 #include <hip/hip_runtime.h>
@@ -103,7 +104,7 @@ int run_copy(int mib, int steps) {
 int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024";
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
-  unsigned skip = 0;
+  std::vector<unsigned> skips{0u};
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
     auto next = [&]() -> const char* {
@@ -116,7 +117,17 @@ int main(int argc, char** argv) {
     if (a == "--config") cfg_name = next();
     else if (a == "--steps") steps = std::atoi(next());
     else if (a == "--warmup") warmup = std::atoi(next());
-    else if (a == "--skip") skip = (unsigned)std::strtoul(next(), nullptr, 0);
+    else if (a == "--skip") {
+      skips.clear();
+      std::string s = next();
+      size_t pos = 0;
+      while (pos <= s.size()) {
+        const size_t q = s.find(',', pos);
+        skips.push_back((unsigned)std::strtoul(s.substr(pos, q == std::string::npos ? std::string::npos : q - pos).c_str(), nullptr, 0));
+        if (q == std::string::npos) break;
+        pos = q + 1;
+      }
+    }
     else if (a == "--copy-mib") copy_mib = std::atoi(next());
     else if (a == "--wg-per-cu") wg_per_cu = std::atoi(next());
     else {
@@ -223,23 +234,26 @@ int main(int argc, char** argv) {
   hipEvent_t e0, e1;
   CHECK_HIP(hipEventCreate(&e0));
   CHECK_HIP(hipEventCreate(&e1));
-  CHECK_HIP(hipEventRecord(e0, stream));
-  for (int i = 0; i < steps; ++i, ++step) {
-    if (moe_step_run(h, &io, sh->T, sh->T, step, base | (skip << 8), stream) != MOE_OK) {
-      std::fprintf(stderr, "moe_step_run: %s\n", moe_step_last_error(h));
+  for (const unsigned skip : skips) {
+    CHECK_HIP(hipEventRecord(e0, stream));
+    for (int i = 0; i < steps; ++i, ++step) {
+      if (moe_step_run(h, &io, sh->T, sh->T, step, base | (skip << 8), stream) != MOE_OK) {
+        std::fprintf(stderr, "moe_step_run: %s\n", moe_step_last_error(h));
+        return 2;
+      }
+    }
+    CHECK_HIP(hipEventRecord(e1, stream));
+    CHECK_HIP(hipEventSynchronize(e1));
+    if (moe_step_status(h) != MOE_OK) {
+      std::fprintf(stderr, "moe_step_status: %s\n", moe_step_last_error(h));
       return 2;
     }
+    float ms = 0.f;
+    CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+    std::printf("%s skip=0x%02x grid=%d: %d updates, %.4f ms/update, %.0f tokens/s\n", sh->name, skip,
+                moe_step_grid_size(h), steps, ms / steps, sh->T * steps / (ms * 1e-3));
+    std::fflush(stdout);
   }
-  CHECK_HIP(hipEventRecord(e1, stream));
-  CHECK_HIP(hipEventSynchronize(e1));
-  if (moe_step_status(h) != MOE_OK) {
-    std::fprintf(stderr, "moe_step_status: %s\n", moe_step_last_error(h));
-    return 2;
-  }
-  float ms = 0.f;
-  CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
-  std::printf("%s skip=0x%02x grid=%d: %d updates, %.4f ms/update, %.0f tokens/s\n", sh->name, skip,
-              moe_step_grid_size(h), steps, ms / steps, sh->T * steps / (ms * 1e-3));
   moe_step_destroy(h);
   for (void* p : {dx_in, dt, (void*)params, (void*)grads, (void*)m, (void*)v, (void*)dxg, (void*)stats})
     CHECK_HIP(hipFree(p));
