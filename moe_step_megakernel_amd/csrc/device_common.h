@@ -120,18 +120,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS traffic only: each wave waits for its own LDS
+// accesses, not for its global stores (which __syncthreads would drain), so
+// stores issued before it stay in flight.  Not for global data exchanged
+// between the waves of a workgroup.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left alone
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
 // Sum over the workgroup in a fixed order; result valid in every thread.
-// `red` is kWaves floats of LDS.  Contains __syncthreads().
+// `red` is kWaves floats of LDS.  Synchronises the workgroup (LDS only).
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
+  lds_sync();
   if (lane == 0) red[wave] = v;
-  __syncthreads();
+  lds_sync();
   float s = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) s += red[w];
-  __syncthreads();
+  lds_sync();
   return s;
 }
 

@@ -260,7 +260,7 @@ __device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2],
           cs[row * CROW + col] = acc[i][j][r];
         }
   }
-  __syncthreads();
+  lds_sync();
   if constexpr (kPre) {
 #pragma unroll
     for (int j = 0; j < kIt; ++j) {
@@ -589,7 +589,7 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
   da.init(A);
   db.init(B);
   const int nk = (K + 63) / 64;
-  __syncthreads();  // the previous user of this LDS is done
+  lds_sync();  // the previous user of this LDS is done (its global stores may still be in flight)
   for (int j = 0; j < DMA_STAGES - 1 && j < nk; ++j) {
     char* st = lds + j * DMA_STAGE;
     da.issue(A, j, st, zero);
@@ -648,8 +648,9 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]));
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();  // every wave is done with the stages
+  // every wave is done with the stages (all direct-to-LDS loads completed at
+  // the last vmcnt wait, none was issued after it)
+  lds_sync();
   epilogue(lds, acc, epi, pre);
 }
 
