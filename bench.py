@@ -140,6 +140,63 @@ def cpu_baseline(cfg, inp, budget_s: float, one_thread: bool = True) -> dict:
     return res
 
 
+def bench_selective(args, cfg, layer, X, Tg, bias, dx, stream):
+    """Selective updates (the pages' "Other measured compiler work" table: shared
+    weights every microbatch, experts every 16): one launch per microbatch of
+    cfg.tokens tokens, router clip+AdamW in every launch, expert gradients
+    accumulated over W launches and applied in the last."""
+    import torch
+
+    W = args.selective
+    T = cfg.tokens
+    n = [0]
+
+    def one_microbatch(ev=None):
+        i = n[0]
+        n[0] += 1
+        groups = dict(zero_router=True, apply_router=True, step_router=i + 1, zero_experts=(i % W == 0),
+                      apply_experts=(i % W == W - 1), step_experts=i // W + 1)
+        if ev is not None:
+            ev[0].record(stream)
+        layer.run(X[:T], Tg[:T], tokens_in_update=T, dx=dx, router_bias=bias, groups=groups)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(W * max(1, -(-args.warmup // W))):
+        one_microbatch()
+    torch.cuda.synchronize()
+    layer.status()
+    steps = W * max(1, -(-args.steps // W))   # whole windows
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        one_microbatch(ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    layer.status()
+    total_ms = t0.elapsed_time(t1)
+    ms = np.array([s.elapsed_time(e) for s, e in ev])
+    per_pos = [float(np.median(ms[j::W])) for j in range(W)]
+    layer.close()
+    line = {
+        "metric": f"ms per microbatch, selective updates (router every microbatch, experts every {W})",
+        "value": T * steps / (total_ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": W * max(1, -(-args.warmup // W)), "ms_per_step": total_ms / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"MoE-FFN layer {cfg.name}, {T}-token microbatches, d_model={cfg.d_model}, "
+                               f"d_ff={cfg.d_ff}, E={cfg.n_experts}, top-{cfg.top_k}, expert window {W}",
+                   "tokens_per_microbatch": T, "parallelism": "single-gpu"},
+        "ms_per_microbatch_median": float(np.median(ms)),
+        "ms_router_only_microbatch_median": float(np.median(np.concatenate([ms[j::W] for j in range(W - 1)])))
+        if W > 1 else None,
+        "ms_expert_update_microbatch_median": per_pos[-1],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +208,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--dump-trace", default=None, help="write the raw phase clocks (.npy) here")
+    ap.add_argument("--selective", type=int, default=0, metavar="W",
+                    help="time selective updates instead: the router is updated after every microbatch, the "
+                         "experts after every W (one timed step = one microbatch)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -195,6 +255,9 @@ def main(argv=None):
                       trace=trace)
             if events is not None:
                 events[mb][1].record(stream)
+
+    if args.selective > 0:
+        return bench_selective(args, cfg, layer, X, Tg, bias, dx, stream)
 
     for _ in range(args.warmup):
         one_update()

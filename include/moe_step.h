@@ -113,6 +113,15 @@ typedef struct {
                                        first (needed after create and whenever the
                                        caller changed params itself) */
 #define MOE_RUN_TRACE 0x8u          /* record per-phase clocks into io.trace */
+/* Per-group variants (selective updates: the shared router W_r and the experts
+ * W1 | W2 keep separate accumulation windows and optimizer steps, the pages'
+ * "Other measured compiler work" table: shared weights every microbatch,
+ * experts every 16).  MOE_RUN_ZERO_GRAD = both ZERO bits, MOE_RUN_APPLY = both
+ * APPLY bits.  The clip norm is taken over the groups applied in the launch. */
+#define MOE_RUN_ZERO_GRAD_ROUTER 0x10u   /* router grads := this launch's (else +=)  */
+#define MOE_RUN_ZERO_GRAD_EXPERTS 0x20u  /* expert grads := this launch's (else +=)  */
+#define MOE_RUN_APPLY_ROUTER 0x40u       /* clip + AdamW on W_r                      */
+#define MOE_RUN_APPLY_EXPERTS 0x80u      /* clip + AdamW on W1 | W2                  */
 /* Profiling aid: skip phase i (0..7) of the persistent kernel and reuse what the
  * previous launch on this handle left in the arena.  Accepted only when the
  * previous launch ran every phase with the same n_tokens (else MOE_ERR_STATE);
@@ -151,6 +160,16 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out);
  * on the middle ones, APPLY on the last. */
 int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
                  int64_t step, uint32_t run_flags, void* hip_stream);
+
+/* moe_step_run with a separate 1-based AdamW step per parameter group, for
+ * selective updates: step_router is used when W_r is applied, step_experts
+ * when W1 | W2 are (each >= 1 when its group is applied).  With both groups
+ * applied, the global-norm clip covers all parameters as in moe_step_run;
+ * with one, only that group's gradients enter the norm.  The loss in
+ * io.stats restarts whenever a ZERO bit is set.  moe_step_run(.., step, ..) is
+ * moe_step_run_groups(.., step, step, ..).  Same errors as moe_step_run. */
+int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
+                        int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream);
 
 /* Waits for the handle's last stream and reads the device status word.
  * Returns MOE_ERR_DEVICE (with the bits in last_error) if a kernel reported an

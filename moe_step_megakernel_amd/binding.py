@@ -17,6 +17,8 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_SHAPE, MOE_ERR_HIP, MOE_ERR_NOMEM, MOE_ERR_DEVICE, 
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_RUN_ZERO_GRAD, MOE_RUN_APPLY, MOE_RUN_REFRESH_SHADOW, MOE_RUN_TRACE = 0x1, 0x2, 0x4, 0x8
 MOE_RUN_SKIP_MASK = 0xFF00
+MOE_RUN_ZERO_GRAD_ROUTER, MOE_RUN_ZERO_GRAD_EXPERTS = 0x10, 0x20
+MOE_RUN_APPLY_ROUTER, MOE_RUN_APPLY_EXPERTS = 0x40, 0x80
 
 
 def MOE_RUN_SKIP_PHASE(i: int) -> int:
@@ -72,6 +74,9 @@ def load_library():
     lib.moe_step_run.argtypes = [ctypes.c_void_p, P(moe_step_io), ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_uint32, ctypes.c_void_p]
     lib.moe_step_run.restype = ctypes.c_int
+    lib.moe_step_run_groups.argtypes = [ctypes.c_void_p, P(moe_step_io), ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    lib.moe_step_run_groups.restype = ctypes.c_int
     lib.moe_step_status.argtypes = [ctypes.c_void_p]
     lib.moe_step_status.restype = ctypes.c_int
     lib.moe_step_trace_words.argtypes = [ctypes.c_void_p]
@@ -122,6 +127,14 @@ def moe_step_run(handle, io: moe_step_io, n_tokens: int, tokens_in_update: int, 
                                      stream)
     if rc != MOE_OK:
         raise MoeStepError("moe_step_run", rc, moe_step_last_error(handle))
+
+
+def moe_step_run_groups(handle, io: moe_step_io, n_tokens: int, tokens_in_update: int, step_router: int,
+                        step_experts: int, run_flags: int, stream=None) -> None:
+    rc = load_library().moe_step_run_groups(handle, ctypes.byref(io), n_tokens, tokens_in_update, step_router,
+                                            step_experts, run_flags, stream)
+    if rc != MOE_OK:
+        raise MoeStepError("moe_step_run_groups", rc, moe_step_last_error(handle))
 
 
 def moe_step_status(handle) -> None:

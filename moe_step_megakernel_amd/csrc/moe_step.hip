@@ -279,6 +279,11 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
 
 int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update, int64_t step,
                  uint32_t run_flags, void* hip_stream) {
+  return moe_step_run_groups(h, io, n_tokens, tokens_in_update, step, step, run_flags, hip_stream);
+}
+
+int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
+                        int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream) {
   if (!h) return MOE_ERR_ARG;
   if (!io) {
     set_err(h->err, "io is NULL");
@@ -293,17 +298,25 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
     set_err(h->err, "tokens_in_update %lld must be >= max(1, n_tokens)", (long long)tokens_in_update);
     return MOE_ERR_ARG;
   }
-  if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK)) {
+  if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK |
+                    MOE_RUN_ZERO_GRAD_ROUTER | MOE_RUN_ZERO_GRAD_EXPERTS | MOE_RUN_APPLY_ROUTER |
+                    MOE_RUN_APPLY_EXPERTS)) {
     set_err(h->err, "unknown run flags 0x%x", run_flags);
     return MOE_ERR_ARG;
   }
+  // the whole-update bits stand for both groups
+  if (run_flags & MOE_RUN_ZERO_GRAD) run_flags |= MOE_RUN_ZERO_GRAD_ROUTER | MOE_RUN_ZERO_GRAD_EXPERTS;
+  if (run_flags & MOE_RUN_APPLY) run_flags |= MOE_RUN_APPLY_ROUTER | MOE_RUN_APPLY_EXPERTS;
+  run_flags &= ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY);
+  const bool apply_r = (run_flags & MOE_RUN_APPLY_ROUTER) != 0u, apply_e = (run_flags & MOE_RUN_APPLY_EXPERTS) != 0u;
   if ((run_flags & MOE_RUN_SKIP_MASK) && h->last_full_tokens != n_tokens) {
     set_err(h->err, "skipping phases needs a previous full launch with the same n_tokens (%d, last %d)", n_tokens,
             h->last_full_tokens);
     return MOE_ERR_STATE;
   }
-  if ((run_flags & MOE_RUN_APPLY) && step < 1) {
-    set_err(h->err, "step must be >= 1 with MOE_RUN_APPLY (got %lld)", (long long)step);
+  if ((apply_r && step_router < 1) || (apply_e && step_experts < 1)) {
+    set_err(h->err, "the AdamW step of an applied group must be >= 1 (router %lld, experts %lld)",
+            (long long)step_router, (long long)step_experts);
     return MOE_ERR_ARG;
   }
   if (n_tokens > 0 && (!io->x || !io->target)) {
@@ -314,7 +327,7 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
     set_err(h->err, "params and grads are required");
     return MOE_ERR_ARG;
   }
-  if ((run_flags & MOE_RUN_APPLY) && (!io->exp_avg || !io->exp_avg_sq)) {
+  if ((apply_r || apply_e) && (!io->exp_avg || !io->exp_avg_sq)) {
     set_err(h->err, "exp_avg and exp_avg_sq are required with MOE_RUN_APPLY");
     return MOE_ERR_ARG;
   }
@@ -349,10 +362,14 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
   p.eps = (float)c.adam_eps;
   p.wd = (float)c.weight_decay;
   p.clip = (float)c.clip_norm;
-  const double s = step >= 1 ? (double)step : 1.0;
-  const double bc1 = 1.0 - std::pow(c.beta1, s), bc2 = 1.0 - std::pow(c.beta2, s);
-  p.inv_bc1 = bc1 > 0.0 ? (float)(1.0 / bc1) : 1.f;
-  p.inv_sqrt_bc2 = bc2 > 0.0 ? (float)(1.0 / std::sqrt(bc2)) : 1.f;
+  // bias corrections per group: [0] router, [1] experts
+  const int64_t steps[2] = {step_router, step_experts};
+  for (int q = 0; q < 2; ++q) {
+    const double s = steps[q] >= 1 ? (double)steps[q] : 1.0;
+    const double bc1 = 1.0 - std::pow(c.beta1, s), bc2 = 1.0 - std::pow(c.beta2, s);
+    p.inv_bc1[q] = bc1 > 0.0 ? (float)(1.0 / bc1) : 1.f;
+    p.inv_sqrt_bc2[q] = bc2 > 0.0 ? (float)(1.0 / std::sqrt(bc2)) : 1.f;
+  }
   p.x = io->x;
   p.t = io->target;
   p.bias = io->router_bias;

@@ -45,7 +45,8 @@ struct KParams {
   float inv_tupd;     // 1 / tokens_in_update
   unsigned flags;
   // optimizer
-  float lr, beta1, beta2, omb1, omb2, eps, wd, clip, inv_bc1, inv_sqrt_bc2;
+  float lr, beta1, beta2, omb1, omb2, eps, wd, clip;
+  float inv_bc1[2], inv_sqrt_bc2[2];   // AdamW bias corrections: [0] router, [1] experts
   unsigned epoch;     // launch number on this handle (barrier targets)
   // caller buffers
   const void* x;
@@ -683,7 +684,7 @@ __device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
 // P5: dH = (dO W2[e]^T) * G' ; dW2[e] = A_e^T dO ; router-gradient partials
 // ===========================================================================
 template <typename T>
-__device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_grad) {
+__device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_experts) {
   const int tid = threadIdx.x;
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E, k = p.k;
@@ -724,7 +725,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
             if (m0 + r < f && n0 + c < d) {
               F8 nv = cvt8(old);
 #pragma unroll
-              for (int u = 0; u < 8; ++u) nv.v[u] = zero_grad ? v[u] : nv.v[u] + v[u];
+              for (int u = 0; u < 8; ++u) nv.v[u] = zero_experts ? v[u] : nv.v[u] + v[u];
               st8(g + (long)(m0 + r) * d + n0 + c, nv);
 #pragma unroll
               for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
@@ -733,7 +734,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
           gemm::NoSink(),
           [&](int r, int c) {
             Raw8<float> old{};
-            if (!zero_grad && m0 + r < f && n0 + c < d) old = ldr8(g + (long)(m0 + r) * d + n0 + c);
+            if (!zero_experts && m0 + r < f && n0 + c < d) old = ldr8(g + (long)(m0 + r) * d + n0 + c);
             return old;
           });
       const float s = block_sum(sq, meta.red);
@@ -819,7 +820,8 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 // P6: dW1[e] = X_e^T dH ; dXs = dH W1[e]^T ; router gradient reduction
 // ===========================================================================
 template <typename T>
-__device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& meta, bool zero_grad, bool want_dx) {
+__device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& meta, bool zero_router, bool zero_experts,
+                                           bool want_dx) {
   const int tid = threadIdx.x;
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E;
@@ -860,7 +862,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
             if (m0 + r < d && n0 + c < f) {
               F8 nv = cvt8(old);
 #pragma unroll
-              for (int u = 0; u < 8; ++u) nv.v[u] = zero_grad ? v[u] : nv.v[u] + v[u];
+              for (int u = 0; u < 8; ++u) nv.v[u] = zero_experts ? v[u] : nv.v[u] + v[u];
               st8(g + (long)(m0 + r) * f + n0 + c, nv);
 #pragma unroll
               for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
@@ -869,7 +871,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
           gemm::NoSink(),
           [&](int r, int c) {
             Raw8<float> old{};
-            if (!zero_grad && m0 + r < d && n0 + c < f) old = ldr8(g + (long)(m0 + r) * f + n0 + c);
+            if (!zero_experts && m0 + r < d && n0 + c < f) old = ldr8(g + (long)(m0 + r) * f + n0 + c);
             return old;
           });
       const float s = block_sum(sq, meta.red);
@@ -906,7 +908,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
         const int c = o / E, e = o % E;
         float s = 0.f;
         for (int r = 0; r < RCH; ++r) s += p.rpart[((long)r * E + e) * d + c];
-        const float nv = zero_grad ? s : p.grads[o] + s;
+        const float nv = zero_router ? s : p.grads[o] + s;
         p.grads[o] = nv;
         sq = nv * nv;
       }
@@ -1003,8 +1005,8 @@ __device__ __forceinline__ void dx_tokens(const KParams& p) {
 }
 
 template <typename T>
-__device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& meta, bool zero_grad, bool apply,
-                            bool want_dx) {
+__device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& meta, bool restart_loss, bool apply_r,
+                                            bool apply_e, bool want_dx) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E, k = p.k;
@@ -1022,21 +1024,22 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
       float tot = 0.f;
       for (int i = 0; i < kThreads; ++i) tot += red[i];
       tot *= 0.5f * p.inv_tupd;
-      p.stats[0] = zero_grad ? tot : p.stats[0] + tot;
+      p.stats[0] = restart_loss ? tot : p.stats[0] + tot;
     }
     __syncthreads();
   }
-  if (!apply) return;
+  if (!apply_r && !apply_e) return;
 
-  // global norm from the per-tile partials, fixed order (same in every workgroup)
+  // global norm from the per-tile partials of the applied groups (the expert
+  // tiles first, then the router items), fixed order (same in every workgroup)
   const int n10 = E * ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
   const int n11 = E * ceil_div(d, gemm::BM) * ceil_div(f, gemm::BN);
   const int nrr = ceil_div(d * E, kThreads);
-  const int np = n10 + n11 + nrr;
+  const int q0 = apply_e ? 0 : n10 + n11, q1 = apply_r ? n10 + n11 + nrr : n10 + n11;
   float* red = reinterpret_cast<float*>(smem);
   {
     float s = 0.f;
-    for (int i = tid; i < np; i += kThreads) s += p.norm_part[i];
+    for (int i = q0 + tid; i < q1; i += kThreads) s += p.norm_part[i];
     __syncthreads();
     red[tid] = s;
     __syncthreads();
@@ -1059,7 +1062,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   const long P4 = P / 4;
   const long nr4 = (long)d * E / 4;
   const float b1 = p.beta1, b2 = p.beta2, omb1 = p.omb1, omb2 = p.omb2, lr = p.lr, eps = p.eps, wd = p.wd;
-  const float ib1 = p.inv_bc1, isb2 = p.inv_sqrt_bc2;
+  // W_r is the float4 range [0, nr4), W1 | W2 the rest; each group has its own
+  // bias correction, and only the applied groups are updated
+  const long lo4 = apply_r ? 0 : nr4, hi4 = apply_e ? P4 : nr4;
   float4* P_ = reinterpret_cast<float4*>(p.params);
   const float4* G_ = reinterpret_cast<const float4*>(p.grads);
   float4* M_ = reinterpret_cast<float4*>(p.m);
@@ -1067,7 +1072,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   // every parameter, gradient and moment is touched once per update: stream them
   // with non-temporal loads and stores so they do not evict reused data
   typedef float nt4 __attribute__((ext_vector_type(4)));
-  auto adamw4 = [&](float4& w, const float4& g, float4& m, float4& v) {
+  auto adamw4 = [&](long i, float4& w, const float4& g, float4& m, float4& v) {
+    const int grp = i < nr4 ? 0 : 1;
+    const float ib1 = p.inv_bc1[grp], isb2 = p.inv_sqrt_bc2[grp];
     float* wv = &w.x;
     const float* gv = &g.x;
     float* mv = &m.x;
@@ -1094,8 +1101,8 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   };
   constexpr int U = 4;
   const long stride = (long)G * kThreads;
-  long i = (long)lwg * kThreads + tid;
-  for (; i + (U - 1) * stride < P4; i += U * stride) {
+  long i = lo4 + (long)lwg * kThreads + tid;
+  for (; i + (U - 1) * stride < hi4; i += U * stride) {
     float4 w[U], g[U], m[U], v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1110,13 +1117,13 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      adamw4(w[u], g[u], m[u], v[u]);
+      adamw4(i + u * stride, w[u], g[u], m[u], v[u]);
       store4(i + u * stride, w[u], m[u], v[u]);
     }
   }
-  for (; i < P4; i += stride) {
+  for (; i < hi4; i += stride) {
     float4 w = P_[i], g = G_[i], m = M_[i], v = V_[i];
-    adamw4(w, g, m, v);
+    adamw4(i, w, g, m, v);
     store4(i, w, m, v);
   }
 }
@@ -1129,8 +1136,9 @@ __global__ void __launch_bounds__(kThreads) moe_step_kernel(KParams p) {
   extern __shared__ __align__(16) char smem_raw[];
   Meta& meta = *reinterpret_cast<Meta*>(smem_raw);
   char* scratch = smem_raw + kMetaBytes;
-  const bool zero_grad = (p.flags & 0x1u) != 0u;
-  const bool apply = (p.flags & 0x2u) != 0u;
+  // the host has expanded the whole-update bits into the per-group ones
+  const bool zero_r = (p.flags & 0x10u) != 0u, zero_e = (p.flags & 0x20u) != 0u;
+  const bool apply_r = (p.flags & 0x40u) != 0u, apply_e = (p.flags & 0x80u) != 0u;
   const bool want_dx = p.dx != nullptr;
 
 #define MOE_SYNC(ph)                                                 \
@@ -1157,13 +1165,13 @@ __global__ void __launch_bounds__(kThreads) moe_step_kernel(KParams p) {
   if (!(skip & 16u)) phase_combine<T>(p, meta);
   MOE_SYNC(4);
   trace_mark(p, 5, 0);
-  if (!(skip & 32u)) phase_bwd2<T>(p, scratch, meta, zero_grad);
+  if (!(skip & 32u)) phase_bwd2<T>(p, scratch, meta, zero_e);
   MOE_SYNC(5);
   trace_mark(p, 6, 0);
-  if (!(skip & 64u)) phase_bwd1<T>(p, scratch, meta, zero_grad, want_dx);
+  if (!(skip & 64u)) phase_bwd1<T>(p, scratch, meta, zero_r, zero_e, want_dx);
   MOE_SYNC(6);
   trace_mark(p, 7, 0);
-  if (!(skip & 128u)) phase_final<T>(p, scratch, meta, zero_grad, apply, want_dx);
+  if (!(skip & 128u)) phase_final<T>(p, scratch, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
   __syncthreads();
   trace_mark(p, 7, 1);
   trace_mark(p, 7, 2);

@@ -32,15 +32,26 @@ class MoeLayerStep:
         self._shadow_valid = False
 
     def run(self, x, target, *, tokens_in_update=None, step=1, zero_grad=True, apply=True, dx=None,
-            router_bias=None, debug=None, trace=None, stream=None):
+            router_bias=None, debug=None, trace=None, stream=None, groups=None):
         """Enqueues one launch.  ``debug`` is an optional dict of preallocated debug tensors
-        (router_logits, topk_idx, topk_gate, expert_counts, route_perm)."""
+        (router_logits, topk_idx, topk_gate, expert_counts, route_perm).  ``groups`` (selective
+        updates) replaces zero_grad/apply/step by per-group settings: a dict with keys
+        zero_router, zero_experts, apply_router, apply_experts (bools) and step_router,
+        step_experts (ints)."""
         n = 0 if x is None else int(x.shape[0])
         flags = 0
-        if zero_grad:
-            flags |= B.MOE_RUN_ZERO_GRAD
-        if apply:
-            flags |= B.MOE_RUN_APPLY
+        step_r = step_e = step
+        if groups is not None:
+            for key, bit in (("zero_router", B.MOE_RUN_ZERO_GRAD_ROUTER), ("zero_experts", B.MOE_RUN_ZERO_GRAD_EXPERTS),
+                             ("apply_router", B.MOE_RUN_APPLY_ROUTER), ("apply_experts", B.MOE_RUN_APPLY_EXPERTS)):
+                if groups.get(key):
+                    flags |= bit
+            step_r, step_e = int(groups.get("step_router", 1)), int(groups.get("step_experts", 1))
+        else:
+            if zero_grad:
+                flags |= B.MOE_RUN_ZERO_GRAD
+            if apply:
+                flags |= B.MOE_RUN_APPLY
         if not self._shadow_valid:
             flags |= B.MOE_RUN_REFRESH_SHADOW
         if trace is not None:
@@ -52,7 +63,8 @@ class MoeLayerStep:
                        topk_gate=dbg.get("topk_gate"), expert_counts=dbg.get("expert_counts"),
                        route_perm=dbg.get("route_perm"), trace=trace)
         s = torch.cuda.current_stream(self.dev) if stream is None else stream
-        B.moe_step_run(self.handle, io, n, tokens_in_update or max(1, n), step, flags, s.cuda_stream)
+        B.moe_step_run_groups(self.handle, io, n, tokens_in_update or max(1, n), step_r, step_e, flags,
+                              s.cuda_stream)
         self._shadow_valid = True
 
     def status(self):

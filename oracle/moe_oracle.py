@@ -312,6 +312,52 @@ def step(xs, ts, params, exp_avg, exp_avg_sq, step_index, *, d, f, E, top_k,
     return out
 
 
+def selective_step(x, t, params, grads, exp_avg, exp_avg_sq, *, step_router, step_experts, d, f, E, top_k,
+                   tokens_in_update, zero_router, zero_experts, apply_router, apply_experts,
+                   lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, clip_norm=1.0,
+                   bias=None, act="gelu_tanh", forced_topk=None):
+    """One microbatch of the selective-update scheme (Latch pages, "Results",
+    table "Other measured compiler work": the shared weights update every
+    microbatch, the experts every 16).  Two parameter groups, the router W_r and
+    the experts W1 | W2, each with its own gradient accumulation window and its
+    own AdamW step count.
+
+    The pages give only the schedule; the reading taken here: the microbatch's
+    gradient (loss denominator ``tokens_in_update``) is added to the running
+    gradient of each group, which first restarts from zero for a group whose
+    ``zero_*`` flag is set; each group whose ``apply_*`` flag is set then gets
+    global-norm clipping and AdamW, the norm taken over the applied groups'
+    running gradients jointly (with both applied this is exactly ``step``).
+    Groups not applied keep their weights and moments.  Returns the new
+    params / grads / moments, the loss, dx and the routing."""
+    w_r, w1, w2 = unpack_params(params, d, f, E)
+    fw = layer_forward(x, t, w_r, w1, w2, top_k, tokens_in_update, bias=bias, act=act, forced_topk=forced_topk)
+    dgr, dg1, dg2, dx = layer_backward(fw, w_r, w1, w2)
+    nr = d * E
+    g_old = np.asarray(grads, np.float64)
+    g_new = pack(dgr, dg1, dg2)
+    acc = g_new.copy()
+    if not zero_router:
+        acc[:nr] += g_old[:nr]
+    if not zero_experts:
+        acc[nr:] += g_old[nr:]
+    new_p = np.asarray(params, np.float64).copy()
+    new_m = np.asarray(exp_avg, np.float64).copy()
+    new_v = np.asarray(exp_avg_sq, np.float64).copy()
+    applied = [s for s, on in ((slice(0, nr), apply_router), (slice(nr, None), apply_experts)) if on]
+    norm, c = None, None
+    if applied:
+        norm = global_norm([acc[s] for s in applied])
+        c = clip_coefficient(norm, clip_norm)
+        for s, on, stp in ((slice(0, nr), apply_router, step_router), (slice(nr, None), apply_experts, step_experts)):
+            if on:
+                new_p[s], new_m[s], new_v[s] = adamw(new_p[s], c * acc[s], new_m[s], new_v[s], stp,
+                                                     lr, beta1, beta2, eps, weight_decay)
+    return dict(loss=fw["loss"], grads=acc, grad_norm=norm, clip_coef=c, params=new_p, exp_avg=new_m,
+                exp_avg_sq=new_v, dx=dx,
+                routing={key: fw[key] for key in ("z", "sel", "g", "counts", "offsets", "perm", "inv")})
+
+
 def forward_loss(x, t, params, *, d, f, E, top_k, bias=None, act="gelu_tanh", forced_topk=None,
                  tokens_in_update=None):
     """Loss only (used by finite-difference pins)."""

@@ -80,6 +80,7 @@ def test_create_without_gpu_reports_hip_error():
 def test_null_handle_calls_are_safe():
     lib = B.load_library()
     assert lib.moe_step_run(None, None, 0, 1, 1, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_step_run_groups(None, None, 0, 1, 1, 1, 0, None) == B.MOE_ERR_ARG
     assert lib.moe_step_status(None) == B.MOE_ERR_ARG
     assert lib.moe_step_trace_words(None) == 0
     assert lib.moe_step_grid_size(None) == 0

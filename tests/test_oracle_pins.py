@@ -440,3 +440,77 @@ def test_zipf_bias_fixture_reproduces_target_loads():
     p = np.arange(1, cfg.n_experts + 1, dtype=np.float64) ** -1.2
     p /= p.sum()
     assert np.abs(load / p - 1).max() <= 0.05
+
+
+# ----------------------------------------------------------------------------
+# Selective updates (router every microbatch, experts on a longer window)
+# ----------------------------------------------------------------------------
+_SEL = dict(d=6, f=8, E=4, top_k=2, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def test_selective_step_with_both_groups_is_the_plain_update():
+    x, t, params, b = _tiny(40, 6, 8, 4, 2, 21, bias=True)
+    m0 = np.abs(np.random.default_rng(1).standard_normal(params.size)) * 1e-3
+    v0 = np.abs(np.random.default_rng(2).standard_normal(params.size)) * 1e-6
+    plain = oracle.step(x, t, params, m0, v0, 4, clip_norm=0.3, bias=b, **_SEL)
+    sel = oracle.selective_step(x, t, params, np.full_like(params, 7.0), m0, v0, step_router=4, step_experts=4,
+                                tokens_in_update=40, zero_router=True, zero_experts=True, apply_router=True,
+                                apply_experts=True, clip_norm=0.3, bias=b, **_SEL)
+    for key in ("params", "exp_avg", "exp_avg_sq", "grads"):
+        np.testing.assert_array_equal(sel[key], plain[key])
+    assert sel["loss"] == plain["loss"]
+
+
+def test_selective_router_only_first_step_closed_form():
+    # AdamW from zero moments at step 1 moves each weight by lr * (c g / (|c g| + eps) + wd w);
+    # the clip norm covers only the router gradient; the experts do not move
+    x, t, params, _ = _tiny(32, 6, 8, 4, 2, 22)
+    nr = 6 * 4
+    g = oracle.step(x, t, params, np.zeros_like(params), np.zeros_like(params), 1, clip_norm=0, **_SEL)["grads"]
+    for clip in (0.0, 1e-3):
+        out = oracle.selective_step(x, t, params, np.zeros_like(params), np.zeros_like(params),
+                                    np.zeros_like(params), step_router=1, step_experts=5, tokens_in_update=32,
+                                    zero_router=True, zero_experts=True, apply_router=True, apply_experts=False,
+                                    clip_norm=clip, **_SEL)
+        gr = g[:nr]
+        norm = math.sqrt(float((gr ** 2).sum()))
+        assert out["grad_norm"] == pytest.approx(norm, rel=1e-12)
+        c = 1.0 if clip == 0 else min(1.0, clip / (norm + 1e-6))
+        expect = params[:nr] - _SEL["lr"] * (c * gr / (np.abs(c * gr) + _SEL["eps"]) + _SEL["weight_decay"] * params[:nr])
+        np.testing.assert_allclose(out["params"][:nr], expect, rtol=1e-12, atol=1e-15)
+        np.testing.assert_array_equal(out["params"][nr:], params[nr:])
+        np.testing.assert_array_equal(out["exp_avg"][nr:], 0.0)
+        np.testing.assert_allclose(out["grads"], g, rtol=1e-13, atol=1e-17)
+
+
+def test_selective_expert_window_accumulates_each_microbatch_gradient():
+    # router applied every microbatch, experts restarted on the first and applied on
+    # the last: the expert gradient used is the sum of the per-microbatch gradients,
+    # each taken at the weights in force for that microbatch
+    rng = np.random.default_rng(23)
+    T, d, f, E, k, n_mb = 24, 6, 8, 4, 2, 3
+    xs = [rng.standard_normal((T, d)) for _ in range(n_mb)]
+    ts = [rng.standard_normal((T, d)) for _ in range(n_mb)]
+    params = np.concatenate([rng.standard_normal(d * E) * 0.8, rng.standard_normal(2 * E * d * f) * 0.5])
+    nr = d * E
+    p, m, v, grads = params.copy(), np.zeros_like(params), np.zeros_like(params), np.zeros_like(params)
+    expert_sum = np.zeros(params.size - nr)
+    for i in range(n_mb):
+        ref = oracle.step(xs[i], ts[i], p, np.zeros_like(p), np.zeros_like(p), 1, clip_norm=0, **_SEL)["grads"]
+        expert_sum += ref[nr:]
+        out = oracle.selective_step(xs[i], ts[i], p, grads, m, v, step_router=i + 1, step_experts=1,
+                                    tokens_in_update=T, zero_router=True, zero_experts=(i == 0),
+                                    apply_router=True, apply_experts=(i == n_mb - 1), clip_norm=0.5, **_SEL)
+        np.testing.assert_allclose(out["grads"][:nr], ref[:nr], rtol=1e-12, atol=1e-17)
+        np.testing.assert_allclose(out["grads"][nr:], expert_sum, rtol=1e-12, atol=1e-17)
+        if i < n_mb - 1:
+            np.testing.assert_array_equal(out["params"][nr:], params[nr:])
+        p, m, v, grads = out["params"], out["exp_avg"], out["exp_avg_sq"], out["grads"]
+    # the experts' single update: AdamW step 1, clipped by the joint norm of the two groups
+    # applied in the last launch (the last router gradient and the accumulated expert gradient)
+    norm = math.sqrt(float((expert_sum ** 2).sum()) + float((ref[:nr] ** 2).sum()))
+    c = min(1.0, 0.5 / (norm + 1e-6))
+    w_e, m_e, v_e = oracle.adamw(params[nr:], c * expert_sum, np.zeros_like(expert_sum), np.zeros_like(expert_sum),
+                                 1, _SEL["lr"], _SEL["beta1"], _SEL["beta2"], _SEL["eps"], _SEL["weight_decay"])
+    np.testing.assert_allclose(p[nr:], w_e, rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(v[nr:], v_e, rtol=1e-12, atol=1e-20)
