@@ -145,6 +145,18 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
   for (int e = 4 * EG0; e < 4 * (EG0 + EGT); ++e) acc[e] = 0.f;
   for (int c0 = 0; c0 < d; c0 += DC) {
     const int dc = min(DC, ceil_div(d - c0, 8 * S) * (8 * S));
+    const int ni = dc / (8 * S);
+    auto load_group = [&](int i0, Raw8<T> (&xr)[4]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + (i0 + u) * 8 * S + 8 * s_me;
+        xr[u] = Raw8<T>{};
+        if (mine && i0 + u < ni && c < d) xr[u] = ldr8(x + (long)tok * d + c);
+      }
+    };
+    // the token's first pieces are in flight while W_r is staged
+    Raw8<T> xa[4], xb[4];
+    load_group(0, xa);
     __syncthreads();
     // all of a thread's loads are issued before its LDS stores (16 per batch)
 #pragma unroll 16
@@ -167,17 +179,6 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
       wl[((i * 8 + j) * EG + eg) * S + s] = w;
     }
     __syncthreads();
-    const int ni = dc / (8 * S);
-    auto load_group = [&](int i0, Raw8<T> (&xr)[4]) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + (i0 + u) * 8 * S + 8 * s_me;
-        xr[u] = Raw8<T>{};
-        if (mine && i0 + u < ni && c < d) xr[u] = ldr8(x + (long)tok * d + c);
-      }
-    };
-    Raw8<T> xa[4], xb[4];
-    load_group(0, xa);
     for (int i0 = 0; i0 < ni; i0 += 4) {
       load_group(i0 + 4, xb);
 #pragma unroll
@@ -271,18 +272,39 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
       router_segment_sums<T, 8, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
       router_segment_sums<T, 8, 8>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
     }
-    // sum the S segments of each token (adjacent lanes), fixed order
+    // sum the S segments of each token in segment order: every thread parks its
+    // partial sums in LDS (rows of E + 4 floats, so the 16-byte writes of a
+    // wave spread over the banks), then one thread per (token, expert) adds
+    // them up; the staged W_r is dead by now, its space holds the partials
+    const int RW = ceil_div(E, 4) * 4 + 4;
+    if (S > 1 && kThreads * RW * 4 <= wbudget) {
+      float* part = reinterpret_cast<float*>(wl);
+      __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e) {
-      if (e < E) {
-        for (int m = S >> 1; m >= 1; m >>= 1) acc[e] += __shfl_xor(acc[e], m, 64);
+      for (int eg = 0; eg < kMaxExperts / 4; ++eg)
+        if (eg * 4 < E)
+          *reinterpret_cast<float4*>(part + tid * RW + eg * 4) =
+              make_float4(acc[eg * 4], acc[eg * 4 + 1], acc[eg * 4 + 2], acc[eg * 4 + 3]);
+      __syncthreads();
+      for (int o = tid; o < nb * E; o += kThreads) {
+        const int tk = o / E, e = o % E;
+        float s = 0.f;
+        for (int sg = 0; sg < S; ++sg) s += part[(tk * S + sg) * RW + e];
+        zacc[tk * EP + e] = s;
       }
-    }
-    __syncthreads();
-    if (t_me < nb && s_me == 0) {
+    } else {
 #pragma unroll
-      for (int e = 0; e < kMaxExperts; ++e)
-        if (e < E) zacc[t_me * EP + e] = acc[e];
+      for (int e = 0; e < kMaxExperts; ++e) {
+        if (e < E) {
+          for (int m = S >> 1; m >= 1; m >>= 1) acc[e] += __shfl_xor(acc[e], m, 64);
+        }
+      }
+      __syncthreads();
+      if (t_me < nb && s_me == 0) {
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e)
+          if (e < E) zacc[t_me * EP + e] = acc[e];
+      }
     }
     __syncthreads();
     // token_topk over each group of EP lanes (the group never crosses a wave)
