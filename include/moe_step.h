@@ -79,7 +79,15 @@ typedef struct {
                              rounds them to fp32 once */
   double clip_norm;       /* global-norm clip; <= 0 disables clipping */
   int32_t device;         /* HIP device ordinal */
-  int32_t wg_per_cu;      /* persistent workgroups per compute unit; 0 = 1 */
+  int32_t wg_per_cu;      /* persistent workgroups per compute unit: 1, 2, or 0 =
+                             automatic (2 for bf16 when max_tokens * top_k >=
+                             16384, else 1).  Two per unit runs a kernel built for
+                             half the registers and LDS per workgroup; fp32
+                             handles always run one.  Results differ between the
+                             settings at rounding level only: the split of the
+                             router dot products over lanes and the loss's
+                             per-workgroup partial sums follow the workgroup
+                             count. */
 } moe_step_config;
 
 /* Buffers of one launch.  Shapes use T = n_tokens, P = moe_step_param_count. */

@@ -89,10 +89,17 @@ int check_config(const moe_step_config* c, char* err) {
 
 }  // namespace
 
+// Routed rows (max_tokens * top_k) from which a bf16 handle runs two workgroups
+// per compute unit by default.
+constexpr long kTwoPerCuRows = 16384;
+
 struct moe_step {
   moe_step_config cfg;
   int grid = 0;
   int cus = 0;
+  int occ = 1;                  // workgroups per compute unit the kernel is built for
+  const void* kern = nullptr;   // that kernel
+  int smem = 0;                 // its dynamic LDS bytes per workgroup
   char* arena = nullptr;
   size_t arena_bytes = 0;
   hipStream_t last_stream = nullptr;
@@ -179,21 +186,29 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
     return MOE_ERR_DEVICE;
   }
 
-  const void* kern = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t>)
-                                                  : reinterpret_cast<const void*>(&moe::moe_step_kernel<float>);
-  he = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, moe::kSmemBytes);
+  // Two workgroups per compute unit pay off once the expert products have
+  // many tiles (each workgroup's waits are covered by the other's matrix
+  // work); small batches keep one, with the deeper pipeline and fewer
+  // workgroups at every grid barrier.  The fp32 kernel is built for one.
+  int want = cfg->wg_per_cu;
+  if (want == 0) want = (cfg->dtype == MOE_DTYPE_BF16 && (long)cfg->max_tokens * cfg->top_k >= kTwoPerCuRows) ? 2 : 1;
+  const int occ = (cfg->dtype == MOE_DTYPE_BF16 && want == 2) ? 2 : 1;
+  const void* kern = cfg->dtype == MOE_DTYPE_F32 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<float, 1>)
+                     : occ == 2                   ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t, 2>)
+                                                  : reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t, 1>);
+  const int smem = moe::smem_bytes(occ);
+  he = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (he != hipSuccess) {
-    set_err(g_create_error, "hipFuncSetAttribute(shared memory %d): %s", moe::kSmemBytes, hipGetErrorString(he));
+    set_err(g_create_error, "hipFuncSetAttribute(shared memory %d): %s", smem, hipGetErrorString(he));
     return MOE_ERR_HIP;
   }
   int per_cu = 0;
-  he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, moe::kThreads, moe::kSmemBytes);
+  he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, moe::kThreads, smem);
   if (he != hipSuccess || per_cu < 1) {
     set_err(g_create_error, "occupancy query failed or zero (%s, %d)", hipGetErrorString(he), per_cu);
     return MOE_ERR_HIP;
   }
-  const int want = cfg->wg_per_cu == 0 ? 1 : cfg->wg_per_cu;
-  const int use = want < per_cu ? want : per_cu;
+  const int use = occ < per_cu ? occ : per_cu;
 
   moe_step* h = new (std::nothrow) moe_step();
   if (!h) {
@@ -203,6 +218,9 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   h->cfg = *cfg;
   h->cus = prop.multiProcessorCount;
   h->grid = h->cus * use;
+  h->occ = occ;
+  h->kern = kern;
+  h->smem = smem;
 
   const int d = cfg->d_model, f = cfg->d_ff, E = cfg->n_experts, k = cfg->top_k;
   const size_t Tm = (size_t)cfg->max_tokens, N = Tm * k;
@@ -417,9 +435,7 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   }
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   void* args[] = {&p};
-  const void* kern = c.dtype == MOE_DTYPE_BF16 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t>)
-                                               : reinterpret_cast<const void*>(&moe::moe_step_kernel<float>);
-  he = hipLaunchCooperativeKernel(kern, dim3(h->grid), dim3(moe::kThreads), args, moe::kSmemBytes, stream);
+  he = hipLaunchCooperativeKernel(h->kern, dim3(h->grid), dim3(moe::kThreads), args, h->smem, stream);
   if (he != hipSuccess) {
     set_err(h->err, "hipLaunchCooperativeKernel: %s", hipGetErrorString(he));
     return MOE_ERR_HIP;

@@ -23,8 +23,15 @@ namespace moe {
 
 constexpr int kPhases = 8;
 constexpr int kMetaBytes = 2048;
-constexpr int kScratchBytes = gemm::LDS_BYTES > gemm::DMA_LDS_BYTES ? gemm::LDS_BYTES : gemm::DMA_LDS_BYTES;
-constexpr int kSmemBytes = kMetaBytes + kScratchBytes;
+// OCC workgroups per compute unit: the kernel is built for one (all of a
+// SIMD's registers per wave, 4-stage GEMM pipeline) or two (at most 256
+// registers per wave, 2-stage pipeline, half the LDS each).
+constexpr int dma_stages(int occ) { return occ == 1 ? 4 : 2; }
+constexpr int scratch_bytes(int occ) {
+  return gemm::LDS_BYTES > gemm::dma_lds_bytes(dma_stages(occ)) ? gemm::LDS_BYTES : gemm::dma_lds_bytes(dma_stages(occ));
+}
+constexpr int smem_bytes(int occ) { return kMetaBytes + scratch_bytes(occ); }
+static_assert(2 * smem_bytes(2) <= 160 * 1024, "two workgroups per compute unit must fit the LDS");
 constexpr int kRouterTokens = 128;   // tokens per router-gradient partial
 constexpr int kRouterBlockTokens = 32;
 
@@ -208,10 +215,55 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
   }
 }
 
+// Sums the S segment partials of experts [4 EG0, 4 (EG0 + EGT)) of each token
+// of the block into zacc, in segment order: every thread parks its partial
+// sums in LDS (rows of the pass's experts + 4 floats, so the 16-byte writes of
+// a wave spread over the banks), then one thread per (token, expert) adds them
+// up.  The staged W_r chunk is dead by now; its space holds the partials.
+// With one segment per token, or too little LDS, the segments are combined by
+// a butterfly over adjacent lanes instead.
+template <int EG0, int EGT>
+__device__ __forceinline__ void router_reduce(float (&acc)[kMaxExperts], float* zacc, float4* wl, int E, int EP, int S,
+                                              int nb, int t_me, int s_me, int wbudget) {
+  const int tid = threadIdx.x;
+  const int e0 = 4 * EG0, ne = min(E, 4 * (EG0 + EGT)) - e0;
+  const int RW = ceil_div(ne, 4) * 4 + 4;
+  if (S > 1 && kThreads * RW * 4 <= wbudget) {
+    float* part = reinterpret_cast<float*>(wl);
+    __syncthreads();
+#pragma unroll
+    for (int eg = 0; eg < EGT; ++eg)
+      if (eg * 4 < ne)
+        *reinterpret_cast<float4*>(part + tid * RW + eg * 4) =
+            make_float4(acc[e0 + eg * 4], acc[e0 + eg * 4 + 1], acc[e0 + eg * 4 + 2], acc[e0 + eg * 4 + 3]);
+    __syncthreads();
+    for (int o = tid; o < nb * ne; o += kThreads) {
+      const int tk = o / ne, e = o % ne;
+      float s = 0.f;
+      for (int sg = 0; sg < S; ++sg) s += part[(tk * S + sg) * RW + e];
+      zacc[tk * EP + e0 + e] = s;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4 * EGT; ++e) {
+      if (e < ne) {
+        for (int m = S >> 1; m >= 1; m >>= 1) acc[e0 + e] += __shfl_xor(acc[e0 + e], m, 64);
+      }
+    }
+    __syncthreads();
+    if (t_me < nb && s_me == 0) {
+#pragma unroll
+      for (int e = 0; e < 4 * EGT; ++e)
+        if (e < ne) zacc[t_me * EP + e0 + e] = acc[e0 + e];
+    }
+  }
+  __syncthreads();
+}
+
 // ===========================================================================
 // P0: weight-copy refresh, W_r^T, router logits + token_topk + gates + histogram
 // ===========================================================================
-template <typename T>
+template <typename T, int OCC>
 __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& meta) {
   const int tid = threadIdx.x;
   const int G = gridDim.x, lwg = logical_wg();
@@ -248,15 +300,21 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   // each piece index i, row j of the piece and 4-expert group eg, the S
   // segments' float4s side by side), so the reads of one wave are either
   // distinct consecutive 16-byte words or broadcasts.
+  // The logits of a block live in LDS (zacc, [TP][EP]) within a quarter of the
+  // scratch; a larger token range takes several blocks.
+  constexpr int kScratch = scratch_bytes(OCC);
   int TP = 1;
-  while (TP < min(t_hi - t_lo, kThreads)) TP <<= 1;
+  while (TP < min(t_hi - t_lo, kThreads) && 2 * TP * EP * 4 <= kScratch / 4) TP <<= 1;
   int S = min(64, kThreads / TP);
   while (S > 1 && 8 * S > d) S >>= 1;
   const int EG = (E + 3) / 4;
   float* zacc = reinterpret_cast<float*>(smem + 256);                          // [TP][EP]
   float4* wl = reinterpret_cast<float4*>(smem + 256 + TP * EP * 4);           // staged W_r chunk
   // (the reads of padded expert groups may run up to 16 * S float4 past the chunk)
-  const int wbudget = kScratchBytes - 256 - TP * EP * 4 - 16 * 64 * 16;
+  const int wbudget = kScratch - 256 - TP * EP * 4 - 16 * 64 * 16;
+  // a chunk holds at least one 8-column piece per segment for every expert
+  // group (8 EG 16 <= 2 KB always fits, so this ends with DC >= 8 S)
+  while (S > 1 && 8 * S * EG * 16 > wbudget) S >>= 1;
   int DC = (wbudget / (EG * 16)) / (8 * S) * (8 * S);                           // columns per chunk
   DC = min(DC, ceil_div(d, 8 * S) * (8 * S));
   const int t_me = tid / S, s_me = tid % S;
@@ -264,49 +322,31 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
     const int nb = min(TP, t_hi - b0);
     float acc[kMaxExperts];
-    // more than 16 experts: two passes over the columns, 8 expert groups each
-    // (one pass over all 64 would not fit the register file)
     if (EG <= 4) {
       router_segment_sums<T, 4, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-    } else {
+      router_reduce<0, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+    } else if constexpr (OCC == 1) {
+      // more than 16 experts: two passes over the columns, 8 expert groups
+      // each (one pass over all 64 would not fit the register file)
       router_segment_sums<T, 8, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
       router_segment_sums<T, 8, 8>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-    }
-    // sum the S segments of each token in segment order: every thread parks its
-    // partial sums in LDS (rows of E + 4 floats, so the 16-byte writes of a
-    // wave spread over the banks), then one thread per (token, expert) adds
-    // them up; the staged W_r is dead by now, its space holds the partials
-    const int RW = ceil_div(E, 4) * 4 + 4;
-    if (S > 1 && kThreads * RW * 4 <= wbudget) {
-      float* part = reinterpret_cast<float*>(wl);
-      __syncthreads();
-#pragma unroll
-      for (int eg = 0; eg < kMaxExperts / 4; ++eg)
-        if (eg * 4 < E)
-          *reinterpret_cast<float4*>(part + tid * RW + eg * 4) =
-              make_float4(acc[eg * 4], acc[eg * 4 + 1], acc[eg * 4 + 2], acc[eg * 4 + 3]);
-      __syncthreads();
-      for (int o = tid; o < nb * E; o += kThreads) {
-        const int tk = o / E, e = o % E;
-        float s = 0.f;
-        for (int sg = 0; sg < S; ++sg) s += part[(tk * S + sg) * RW + e];
-        zacc[tk * EP + e] = s;
-      }
+      router_reduce<0, 16>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
     } else {
-#pragma unroll
-      for (int e = 0; e < kMaxExperts; ++e) {
-        if (e < E) {
-          for (int m = S >> 1; m >= 1; m >>= 1) acc[e] += __shfl_xor(acc[e], m, 64);
-        }
+      // with half the registers: passes of 16 experts, each summed over the
+      // segments before the next one starts
+      router_segment_sums<T, 4, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+      router_reduce<0, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+      router_segment_sums<T, 4, 4>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+      router_reduce<4, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+      if (EG > 8) {
+        router_segment_sums<T, 4, 8>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+        router_reduce<8, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
       }
-      __syncthreads();
-      if (t_me < nb && s_me == 0) {
-#pragma unroll
-        for (int e = 0; e < kMaxExperts; ++e)
-          if (e < E) zacc[t_me * EP + e] = acc[e];
+      if (EG > 12) {
+        router_segment_sums<T, 4, 12>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
+        router_reduce<12, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
       }
     }
-    __syncthreads();
     // token_topk over each group of EP lanes (the group never crosses a wave)
     for (int g0 = 0; g0 < nb; g0 += TPI) {
       const int tok = b0 + g0 + slot;
@@ -493,7 +533,7 @@ __device__ __forceinline__ const T* w2_ptr(const KParams& p) {
 // ===========================================================================
 // P2: ragged_mm 1 + GELU.  Rows of expert e: x[perm[p]/k], p in its segment.
 // ===========================================================================
-template <typename T>
+template <typename T, int NS>
 __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Meta& meta) {
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f;
@@ -535,12 +575,12 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
               *reinterpret_cast<uint4*>(xs + (long)(p0 + r) * d + col) = gemm::dma_krows_unit(st, r, u);
           }
         };
-        gemm::tile<T, false, true>(lds, A, B, d, p.zero, epi, sink);
+        gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi, sink);
       } else {
-        gemm::tile<T, false, true>(lds, A, B, d, p.zero, epi);
+        gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
       }
     } else {
-      gemm::tile<T, false, true>(lds, A, B, d, p.zero, epi);
+      gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
     }
   }
 }
@@ -548,7 +588,7 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
 // ===========================================================================
 // P3: ragged_mm 2:  O = A_e W2[e]
 // ===========================================================================
-template <typename T>
+template <typename T, int NS>
 __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Meta& meta) {
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f;
@@ -565,7 +605,7 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
     gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1, 0, f, d,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
-    gemm::tile<T, false, true>(lds, A, B, f, p.zero, [&](int r, int c, const float (&v)[8]) {
+    gemm::tile<T, NS, false, true>(lds, A, B, f, p.zero, [&](int r, int c, const float (&v)[8]) {
       if (r < mrows && n0 + c < d) {
         F8 o;
 #pragma unroll
@@ -705,7 +745,7 @@ __device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
 // ===========================================================================
 // P5: dH = (dO W2[e]^T) * G' ; dW2[e] = A_e^T dO ; router-gradient partials
 // ===========================================================================
-template <typename T>
+template <typename T, int NS>
 __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_experts) {
   const int tid = threadIdx.x;
   const int G = gridDim.x, lwg = logical_wg();
@@ -741,7 +781,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, pe, ce, d, n0};
       float* g = gw2 + (long)e * f * d;
       float sq = 0.f;
-      gemm::tile<T, true, true>(
+      gemm::tile<T, NS, true, true>(
           lds, A, B, ce, p.zero,
           [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
             if (m0 + r < f && n0 + c < d) {
@@ -773,7 +813,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, f - nt * gemm::BN), d, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(
+      gemm::tile<T, NS, false, false>(
           lds, A, B, d, p.zero,
           [&](int r, int c, const float (&v)[8], const Raw8<T>& graw) {
             if (r < mrows && n0 + c < f) {
@@ -841,7 +881,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 // ===========================================================================
 // P6: dW1[e] = X_e^T dH ; dXs = dH W1[e]^T ; router gradient reduction
 // ===========================================================================
-template <typename T>
+template <typename T, int NS>
 __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& meta, bool zero_router, bool zero_experts,
                                            bool want_dx) {
   const int tid = threadIdx.x;
@@ -878,7 +918,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, pe, ce, f, n0};
       float* g = gw1 + (long)e * d * f;
       float sq = 0.f;
-      gemm::tile<T, true, true>(
+      gemm::tile<T, NS, true, true>(
           lds, A, B, ce, p.zero,
           [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
             if (m0 + r < d && n0 + c < f) {
@@ -910,7 +950,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1,
                       nt * gemm::BN, min(gemm::BN, d - nt * gemm::BN), f, 0};
       const int n0 = nt * gemm::BN;
-      gemm::tile<T, false, false>(
+      gemm::tile<T, NS, false, false>(
           lds, A, B, f, p.zero,
           [&](int r, int c, const float (&v)[8], int slot) {
             if (r < mrows && n0 + c < d) {
@@ -1153,8 +1193,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
 // ===========================================================================
 // The persistent kernel: one cooperative launch per update (or microbatch)
 // ===========================================================================
-template <typename T>
-__global__ void __launch_bounds__(kThreads) moe_step_kernel(KParams p) {
+template <typename T, int OCC>
+__global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
+  constexpr int NS = dma_stages(OCC);
   extern __shared__ __align__(16) char smem_raw[];
   Meta& meta = *reinterpret_cast<Meta*>(smem_raw);
   char* scratch = smem_raw + kMetaBytes;
@@ -1172,25 +1213,25 @@ __global__ void __launch_bounds__(kThreads) moe_step_kernel(KParams p) {
 
   const unsigned skip = p.flags >> 8;
   trace_mark(p, 0, 0);
-  if (!(skip & 1u)) phase_route<T>(p, scratch, meta);
+  if (!(skip & 1u)) phase_route<T, OCC>(p, scratch, meta);
   MOE_SYNC(0);
   trace_mark(p, 1, 0);
   phase_order(p, scratch, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
   MOE_SYNC(1);
   trace_mark(p, 2, 0);
-  if (!(skip & 4u)) phase_ffn1<T>(p, scratch, meta);
+  if (!(skip & 4u)) phase_ffn1<T, NS>(p, scratch, meta);
   MOE_SYNC(2);
   trace_mark(p, 3, 0);
-  if (!(skip & 8u)) phase_ffn2<T>(p, scratch, meta);
+  if (!(skip & 8u)) phase_ffn2<T, NS>(p, scratch, meta);
   MOE_SYNC(3);
   trace_mark(p, 4, 0);
   if (!(skip & 16u)) phase_combine<T>(p, meta);
   MOE_SYNC(4);
   trace_mark(p, 5, 0);
-  if (!(skip & 32u)) phase_bwd2<T>(p, scratch, meta, zero_e);
+  if (!(skip & 32u)) phase_bwd2<T, NS>(p, scratch, meta, zero_e);
   MOE_SYNC(5);
   trace_mark(p, 6, 0);
-  if (!(skip & 64u)) phase_bwd1<T>(p, scratch, meta, zero_r, zero_e, want_dx);
+  if (!(skip & 64u)) phase_bwd1<T, NS>(p, scratch, meta, zero_r, zero_e, want_dx);
   MOE_SYNC(6);
   trace_mark(p, 7, 0);
   if (!(skip & 128u)) phase_final<T>(p, scratch, meta, zero_r || zero_e, apply_r, apply_e, want_dx);

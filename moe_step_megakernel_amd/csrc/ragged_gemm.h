@@ -344,11 +344,11 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
 // loop waits on the vector-memory counter itself and synchronises with a bare
 // s_barrier, so the loads of later k-tiles stay in flight across it.
 // ---------------------------------------------------------------------------
-constexpr int DMA_STAGES = 4;
 constexpr int DMA_OP = 16384;                  // bytes per operand per stage
 constexpr int DMA_STAGE = 2 * DMA_OP;
-constexpr int DMA_LDS_BYTES = DMA_STAGES * DMA_STAGE;   // 131,072 bytes
-static_assert(BM * CROW * 4 <= DMA_LDS_BYTES, "staged tile must fit");
+// LDS of a tile with NS stages: the stages, or the staged fp32 tile of the
+// epilogue if that is larger (4 stages: 131,072 bytes; 2 stages: 67,584)
+constexpr int dma_lds_bytes(int NS) { return NS * DMA_STAGE > BM * CROW * 4 ? NS * DMA_STAGE : BM * CROW * 4; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
@@ -563,19 +563,22 @@ __device__ __forceinline__ void pipe_mma(const Frags& c, f32x16_t (&acc)[2][2]) 
 // bf16 tile through the DMA pipeline.  sink(kt, stage) runs once per k-tile
 // after its data landed (all waves), before any wave reads it for the MFMAs.
 //
-// Schedule of k-tile kt (stage slot kt % 4; the fragments of chunks 0 and 1
-// are already read, F[c] holds chunk c):
+// Schedule of k-tile kt (NS stages, slot kt % NS; the fragments of chunks 0
+// and 1 are already read, F[c] holds chunk c):
 //   MFMAs of chunk 0 | reads of chunk 2 -> F2 | wait for F1
 //   MFMAs of chunk 1 | reads of chunk 3 -> F3 | wait for all: stage kt is in registers
 //   wait for the loads of stage kt+1, barrier, sink, issue the loads of stage
-//   kt+4 into slot kt % 4 (every wave is past its reads of it)
+//   kt+NS into slot kt % NS (every wave is past its reads of it)
 //   MFMAs of chunk 2 | reads of chunk 0 of stage kt+1 -> F0
 //   MFMAs of chunk 3 | reads of chunk 1 of stage kt+1 -> F1 | wait for F0
-// so three k-tiles of loads are in flight while one is computed, and each LDS
-// read has at least one block of matrix work to hide behind.
-template <bool MN_A, bool MN_B, class Epi, class Sink, class Pre>
+// so NS - 1 k-tiles of loads are in flight while one is computed, and each
+// LDS read has at least one block of matrix work to hide behind.  NS = 4 with
+// one workgroup per compute unit; NS = 2 when two workgroups share one (each
+// then has half the LDS, and the other workgroup's work covers the waits).
+template <int NS, bool MN_A, bool MN_B, class Epi, class Sink, class Pre>
 __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
                                          Epi&& epi, Sink&& sink, Pre&& pre) {
+  static_assert(NS >= 2 && NS <= 4, "wait_vm covers up to two k-tiles in flight behind the one awaited");
   using P = Pipe<MN_A, MN_B>;
   f32x16_t acc[2][2];
 #pragma unroll
@@ -590,7 +593,7 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
   db.init(B);
   const int nk = (K + 63) / 64;
   lds_sync();  // the previous user of this LDS is done (its global stores may still be in flight)
-  for (int j = 0; j < DMA_STAGES - 1 && j < nk; ++j) {
+  for (int j = 0; j < NS - 1 && j < nk; ++j) {
     char* st = lds + j * DMA_STAGE;
     da.issue(A, j, st, zero);
     db.issue(B, j, st + DMA_OP, zero);
@@ -607,37 +610,37 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
       fb0[c] = dma_frag_addr<MN_B>(lds + DMA_OP, wn * 64, c);
       fb1[c] = dma_frag_addr<MN_B>(lds + DMA_OP, wn * 64 + 32, c);
     }
-    wait_vm(min(DMA_STAGES - 2, nk - 1));
+    wait_vm(min(NS - 2, nk - 1));
     lds_barrier();
     sink(0, lds);
-    if (DMA_STAGES - 1 < nk) {
-      char* nx = lds + (DMA_STAGES - 1) * DMA_STAGE;
-      da.issue(A, DMA_STAGES - 1, nx, zero);
-      db.issue(B, DMA_STAGES - 1, nx + DMA_OP, zero);
+    if (NS - 1 < nk) {
+      char* nx = lds + (NS - 1) * DMA_STAGE;
+      da.issue(A, NS - 1, nx, zero);
+      db.issue(B, NS - 1, nx + DMA_OP, zero);
     }
     Frags F0, F1, F2, F3;
     P::template step<false, -1>(F0, F0, acc, fa0[0], fa1[0], fb0[0], fb1[0]);
     P::template step<false, 0>(F1, F1, acc, fa0[1], fa1[1], fb0[1], fb1[1]);
     for (int kt = 0; kt < nk - 1; ++kt) {
-      const uint32_t so = (uint32_t)(kt % DMA_STAGES) * DMA_STAGE;
-      const uint32_t sn = (uint32_t)((kt + 1) % DMA_STAGES) * DMA_STAGE;
+      const uint32_t so = (uint32_t)(kt % NS) * DMA_STAGE;
+      const uint32_t sn = (uint32_t)((kt + 1) % NS) * DMA_STAGE;
       P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
       P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
-      // every stage up to min(kt + 3, nk - 1) has all its loads issued
-      wait_vm(min(DMA_STAGES - 2, nk - 2 - kt));
+      // every stage up to min(kt + NS - 1, nk - 1) has all its loads issued
+      wait_vm(min(NS - 2, nk - 2 - kt));
       lds_barrier();
       sink(kt + 1, lds + sn);
-      if (kt + DMA_STAGES < nk) {
+      if (kt + NS < nk) {
         char* nx = lds + so;
-        da.issue(A, kt + DMA_STAGES, nx, zero);
-        db.issue(B, kt + DMA_STAGES, nx + DMA_OP, zero);
+        da.issue(A, kt + NS, nx, zero);
+        db.issue(B, kt + NS, nx + DMA_OP, zero);
       }
       P::template step<true, -1>(F0, F2, acc, fa0[0] + sn, fa1[0] + sn, fb0[0] + sn, fb1[0] + sn);
       P::template step<true, 1>(F1, F3, acc, fa0[1] + sn, fa1[1] + sn, fb0[1] + sn, fb1[1] + sn);
     }
     {
       // last k-tile: its chunks 0 and 1 are in flight or landed
-      const uint32_t so = (uint32_t)((nk - 1) % DMA_STAGES) * DMA_STAGE;
+      const uint32_t so = (uint32_t)((nk - 1) % NS) * DMA_STAGE;
       P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
       P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
       pipe_mma<MN_A, MN_B>(F2, acc);
@@ -658,11 +661,12 @@ struct NoSink {
   __device__ __forceinline__ void operator()(int, const char*) const {}
 };
 
-// One tile: bf16 through the DMA pipeline, fp32 through register staging.
-template <typename T, bool MN_A, bool MN_B, class Epi, class Sink = NoSink, class Pre = NoPre>
+// One tile: bf16 through the DMA pipeline (NS stages), fp32 through register
+// staging.
+template <typename T, int NS, bool MN_A, bool MN_B, class Epi, class Sink = NoSink, class Pre = NoPre>
 __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
                                      Epi&& epi, Sink&& sink = Sink(), Pre&& pre = Pre()) {
-  if constexpr (sizeof(T) == 2) tile_dma<MN_A, MN_B>(lds, A, B, K, zero, epi, sink, pre);
+  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B>(lds, A, B, K, zero, epi, sink, pre);
   else tile_reg<T, MN_A, MN_B>(lds, A, B, K, epi, pre);
 }
 

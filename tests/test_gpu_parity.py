@@ -84,6 +84,14 @@ def test_ragged_shapes_bf16(T, d, f, E, k):
     _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1)
 
 
+@pytest.mark.parametrize("T,d,f,E,k", [(333, 72, 136, 5, 2), (1000, 256, 384, 16, 2), (300, 128, 64, 64, 8)])
+def test_ragged_shapes_bf16_two_workgroups_per_cu(T, d, f, E, k):
+    # the kernel built for two workgroups per compute unit: 2-stage GEMM
+    # pipeline, half the LDS, router passes of 16 experts (E = 64 takes four)
+    cfg = synth.small_config("ragged_bf16_occ2", T, d, f, E, k, "bf16")
+    _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1, wg_per_cu=2)
+
+
 def test_bf16_2x1024_two_steps():
     cfg = synth.CONFIGS["bf16_2x1024"]
     _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL)
