@@ -6,7 +6,8 @@
 //
 //   P0  bf16 weight copy refresh (optional); copy of W_r^T;
 //       router logits, token_topk, gates, per-workgroup expert histogram
-//   P1  route_order: global offsets, stable scatter into perm / inv
+//   P1  route_order: global offsets, stable scatter into perm / inv; the
+//       dispatch gather of the token rows into expert order (bf16)
 //   P2  ragged_mm 1 + GELU        A = gelu(X_e W1[e]),  G' = gelu'(X_e W1[e])
 //   P3  ragged_mm 2               O = A_e W2[e]
 //   P4  weighted combine, loss, dL/dO, dL/dgate, dL/dlogit
@@ -89,7 +90,7 @@ struct KParams {
   float* loss_part;  // [G]
   float* norm_part;  // [n10 + n11 + nr]
   uint16_t* shadow;  // [2*E*d*f] bf16 copy of W1 | W2 (bf16 mode)
-  void* xs;          // [N, d] token rows in expert order (bf16 mode), written by GEMM 1
+  void* xs;          // [N, d] token rows in expert order (bf16 mode), written by route_order
   const char* zero;  // 256 zero bytes (source of out-of-range tile elements)
   Ctrl ctrl;
 };
@@ -417,6 +418,7 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
 // ===========================================================================
 // P1: route_order -- offsets and a stable scatter of the flat ids by expert
 // ===========================================================================
+template <typename T>
 __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& meta, bool skip_scatter) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, lwg = logical_wg();
@@ -429,6 +431,7 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   int* st = sp + kThreads;                            // [parts][EP] totals
   int* base = st + kThreads;                          // [EP]
   int* cw = base + kMaxExperts;                       // [kWaves][EP]
+  int* posl = cw + kWaves * kMaxExperts;              // [kThreads] sorted positions of this block
   {
     const int e = tid % EP, part = tid / EP;
     int pre = 0, tot = 0;
@@ -503,8 +506,23 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
       p.perm[pos] = q;
       p.inv[q] = pos;
       if (p.dbg_perm) p.dbg_perm[pos] = q;
+      posl[tid] = pos;
     }
     __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      // dispatch gather: the token row of each routed row of this block is
+      // copied to its sorted position (xs, [N, d] in expert order), so the
+      // expert products read contiguous rows
+      const int nq = min(kThreads, q_hi - q0), d = p.d, U = d / 8;
+      const uint16_t* xg = reinterpret_cast<const uint16_t*>(p.x);
+      uint16_t* xs = reinterpret_cast<uint16_t*>(p.xs);
+#pragma unroll 4
+      for (int u = tid; u < nq * U; u += kThreads) {
+        const int i = u / U, c = (u - i * U) * 8;
+        *reinterpret_cast<uint4*>(xs + (long)posl[i] * d + c) =
+            *reinterpret_cast<const uint4*>(xg + (long)((q0 + i) / k) * d + c);
+      }
+    }
     if (tid < E) {
       int s = 0;
       for (int w = 0; w < kWaves; ++w) s += cw[w * EP + tid];
@@ -531,7 +549,8 @@ __device__ __forceinline__ const T* w2_ptr(const KParams& p) {
 }
 
 // ===========================================================================
-// P2: ragged_mm 1 + GELU.  Rows of expert e: x[perm[p]/k], p in its segment.
+// P2: ragged_mm 1 + GELU.  Rows of expert e: x[perm[p]/k], p in its segment
+// (bf16: read from the copy in xs).
 // ===========================================================================
 template <typename T, int NS>
 __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Meta& meta) {
@@ -548,7 +567,10 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
     const int m0 = (mg - meta.moff[e]) * gemm::BM;
     const int p0 = meta.off[e] + m0;
     const int mrows = min(gemm::BM, meta.cnt[e] - m0);
-    gemm::Operand A{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, p0, mrows, d, 0};
+    // bf16: the gathered rows (xs, contiguous); fp32: token rows through perm
+    const gemm::Operand A = sizeof(T) == 2
+                                ? gemm::Operand{reinterpret_cast<const char*>(p.xs), d, nullptr, 1, p0, mrows, d, 0}
+                                : gemm::Operand{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, p0, mrows, d, 0};
     gemm::Operand B{reinterpret_cast<const char*>(w1_ptr<T>(p) + (long)e * d * f), f, nullptr, 1, 0, d, f,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
@@ -562,26 +584,7 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
         st8(gp + o, da);
       }
     };
-    if constexpr (sizeof(T) == 2) {
-      if (nt == 0) {
-        // the first column block also writes the gathered token rows in expert
-        // order, for the dW1 product (its k runs over these rows)
-        uint16_t* xs = reinterpret_cast<uint16_t*>(p.xs);
-        auto sink = [&](int kt, const char* st) {
-          for (int idx = threadIdx.x; idx < gemm::BM * 8; idx += kThreads) {
-            const int r = idx >> 3, u = idx & 7;
-            const int col = kt * 64 + u * 8;
-            if (r < mrows && col < d)
-              *reinterpret_cast<uint4*>(xs + (long)(p0 + r) * d + col) = gemm::dma_krows_unit(st, r, u);
-          }
-        };
-        gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi, sink);
-      } else {
-        gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
-      }
-    } else {
-      gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
-    }
+    gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
   }
 }
 
@@ -793,7 +796,6 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
               for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
             }
           },
-          gemm::NoSink(),
           [&](int r, int c) {
             Raw8<float> old{};
             if (!zero_experts && m0 + r < f && n0 + c < d) old = ldr8(g + (long)(m0 + r) * d + n0 + c);
@@ -823,7 +825,6 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
               st8(dh + (long)(p0 + r) * f + n0 + c, g8);
             }
           },
-          gemm::NoSink(),
           [&](int r, int c) {
             Raw8<T> graw{};
             if (r < mrows && n0 + c < f) graw = ldr8(gp + (long)(p0 + r) * f + n0 + c);
@@ -930,7 +931,6 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
               for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
             }
           },
-          gemm::NoSink(),
           [&](int r, int c) {
             Raw8<float> old{};
             if (!zero_experts && m0 + r < d && n0 + c < f) old = ldr8(g + (long)(m0 + r) * f + n0 + c);
@@ -960,7 +960,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
               st8(dxs + (long)slot * d + n0 + c, o);
             }
           },
-          gemm::NoSink(), [&](int r, int c) { return (r < mrows && n0 + c < d) ? p.perm[p0 + r] : 0; });
+          [&](int r, int c) { return (r < mrows && n0 + c < d) ? p.perm[p0 + r] : 0; });
     } else {
       // dW_r[c][e] = sum over token chunks (ascending) of the partials
       const int ir = item - n11 - n12;
@@ -1216,7 +1216,7 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   if (!(skip & 1u)) phase_route<T, OCC>(p, scratch, meta);
   MOE_SYNC(0);
   trace_mark(p, 1, 0);
-  phase_order(p, scratch, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
+  phase_order<T>(p, scratch, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
   MOE_SYNC(1);
   trace_mark(p, 2, 0);
   if (!(skip & 4u)) phase_ffn1<T, NS>(p, scratch, meta);

@@ -425,14 +425,6 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
-// Reads logical 16-byte unit u of row r from a K-rows DMA stage.
-__device__ __forceinline__ uint4 dma_krows_unit(const char* st, int r, int u) {
-  const uint32_t a = lds_addr(st + r * 128 + ((u ^ ((r >> 1) & 7)) << 4));
-  u32x4_t v;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // LDS byte address of this lane's fragment (K-rows: the b128 read; MN-rows:
 // the first of the two transpose reads, the second is 1024 bytes further)
 template <bool MN>
@@ -560,14 +552,13 @@ __device__ __forceinline__ void pipe_mma(const Frags& c, f32x16_t (&acc)[2][2]) 
 #undef MOE_PIPE_OUTS_KK
 #undef MOE_PIPE_OUTS_MM
 
-// bf16 tile through the DMA pipeline.  sink(kt, stage) runs once per k-tile
-// after its data landed (all waves), before any wave reads it for the MFMAs.
+// bf16 tile through the DMA pipeline.
 //
 // Schedule of k-tile kt (NS stages, slot kt % NS; the fragments of chunks 0
 // and 1 are already read, F[c] holds chunk c):
 //   MFMAs of chunk 0 | reads of chunk 2 -> F2 | wait for F1
 //   MFMAs of chunk 1 | reads of chunk 3 -> F3 | wait for all: stage kt is in registers
-//   wait for the loads of stage kt+1, barrier, sink, issue the loads of stage
+//   wait for the loads of stage kt+1, barrier, issue the loads of stage
 //   kt+NS into slot kt % NS (every wave is past its reads of it)
 //   MFMAs of chunk 2 | reads of chunk 0 of stage kt+1 -> F0
 //   MFMAs of chunk 3 | reads of chunk 1 of stage kt+1 -> F1 | wait for F0
@@ -575,9 +566,9 @@ __device__ __forceinline__ void pipe_mma(const Frags& c, f32x16_t (&acc)[2][2]) 
 // LDS read has at least one block of matrix work to hide behind.  NS = 4 with
 // one workgroup per compute unit; NS = 2 when two workgroups share one (each
 // then has half the LDS, and the other workgroup's work covers the waits).
-template <int NS, bool MN_A, bool MN_B, class Epi, class Sink, class Pre>
+template <int NS, bool MN_A, bool MN_B, class Epi, class Pre>
 __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
-                                         Epi&& epi, Sink&& sink, Pre&& pre) {
+                                         Epi&& epi, Pre&& pre) {
   static_assert(NS >= 2 && NS <= 4, "wait_vm covers up to two k-tiles in flight behind the one awaited");
   using P = Pipe<MN_A, MN_B>;
   f32x16_t acc[2][2];
@@ -612,7 +603,6 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
     }
     wait_vm(min(NS - 2, nk - 1));
     lds_barrier();
-    sink(0, lds);
     if (NS - 1 < nk) {
       char* nx = lds + (NS - 1) * DMA_STAGE;
       da.issue(A, NS - 1, nx, zero);
@@ -629,7 +619,6 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
       // every stage up to min(kt + NS - 1, nk - 1) has all its loads issued
       wait_vm(min(NS - 2, nk - 2 - kt));
       lds_barrier();
-      sink(kt + 1, lds + sn);
       if (kt + NS < nk) {
         char* nx = lds + so;
         da.issue(A, kt + NS, nx, zero);
@@ -657,16 +646,12 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
   epilogue(lds, acc, epi, pre);
 }
 
-struct NoSink {
-  __device__ __forceinline__ void operator()(int, const char*) const {}
-};
-
 // One tile: bf16 through the DMA pipeline (NS stages), fp32 through register
 // staging.
-template <typename T, int NS, bool MN_A, bool MN_B, class Epi, class Sink = NoSink, class Pre = NoPre>
+template <typename T, int NS, bool MN_A, bool MN_B, class Epi, class Pre = NoPre>
 __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
-                                     Epi&& epi, Sink&& sink = Sink(), Pre&& pre = Pre()) {
-  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B>(lds, A, B, K, zero, epi, sink, pre);
+                                     Epi&& epi, Pre&& pre = Pre()) {
+  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B>(lds, A, B, K, zero, epi, pre);
   else tile_reg<T, MN_A, MN_B>(lds, A, B, K, epi, pre);
 }
 
