@@ -139,6 +139,16 @@ typedef struct {
  * 7 dx sum + norm + clip/AdamW. */
 #define MOE_RUN_SKIP_PHASE(i) (0x100u << (i))
 #define MOE_RUN_SKIP_MASK 0xff00u
+/* Readiness-driven scheduling between expert GEMM 1 and GEMM 2 (the pages'
+ * "Open problems", Performance 1: replace whole-grid barriers by finer
+ * dependencies).  Without it a grid barrier separates the two products.  With
+ * it there is none: every GEMM-1 tile, once its stores are out, releases at
+ * agent scope and counts itself done on its 128-row tile, and a GEMM-2 tile
+ * waits (bounded) until every GEMM-1 column tile of its rows is counted, then
+ * acquires.  Results are identical.  It is slower on MI355X (each release
+ * writes the XCD's L2 back to memory, each acquire drops the L2's clean lines),
+ * so it is off by default. */
+#define MOE_RUN_READY_GEMM12 0x10000u
 
 /* Status-word bits reported by moe_step_status as MOE_ERR_DEVICE. */
 #define MOE_DEVICE_BARRIER_TIMEOUT 0x1u

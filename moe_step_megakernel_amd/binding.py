@@ -19,6 +19,7 @@ MOE_RUN_ZERO_GRAD, MOE_RUN_APPLY, MOE_RUN_REFRESH_SHADOW, MOE_RUN_TRACE = 0x1, 0
 MOE_RUN_SKIP_MASK = 0xFF00
 MOE_RUN_ZERO_GRAD_ROUTER, MOE_RUN_ZERO_GRAD_EXPERTS = 0x10, 0x20
 MOE_RUN_APPLY_ROUTER, MOE_RUN_APPLY_EXPERTS = 0x40, 0x80
+MOE_RUN_READY_GEMM12 = 0x10000
 
 
 def MOE_RUN_SKIP_PHASE(i: int) -> int:

@@ -204,6 +204,25 @@ __device__ __forceinline__ bool wait_for(const Ctrl& c, const unsigned* p, unsig
   return true;
 }
 
+// Polls *p (relaxed, agent scope) until it is at least target; false on
+// timeout or when another workgroup already gave up.
+__device__ __forceinline__ bool wait_count(const Ctrl& c, const int* p, int target) {
+  const uint64_t t0 = wall_clock64();
+  unsigned polls = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if ((++polls & 255u) == 0u) {
+      if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+          wall_clock64() - t0 > kBarrierTimeoutTicks) {
+        __hip_atomic_fetch_or(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(c.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+      }
+    }
+  }
+  return true;
+}
+
 // Grid-wide barrier.  Every wave first waits until its own stores have
 // reached L2; after a workgroup barrier one wave releases at agent scope for
 // the whole workgroup (writes the XCD's dirty L2 lines back, so the other XCDs

@@ -112,6 +112,8 @@ struct moe_step {
   float* gate;
   float* dzsel;
   int* hist;
+  int* ready;
+  int nrb = 0;
   int* perm;
   int* inv;
   void* act;
@@ -251,6 +253,8 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const size_t o_shadow = cfg->dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
   const size_t o_xs = cfg->dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
   const size_t o_zero = take(256);
+  const int nrb = (int)((N + moe::gemm::BM - 1) / moe::gemm::BM) + E;   // row tiles of GEMM 1 (upper bound)
+  const size_t o_ready = take((size_t)nrb * 4);
   h->arena_bytes = off;
 
   he = hipMalloc(reinterpret_cast<void**>(&h->arena), h->arena_bytes);
@@ -265,6 +269,8 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   h->gate = reinterpret_cast<float*>(a + o_gate);
   h->dzsel = reinterpret_cast<float*>(a + o_dz);
   h->hist = reinterpret_cast<int*>(a + o_hist);
+  h->ready = reinterpret_cast<int*>(a + o_ready);
+  h->nrb = nrb;
   h->perm = reinterpret_cast<int*>(a + o_perm);
   h->inv = reinterpret_cast<int*>(a + o_inv);
   h->act = a + o_act;
@@ -318,7 +324,7 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   }
   if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK |
                     MOE_RUN_ZERO_GRAD_ROUTER | MOE_RUN_ZERO_GRAD_EXPERTS | MOE_RUN_APPLY_ROUTER |
-                    MOE_RUN_APPLY_EXPERTS)) {
+                    MOE_RUN_APPLY_EXPERTS | MOE_RUN_READY_GEMM12)) {
     set_err(h->err, "unknown run flags 0x%x", run_flags);
     return MOE_ERR_ARG;
   }
@@ -407,6 +413,8 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   p.gate = h->gate;
   p.dzsel = h->dzsel;
   p.hist = h->hist;
+  p.ready = h->ready;
+  p.nrb = h->nrb;
   p.perm = h->perm;
   p.inv = h->inv;
   p.act = h->act;

@@ -77,6 +77,8 @@ struct KParams {
   float* gate;     // [T*k]
   float* dzsel;    // [T*k] dL/dlogit of the selected experts
   int* hist;       // [G][E]
+  int* ready;      // [nrb] GEMM-1 column tiles done per 128-row tile (readiness mode)
+  int nrb;
   int* perm;       // [T*k] sorted position -> flat id
   int* inv;        // [T*k] flat id -> sorted position
   void* act;       // [N, f] gelu(H)            (T-typed)
@@ -432,6 +434,8 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   int* base = st + kThreads;                          // [EP]
   int* cw = base + kMaxExperts;                       // [kWaves][EP]
   int* posl = cw + kWaves * kMaxExperts;              // [kThreads] sorted positions of this block
+  if (p.flags & 0x10000u)   // readiness counters of this launch, zero before GEMM 1 starts
+    for (int i = lwg * kThreads + tid; i < p.nrb; i += G * kThreads) p.ready[i] = 0;
   {
     const int e = tid % EP, part = tid / EP;
     int pre = 0, tot = 0;
@@ -553,7 +557,7 @@ __device__ __forceinline__ const T* w2_ptr(const KParams& p) {
 // (bf16: read from the copy in xs).
 // ===========================================================================
 template <typename T, int NS>
-__device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Meta& meta) {
+__device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Meta& meta, bool publish) {
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f;
   const int NT = ceil_div(f, gemm::BN);
@@ -585,14 +589,24 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
       }
     };
     gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
+    if (publish) {
+      // every wave's stores of the tile have reached L2; one agent-scope
+      // release for the workgroup (the XCD's L2 is written back), then the count
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(p.ready + mg, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
 // ===========================================================================
 // P3: ragged_mm 2:  O = A_e W2[e]
 // ===========================================================================
+// With `wait` (readiness mode), a tile first waits until every GEMM-1 column
+// tile of its 128 rows is counted done, then acquires.  False if that wait
+// timed out (or another workgroup gave up).
 template <typename T, int NS>
-__device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Meta& meta) {
+__device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& meta, bool wait) {
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f;
   const int NT = ceil_div(d, gemm::BN);
@@ -600,6 +614,15 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
   const Span sp = xcd_span(ntiles);
   for (int tI = sp.begin; tI < sp.end; tI += sp.step) {
     const int mg = tI / NT, nt = tI % NT;
+    if (wait) {
+      if (threadIdx.x == 0) {
+        const bool ok = wait_count(p.ctrl, p.ready + mg, ceil_div(f, gemm::BN));
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        meta.flag = ok ? 1u : 0u;
+      }
+      __syncthreads();
+      if (meta.flag == 0u) return false;
+    }
     const int e = expert_of_tile(meta, p.E, mg);
     const int m0 = (mg - meta.moff[e]) * gemm::BM;
     const int p0 = meta.off[e] + m0;
@@ -617,6 +640,7 @@ __device__ __forceinline__ void phase_ffn2(const KParams& p, char* lds, const Me
       }
     });
   }
+  return true;
 }
 
 // ===========================================================================
@@ -1219,10 +1243,16 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   phase_order<T>(p, scratch, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
   MOE_SYNC(1);
   trace_mark(p, 2, 0);
-  if (!(skip & 4u)) phase_ffn1<T, NS>(p, scratch, meta);
-  MOE_SYNC(2);
+  const bool ready12 = (p.flags & 0x10000u) != 0u;
+  if (!(skip & 4u)) phase_ffn1<T, NS>(p, scratch, meta, ready12);
+  if (ready12) {   // readiness counters instead of a grid barrier
+    trace_mark(p, 2, 1);
+    trace_mark(p, 2, 2);
+  } else {
+    MOE_SYNC(2);
+  }
   trace_mark(p, 3, 0);
-  if (!(skip & 8u)) phase_ffn2<T, NS>(p, scratch, meta);
+  if (!(skip & 8u) && !phase_ffn2<T, NS>(p, scratch, meta, ready12 && !(skip & 4u))) return;
   MOE_SYNC(3);
   trace_mark(p, 4, 0);
   if (!(skip & 16u)) phase_combine<T>(p, meta);

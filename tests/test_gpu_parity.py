@@ -41,10 +41,10 @@ def _check_routing(cfg, inp, out, w_router):
                 f"rows per expert min {counts.min()} max {counts.max()}")
 
 
-def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0):
+def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, ready_gemm12=False):
     say(f"[gpu] {cfg.name} T={cfg.tokens}x{cfg.microbatches} d={cfg.d_model} f={cfg.d_ff} E={cfg.n_experts} "
         f"k={cfg.top_k} {cfg.dtype} clip={cfg.clip_norm if clip_norm is None else clip_norm}")
-    run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu)
+    run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu, ready_gemm12=ready_gemm12)
     try:
         params = inp.flat_params().astype(np.float64)
         m = np.zeros_like(params)
@@ -90,6 +90,16 @@ def test_ragged_shapes_bf16_two_workgroups_per_cu(T, d, f, E, k):
     # pipeline, half the LDS, router passes of 16 experts (E = 64 takes four)
     cfg = synth.small_config("ragged_bf16_occ2", T, d, f, E, k, "bf16")
     _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1, wg_per_cu=2)
+
+
+@pytest.mark.parametrize("wg_per_cu", [1, 2])
+def test_readiness_counters_between_expert_products(wg_per_cu):
+    # no grid barrier between GEMM 1 and GEMM 2: per-row-tile ready counters
+    # (both kernels; the fp32 path and a ragged bf16 shape with E = 64)
+    for cfg, seed, tol in ((synth.small_config("ready_f32", 333, 72, 136, 5, 2, "f32"), 3, F32_TOL),
+                           (synth.small_config("ready_bf16", 300, 128, 64, 64, 8, "bf16"), 4, BF16_TOL),
+                           (synth.CONFIGS["bf16_2x1024"], 0, BF16_TOL)):
+        _run_and_compare(cfg, synth.make_inputs(cfg, seed), tol, steps=1, wg_per_cu=wg_per_cu, ready_gemm12=True)
 
 
 def test_bf16_2x1024_two_steps():
