@@ -149,6 +149,9 @@ typedef struct {
  * writes the XCD's L2 back to memory, each acquire drops the L2's clean lines),
  * so it is off by default. */
 #define MOE_RUN_READY_GEMM12 0x10000u
+/* Launch through hipLaunchCooperativeKernel (the runtime guarantees that the
+ * whole grid is resident) instead of an ordinary launch. */
+#define MOE_RUN_COOPERATIVE 0x20000u
 
 /* Status-word bits reported by moe_step_status as MOE_ERR_DEVICE. */
 #define MOE_DEVICE_BARRIER_TIMEOUT 0x1u
@@ -170,7 +173,16 @@ int moe_step_check_config(const moe_step_config* cfg);
 int moe_step_create(const moe_step_config* cfg, moe_step_t* out);
 
 /* Enqueues one update on hip_stream (a hipStream_t; NULL = default stream):
- * one cooperative launch of the persistent kernel.  Asynchronous.
+ * one launch of the persistent kernel.  Asynchronous.
+ * The kernel needs all of its workgroups resident at once (grid barriers).  Its
+ * grid is sized at create to exactly what the device holds (occupancy x CUs),
+ * and by default it goes out as an ordinary launch: a cooperative launch costs
+ * about 19 us more per update on MI355X.  Launches of two handles on different
+ * streams of one device must then not overlap (order them with events); with
+ * MOE_RUN_COOPERATIVE the runtime guarantees co-residency instead.  If the
+ * grid cannot become resident (another kernel holds compute units for longer
+ * than the barrier's bound of about 2 s), the launch ends with
+ * MOE_DEVICE_BARRIER_TIMEOUT from moe_step_status; it never hangs.
  * n_tokens in [0, max_tokens]; tokens_in_update >= max(1, n_tokens) is the loss
  * denominator (the tokens of all microbatches of one update); step >= 1 is the
  * 1-based AdamW step, used only with MOE_RUN_APPLY.

@@ -7,7 +7,7 @@
 // depend on the exact values).  Prints one line per run with ms/update.
 //
 //   moe_step_bench [--config NAME] [--steps K] [--warmup W] [--skip MASK[,MASK...]] [--wg-per-cu N] [--ready]
-//                  [--copy-mib N]
+//                  [--coop] [--copy-mib N]
 //     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024
 //     --skip MASK: after the warm-up, time K launches that skip the phases in MASK
 //                  (bit i = phase i), for per-phase timing and counter collection;
@@ -105,7 +105,7 @@ int run_copy(int mib, int steps) {
 int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024";
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
-  bool ready = false;
+  bool ready = false, coop = false;
   std::vector<unsigned> skips{0u};
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -133,6 +133,7 @@ int main(int argc, char** argv) {
     else if (a == "--copy-mib") copy_mib = std::atoi(next());
     else if (a == "--wg-per-cu") wg_per_cu = std::atoi(next());
     else if (a == "--ready") ready = true;
+    else if (a == "--coop") coop = true;
     else {
       std::fprintf(stderr, "unknown argument %s\n", a.c_str());
       return 1;
@@ -222,7 +223,8 @@ int main(int argc, char** argv) {
   io.stats = stats;
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
-  const uint32_t base = MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | (ready ? MOE_RUN_READY_GEMM12 : 0u);
+  const uint32_t base =
+      MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | (ready ? MOE_RUN_READY_GEMM12 : 0u) | (coop ? MOE_RUN_COOPERATIVE : 0u);
   int64_t step = 1;
   for (int i = 0; i < warmup; ++i, ++step) {
     if (moe_step_run(h, &io, sh->T, sh->T, step, base | (i == 0 ? MOE_RUN_REFRESH_SHADOW : 0u), stream) != MOE_OK) {

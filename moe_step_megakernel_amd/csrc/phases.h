@@ -936,7 +936,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       const int mt = rem / NT11, nt = rem % NT11;
       const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
       const int pe = meta.off[e], ce = meta.cnt[e];
-      // bf16: the token rows gathered by GEMM 1; fp32: x through perm
+      // bf16: the token rows gathered in route_order; fp32: x through perm
       const gemm::Operand A = (sizeof(T) == 2)
           ? gemm::Operand{reinterpret_cast<const char*>(p.xs), d, nullptr, 1, pe, ce, d, m0}
           : gemm::Operand{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, pe, ce, d, m0};

@@ -32,13 +32,15 @@ class MoeLayerStep:
         self._shadow_valid = False
 
     def run(self, x, target, *, tokens_in_update=None, step=1, zero_grad=True, apply=True, dx=None,
-            router_bias=None, debug=None, trace=None, stream=None, groups=None, ready_gemm12=False):
+            router_bias=None, debug=None, trace=None, stream=None, groups=None, ready_gemm12=False,
+            cooperative=False):
         """Enqueues one launch.  ``debug`` is an optional dict of preallocated debug tensors
         (router_logits, topk_idx, topk_gate, expert_counts, route_perm).  ``groups`` (selective
         updates) replaces zero_grad/apply/step by per-group settings: a dict with keys
         zero_router, zero_experts, apply_router, apply_experts (bools) and step_router,
         step_experts (ints).  ``ready_gemm12`` replaces the grid barrier between the two
-        expert products by per-row-tile readiness counters (same results)."""
+        expert products by per-row-tile readiness counters (same results).  ``cooperative``
+        launches through hipLaunchCooperativeKernel instead of an ordinary launch."""
         n = 0 if x is None else int(x.shape[0])
         flags = 0
         step_r = step_e = step
@@ -59,6 +61,8 @@ class MoeLayerStep:
             flags |= B.MOE_RUN_TRACE
         if ready_gemm12:
             flags |= B.MOE_RUN_READY_GEMM12
+        if cooperative:
+            flags |= B.MOE_RUN_COOPERATIVE
         dbg = debug or {}
         io = B.make_io(x=x, target=target, router_bias=router_bias, params=self.params, grads=self.grads,
                        exp_avg=self.exp_avg, exp_avg_sq=self.exp_avg_sq, dx=dx, stats=self.stats,

@@ -42,9 +42,10 @@ class GpuRun:
     """One layer on cuda:0 with the inputs of ``inp`` (all microbatches)."""
 
     def __init__(self, cfg: synth.LayerConfig, inp: synth.LayerInputs, *, clip_norm=None, wg_per_cu=0,
-                 ready_gemm12=False):
+                 ready_gemm12=False, cooperative=False):
         self.cfg, self.inp = cfg, inp
         self.ready_gemm12 = ready_gemm12
+        self.cooperative = cooperative
         self.dev = torch.device("cuda", 0)
         self.layer = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, max(1, cfg.tokens), cfg.dtype,
                                   lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.eps,
@@ -77,7 +78,7 @@ class GpuRun:
             dx = torch.empty(T, d, dtype=torch.float32, device=self.dev) if want_dx else None
             self.layer.run(x, t, tokens_in_update=cfg.tokens_in_update, step=step, zero_grad=(mb == 0),
                            apply=(mb == cfg.microbatches - 1), dx=dx, router_bias=self.bias, debug=dbg,
-                           ready_gemm12=self.ready_gemm12)
+                           ready_gemm12=self.ready_gemm12, cooperative=self.cooperative)
             self.layer.status()
             if debug:
                 outs["logits"].append(dbg["router_logits"].cpu().numpy())

@@ -41,10 +41,11 @@ def _check_routing(cfg, inp, out, w_router):
                 f"rows per expert min {counts.min()} max {counts.max()}")
 
 
-def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, ready_gemm12=False):
+def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, ready_gemm12=False, cooperative=False):
     say(f"[gpu] {cfg.name} T={cfg.tokens}x{cfg.microbatches} d={cfg.d_model} f={cfg.d_ff} E={cfg.n_experts} "
         f"k={cfg.top_k} {cfg.dtype} clip={cfg.clip_norm if clip_norm is None else clip_norm}")
-    run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu, ready_gemm12=ready_gemm12)
+    run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu, ready_gemm12=ready_gemm12,
+                 cooperative=cooperative)
     try:
         params = inp.flat_params().astype(np.float64)
         m = np.zeros_like(params)
@@ -100,6 +101,13 @@ def test_readiness_counters_between_expert_products(wg_per_cu):
                            (synth.small_config("ready_bf16", 300, 128, 64, 64, 8, "bf16"), 4, BF16_TOL),
                            (synth.CONFIGS["bf16_2x1024"], 0, BF16_TOL)):
         _run_and_compare(cfg, synth.make_inputs(cfg, seed), tol, steps=1, wg_per_cu=wg_per_cu, ready_gemm12=True)
+
+
+@pytest.mark.parametrize("wg_per_cu", [1, 2])
+def test_cooperative_launch(wg_per_cu):
+    # the same kernel through hipLaunchCooperativeKernel
+    for cfg, seed, tol in ((synth.CONFIGS["tiny_f32"], 0, F32_TOL), (synth.CONFIGS["bf16_2x1024"], 0, BF16_TOL)):
+        _run_and_compare(cfg, synth.make_inputs(cfg, seed), tol, steps=1, wg_per_cu=wg_per_cu, cooperative=True)
 
 
 def test_bf16_2x1024_two_steps():
