@@ -361,6 +361,7 @@ def main(argv=None):
         print("# timing the FP64 oracle on the host ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, inp, args.cpu_budget)
 
+    arena_bytes = layer.arena_bytes()
     layer.close()
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -374,7 +375,7 @@ def main(argv=None):
         "ms_per_update_median": float(np.median(upd_ms)), "ms_per_update_p10": float(np.percentile(upd_ms, 10)),
         "ms_per_update_p90": float(np.percentile(upd_ms, 90)),
         "ms_per_update_fresh_median": float(np.median(fresh_ms)),
-        "roofline": roofline, "cpu_baseline": cpu, "phases": phases,
+        "roofline": roofline, "cpu_baseline": cpu, "phases": phases, "arena_bytes": arena_bytes,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -132,8 +132,10 @@ typedef struct {
 #define MOE_RUN_APPLY_EXPERTS 0x80u      /* clip + AdamW on W1 | W2                  */
 /* Profiling aid: skip phase i (0..7) of the persistent kernel and reuse what the
  * previous launch on this handle left in the arena.  Accepted only when the
- * previous launch ran every phase with the same n_tokens (else MOE_ERR_STATE);
- * results are then those of the previous launch for the skipped phases.  Phase
+ * previous launch ran every phase with the same n_tokens (else MOE_ERR_STATE).
+ * Only the timing is meaningful: a skipped phase's output comes from the
+ * previous launch, but buffers shared between phases of disjoint lifetimes
+ * may by then hold a later phase's data (all values finite).  Phase
  * order: 0 routing, 1 route_order, 2 expert GEMM 1, 3 expert GEMM 2,
  * 4 combine/loss, 5 dH + dW2 + router partials, 6 dW1 + dX + router gradient,
  * 7 dx sum + norm + clip/AdamW. */
@@ -211,6 +213,12 @@ size_t moe_step_trace_words(moe_step_t h);
 
 /* Persistent workgroups of the handle's launches. */
 int moe_step_grid_size(moe_step_t h);
+
+/* Bytes of device memory the handle holds (its arena; 0 for NULL).  Stored
+ * activations whose lifetimes do not overlap share memory (the expert outputs
+ * O with dH, the activations A with the per-slot input gradients), the
+ * memory rule of the pages' "Open problems", Generality 2. */
+size_t moe_step_arena_bytes(moe_step_t h);
 
 /* Text of the last error on h (or of the last failed create if h is NULL).
  * Valid until the next call on the same handle. Never NULL. */

@@ -85,6 +85,8 @@ def load_library():
     lib.moe_step_trace_words.restype = ctypes.c_size_t
     lib.moe_step_grid_size.argtypes = [ctypes.c_void_p]
     lib.moe_step_grid_size.restype = ctypes.c_int
+    lib.moe_step_arena_bytes.argtypes = [ctypes.c_void_p]
+    lib.moe_step_arena_bytes.restype = ctypes.c_size_t
     lib.moe_step_last_error.argtypes = [ctypes.c_void_p]
     lib.moe_step_last_error.restype = ctypes.c_char_p
     lib.moe_step_destroy.argtypes = [ctypes.c_void_p]
@@ -151,6 +153,10 @@ def moe_step_trace_words(handle) -> int:
 
 def moe_step_grid_size(handle) -> int:
     return int(load_library().moe_step_grid_size(handle))
+
+
+def moe_step_arena_bytes(handle) -> int:
+    return int(load_library().moe_step_arena_bytes(handle))
 
 
 def moe_step_destroy(handle) -> None:

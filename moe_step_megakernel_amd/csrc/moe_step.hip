@@ -3,6 +3,7 @@
 // default, cooperative on request).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -149,6 +150,8 @@ const char* moe_step_last_error(moe_step_t h) { return h ? h->err : g_create_err
 
 int moe_step_grid_size(moe_step_t h) { return h ? h->grid : 0; }
 
+size_t moe_step_arena_bytes(moe_step_t h) { return h ? h->arena_bytes : 0; }
+
 size_t moe_step_trace_words(moe_step_t h) { return h ? (size_t)h->grid * moe::kPhases * 3 : 0; }
 
 int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
@@ -244,9 +247,15 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const size_t o_idx = take(N * 4), o_gate = take(N * 4), o_dz = take(N * 4);
   const size_t o_hist = take((size_t)h->grid * E * 4);
   const size_t o_perm = take(N * 4), o_inv = take(N * 4);
-  const size_t o_act = take(N * f * es), o_gp = take(N * f * es);
-  const size_t o_out = take(N * d * 4), o_dout = take(N * d * es), o_dh = take(N * f * es);
-  const size_t o_dxs = take(N * d * es);
+  // Stored activations share memory where their lifetimes (phases between the
+  // grid barriers) do not overlap:
+  //   O  [N, d] fp32: written by GEMM 2, last read by the combine;
+  //   dH [N, f]:      written by the dH tiles after the combine's barrier;
+  //   A  [N, f]:      written by GEMM 1, last read by the dW2 tiles;
+  //   dXs [N, d]:     written by the dX tiles after that phase's barrier.
+  const size_t o_out_dh = take(std::max(N * d * 4, N * f * es));
+  const size_t o_act_dxs = take(std::max(N * f * es, N * d * es));
+  const size_t o_gp = take(N * f * es), o_dout = take(N * d * es);
   const size_t o_wrt = take((size_t)E * d * 4);
   const size_t o_rpart = take(rch * E * d * 4);
   const size_t o_loss = take((size_t)h->grid * 4);
@@ -274,12 +283,12 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   h->nrb = nrb;
   h->perm = reinterpret_cast<int*>(a + o_perm);
   h->inv = reinterpret_cast<int*>(a + o_inv);
-  h->act = a + o_act;
+  h->act = a + o_act_dxs;
   h->gp = a + o_gp;
-  h->out = reinterpret_cast<float*>(a + o_out);
+  h->out = reinterpret_cast<float*>(a + o_out_dh);
   h->dout = a + o_dout;
-  h->dh = a + o_dh;
-  h->dxs = a + o_dxs;
+  h->dh = a + o_out_dh;
+  h->dxs = a + o_act_dxs;
   h->wrt = reinterpret_cast<float*>(a + o_wrt);
   h->rpart = reinterpret_cast<float*>(a + o_rpart);
   h->loss_part = reinterpret_cast<float*>(a + o_loss);

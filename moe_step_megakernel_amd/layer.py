@@ -80,6 +80,9 @@ class MoeLayerStep:
     def trace_words(self):
         return B.moe_step_trace_words(self.handle)
 
+    def arena_bytes(self):
+        return B.moe_step_arena_bytes(self.handle)
+
     def close(self):
         if self.handle:
             B.moe_step_destroy(self.handle)

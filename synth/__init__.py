@@ -76,9 +76,10 @@ CONFIGS = {
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even); return uint16 bit patterns."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounding = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + rounding) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (at most
+    # 0xFF800000 + 0x8000); NaNs are replaced below
+    out = ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = 0x7FC0

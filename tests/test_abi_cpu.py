@@ -84,5 +84,6 @@ def test_null_handle_calls_are_safe():
     assert lib.moe_step_status(None) == B.MOE_ERR_ARG
     assert lib.moe_step_trace_words(None) == 0
     assert lib.moe_step_grid_size(None) == 0
+    assert lib.moe_step_arena_bytes(None) == 0
     lib.moe_step_destroy(None)
     assert isinstance(B.moe_step_last_error(None), str)
