@@ -42,6 +42,8 @@ struct Meta {
   int cnt[kMaxExperts];         // routed rows per expert
   int off[kMaxExperts + 1];     // first sorted position of each expert
   int moff[kMaxExperts + 1];    // first 128-row tile of each expert
+  int ord[kMaxExperts];         // experts by descending row count (ties: lower index first)
+  int skewed;                   // some expert holds more than twice the mean rows
   float red[8];                 // block reductions
   unsigned flag;                // barrier result broadcast
 };
@@ -134,6 +136,42 @@ __device__ __forceinline__ Span xcd_span_last(int n) {
   const int lo = min(n, x * chunk);
   const int hi = min(n, lo + chunk);
   return {lo + j, hi, per};
+}
+
+// Weight-gradient tiles of all experts (tpe per expert, expert-major index).
+// Their contraction runs over the expert's rows, so under skewed routing the
+// tiles of a heavy expert cost many times those of a light one.  Balanced
+// routing keeps the XCD-contiguous deal of xcd_span (an expert's operands stay
+// in one XCD's L2).  Skewed routing takes the tiles in order of descending
+// expert row count and deals them over all workgroups in a snake (0..G-1,
+// G-1..0, ...), so every workgroup gets about the same sum of contraction
+// lengths.
+struct DealW {
+  Span sp;
+  bool snake;
+  int G, w, tpe, n;
+  __device__ __forceinline__ int count() const {
+    if (!snake) return max(0, ceil_div(sp.end - sp.begin, sp.step));
+    const int full = n / G, rem = n % G;   // rounds of G tiles, then a partial round
+    const int last = (full & 1) ? G - 1 - w : w;
+    return full + (last < rem ? 1 : 0);
+  }
+  // this workgroup's t-th tile (expert-major index)
+  __device__ __forceinline__ int item(const Meta& meta, int t) const {
+    if (!snake) return sp.begin + t * sp.step;
+    const int q = t * G + ((t & 1) ? G - 1 - w : w);
+    return meta.ord[q / tpe] * tpe + q % tpe;
+  }
+};
+__device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int n, int tpe) {
+  DealW dl;
+  dl.snake = meta.skewed != 0;
+  dl.sp = xcd_span(n);
+  dl.G = gridDim.x;
+  dl.w = blockIdx.x;
+  dl.tpe = tpe;
+  dl.n = n;
+  return dl;
 }
 
 __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot) {
@@ -481,6 +519,19 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     meta.moff[E] = mo;
   }
   __syncthreads();
+  if (tid < E) {
+    // rank of this expert by row count, for dealing the weight-gradient tiles
+    const int c = meta.cnt[tid];
+    int r = 0;
+    for (int e = 0; e < E; ++e) r += (meta.cnt[e] > c) || (meta.cnt[e] == c && e < tid);
+    meta.ord[r] = tid;
+  }
+  if (tid == 0) {
+    int mx = 0;
+    for (int e = 0; e < E; ++e) mx = max(mx, meta.cnt[e]);
+    meta.skewed = (long)mx * E > 2L * meta.off[E];
+  }
+  __syncthreads();
   if (tid < E) base[tid] = meta.off[tid] + sp[tid];
   if (lwg == 0 && tid < E && p.dbg_counts) p.dbg_counts[tid] = meta.cnt[tid];
   if (skip_scatter) return;
@@ -790,12 +841,13 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 
   // each kind of work is dealt over the XCDs on its own, so every XCD gets the
   // same mix (the kinds differ a lot in cost)
-  const Span s10 = xcd_span(n10), s9 = xcd_span(n9), sr = xcd_span_last(nr);
-  const int c10 = max(0, ceil_div(s10.end - s10.begin, s10.step));
+  const DealW d10 = deal_weight_tiles(meta, n10, MT10 * NT10);
+  const Span s9 = xcd_span(n9), sr = xcd_span_last(nr);
+  const int c10 = d10.count();
   const int c9 = max(0, ceil_div(s9.end - s9.begin, s9.step));
   const int cr = max(0, ceil_div(sr.end - sr.begin, sr.step));
   for (int q = 0; q < c10 + c9 + cr; ++q) {
-    const int item = q < c10 ? s10.begin + q * s10.step
+    const int item = q < c10 ? d10.item(meta, q)
                    : q < c10 + c9 ? n10 + s9.begin + (q - c10) * s9.step
                                   : n10 + n9 + sr.begin + (q - c10 - c9) * sr.step;
     if (item < n10) {
@@ -922,12 +974,13 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
-  const Span s11 = xcd_span(n11), s12 = xcd_span(n12), srr = xcd_span_last(nrr);
-  const int c11 = max(0, ceil_div(s11.end - s11.begin, s11.step));
+  const DealW d11 = deal_weight_tiles(meta, n11, MT11 * NT11);
+  const Span s12 = xcd_span(n12), srr = xcd_span_last(nrr);
+  const int c11 = d11.count();
   const int c12 = max(0, ceil_div(s12.end - s12.begin, s12.step));
   const int crr = max(0, ceil_div(srr.end - srr.begin, srr.step));
   for (int q = 0; q < c11 + c12 + crr; ++q) {
-    const int item = q < c11 ? s11.begin + q * s11.step
+    const int item = q < c11 ? d11.item(meta, q)
                    : q < c11 + c12 ? n11 + s12.begin + (q - c11) * s12.step
                                    : n11 + n12 + srr.begin + (q - c11 - c12) * srr.step;
     if (item < n11) {
