@@ -1040,15 +1040,29 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
           [&](int r, int c) { return (r < mrows && n0 + c < d) ? p.perm[p0 + r] : 0; });
     } else {
       // dW_r[c][e] = sum over token chunks (ascending) of the partials
+      // one (expert, column) pair per thread, columns consecutive across the
+      // threads so every chunk's partials are read in 1 KB pieces; the chunk
+      // partials are added in ascending chunk order, eight loads in flight
       const int ir = item - n11 - n12;
       const int o = ir * kThreads + tid;
       float sq = 0.f;
       if (o < d * E) {
-        const int c = o / E, e = o % E;
+        const int e = o / d, c = o % d;
+        const float* src = p.rpart + (long)e * d + c;
+        const long stride = (long)E * d;
         float s = 0.f;
-        for (int r = 0; r < RCH; ++r) s += p.rpart[((long)r * E + e) * d + c];
-        const float nv = zero_router ? s : p.grads[o] + s;
-        p.grads[o] = nv;
+        int r = 0;
+        for (; r + 8 <= RCH; r += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = src[(r + u) * stride];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; r < RCH; ++r) s += src[r * stride];
+        const int gi = c * E + e;   // W_r is [d, E]
+        const float nv = zero_router ? s : p.grads[gi] + s;
+        p.grads[gi] = nv;
         sq = nv * nv;
       }
       const float s = block_sum(sq, meta.red);
