@@ -1157,7 +1157,7 @@ __device__ __forceinline__ void dx_tokens(const KParams& p) {
   }
 }
 
-template <typename T>
+template <typename T, int OCC>
 __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& meta, bool restart_loss, bool apply_r,
                                             bool apply_e, bool want_dx) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1252,7 +1252,9 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
       reinterpret_cast<uint2*>(p.shadow)[i - nr4] = s;
     }
   };
-  constexpr int U = 4;
+  // loads in flight per thread: four of each array with a SIMD's full register
+  // file, two with half of it (twice the workgroups keep as many in flight)
+  constexpr int U = OCC == 1 ? 4 : 2;
   const long stride = (long)G * kThreads;
   long i = lo4 + (long)lwg * kThreads + tid;
   for (; i + (U - 1) * stride < hi4; i += U * stride) {
@@ -1331,7 +1333,7 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   if (!(skip & 64u)) phase_bwd1<T, NS>(p, scratch, meta, zero_r, zero_e, want_dx);
   MOE_SYNC(6);
   trace_mark(p, 7, 0);
-  if (!(skip & 128u)) phase_final<T>(p, scratch, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
+  if (!(skip & 128u)) phase_final<T, OCC>(p, scratch, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
   __syncthreads();
   trace_mark(p, 7, 1);
   trace_mark(p, 7, 2);
