@@ -130,6 +130,8 @@ struct moe_step {
   float* norm_part;
   uint16_t* shadow;
   void* xs;
+  float* wpart2;
+  float* wpart1;
   char* zero;
   unsigned* ctrl;
 };
@@ -263,6 +265,11 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const size_t o_shadow = cfg->dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
   const size_t o_xs = cfg->dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
   const size_t o_zero = take(256);
+  // partial weight-gradient tiles of split contractions (skewed routing): at most
+  // E/2 extra chunks over all experts, each a 128 x 128 fp32 tile per gradient tile
+  const size_t wtiles = (size_t)cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
+  const size_t o_wpart2 = take(((size_t)E / 2 + 1) * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
+  const size_t o_wpart1 = take(((size_t)E / 2 + 1) * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
   const int nrb = (int)((N + moe::gemm::BM - 1) / moe::gemm::BM) + E;   // row tiles of GEMM 1 (upper bound)
   const size_t o_ready = take((size_t)nrb * 4);
   h->arena_bytes = off;
@@ -295,6 +302,8 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   h->norm_part = reinterpret_cast<float*>(a + o_norm);
   h->shadow = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a + o_shadow) : nullptr;
   h->xs = cfg->dtype == MOE_DTYPE_BF16 ? a + o_xs : nullptr;
+  h->wpart2 = reinterpret_cast<float*>(a + o_wpart2);
+  h->wpart1 = reinterpret_cast<float*>(a + o_wpart1);
   h->zero = a + o_zero;
 
   // the arena starts zeroed (every stored index is then in range) and so do
@@ -439,6 +448,8 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   p.norm_part = h->norm_part;
   p.shadow = h->shadow;
   p.xs = h->xs;
+  p.wpart2 = h->wpart2;
+  p.wpart1 = h->wpart1;
   p.zero = h->zero;
   p.ctrl.gen = h->ctrl;
   p.ctrl.status = h->ctrl + 32;

@@ -23,7 +23,7 @@
 namespace moe {
 
 constexpr int kPhases = 8;
-constexpr int kMetaBytes = 2048;
+constexpr int kMetaBytes = 2560;
 // OCC workgroups per compute unit: the kernel is built for one (all of a
 // SIMD's registers per wave, 4-stage GEMM pipeline) or two (at most 256
 // registers per wave, 2-stage pipeline, half the LDS each).
@@ -44,6 +44,14 @@ struct Meta {
   int moff[kMaxExperts + 1];    // first 128-row tile of each expert
   int ord[kMaxExperts];         // experts by descending row count (ties: lower index first)
   int skewed;                   // some expert holds more than twice the mean rows
+  // skewed routing: an expert's weight-gradient contraction is split into
+  // chunks of kc rows (a multiple of 64, about twice the mean rows per expert)
+  int kc;
+  int nch[kMaxExperts];         // chunks of each expert (1 unless skewed)
+  int pbase[kMaxExperts];       // first partial-tile block of each expert (sum of nch - 1 before it)
+  int cpre[kMaxExperts + 1];    // chunks of the experts before rank r, in ord order
+  int nsplit;                   // experts with more than one chunk
+  int splitlist[kMaxExperts];   // those experts, ascending
   float red[8];                 // block reductions
   unsigned flag;                // barrier result broadcast
 };
@@ -94,6 +102,8 @@ struct KParams {
   float* loss_part;  // [G]
   float* norm_part;  // [n10 + n11 + nr]
   uint16_t* shadow;  // [2*E*d*f] bf16 copy of W1 | W2 (bf16 mode)
+  float* wpart2;     // partial dW2 tiles of split contractions [blocks][tiles per expert][128 x 128]
+  float* wpart1;     // the same for dW1
   void* xs;          // [N, d] token rows in expert order (bf16 mode), written by route_order
   const char* zero;  // 256 zero bytes (source of out-of-range tile elements)
   Ctrl ctrl;
@@ -138,40 +148,75 @@ __device__ __forceinline__ Span xcd_span_last(int n) {
   return {lo + j, hi, per};
 }
 
-// Weight-gradient tiles of all experts (tpe per expert, expert-major index).
-// Their contraction runs over the expert's rows, so under skewed routing the
-// tiles of a heavy expert cost many times those of a light one.  Balanced
-// routing keeps the XCD-contiguous deal of xcd_span (an expert's operands stay
-// in one XCD's L2).  Skewed routing takes the tiles in order of descending
-// expert row count and deals them over all workgroups in a snake (0..G-1,
-// G-1..0, ...), so every workgroup gets about the same sum of contraction
-// lengths.
+// Weight-gradient tiles of all experts (tpe per expert).  Their contraction
+// runs over the expert's rows, so under skewed routing the tiles of a heavy
+// expert cost many times those of a light one.  Balanced routing keeps the
+// XCD-contiguous deal of xcd_span (an expert's operands stay in one XCD's L2),
+// one item per tile.  Skewed routing splits each expert's contraction into
+// chunks of kc rows (item = expert, chunk, tile), takes the items in order of
+// descending expert row count and deals them over all workgroups in a snake
+// (0..G-1, G-1..0, ...), so every workgroup gets about the same sum of
+// contraction lengths.
+struct WItem {
+  int e, c, t;   // expert, chunk, tile within the expert
+};
 struct DealW {
   Span sp;
   bool snake;
   int G, w, tpe, n;
   __device__ __forceinline__ int count() const {
     if (!snake) return max(0, ceil_div(sp.end - sp.begin, sp.step));
-    const int full = n / G, rem = n % G;   // rounds of G tiles, then a partial round
+    const int full = n / G, rem = n % G;   // rounds of G items, then a partial round
     const int last = (full & 1) ? G - 1 - w : w;
     return full + (last < rem ? 1 : 0);
   }
-  // this workgroup's t-th tile (expert-major index)
-  __device__ __forceinline__ int item(const Meta& meta, int t) const {
-    if (!snake) return sp.begin + t * sp.step;
-    const int q = t * G + ((t & 1) ? G - 1 - w : w);
-    return meta.ord[q / tpe] * tpe + q % tpe;
+  // this workgroup's i-th item
+  __device__ __forceinline__ WItem item(const Meta& meta, int E, int i) const {
+    if (!snake) {
+      const int q = sp.begin + i * sp.step;
+      return {q / tpe, 0, q % tpe};
+    }
+    const int q = i * G + ((i & 1) ? G - 1 - w : w);
+    int r = 0;
+    while (r + 1 < E && meta.cpre[r + 1] * tpe <= q) ++r;
+    const int rem = q - meta.cpre[r] * tpe;
+    return {meta.ord[r], rem / tpe, rem % tpe};
   }
 };
-__device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int n, int tpe) {
+__device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int E, int tpe) {
   DealW dl;
   dl.snake = meta.skewed != 0;
-  dl.sp = xcd_span(n);
   dl.G = gridDim.x;
   dl.w = blockIdx.x;
   dl.tpe = tpe;
-  dl.n = n;
+  dl.n = tpe * (dl.snake ? meta.cpre[E] : E);
+  dl.sp = xcd_span(dl.n);
   return dl;
+}
+
+// Completes the weight-gradient tiles whose contraction was split: grads of
+// tile t of expert e (an m x n block of a [M, N] gradient at g) += the
+// partial tiles of chunks 1.. in chunk order; returns this thread's share of
+// the tile's sum of squares.  part holds 128 x 128 fp32 tiles, row-major.
+__device__ __forceinline__ float fix_split_tile(const Meta& meta, float* g, const float* part, int e, int t, int M,
+                                                int N, int NT) {
+  const int mt = t / NT, nt = t % NT, m0 = mt * gemm::BM, n0 = nt * gemm::BN, S = meta.nch[e];
+  const int tpe = ceil_div(M, gemm::BM) * NT;
+  float sq = 0.f;
+  for (int idx = threadIdx.x; idx < gemm::BM * gemm::BN / 4; idx += kThreads) {
+    const int r = idx / (gemm::BN / 4), c = (idx % (gemm::BN / 4)) * 4;
+    if (m0 + r >= M || n0 + c >= N) continue;
+    float4* gp = reinterpret_cast<float4*>(g + (long)(m0 + r) * N + n0 + c);
+    float4 v = *gp;
+    for (int ch = 1; ch < S; ++ch) {
+      const float4 u = *reinterpret_cast<const float4*>(
+          part + ((long)(meta.pbase[e] + ch - 1) * tpe + t) * (gemm::BM * gemm::BN) + r * gemm::BN + c);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    *gp = v;
+    sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  return sq;
 }
 
 __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot) {
@@ -530,6 +575,26 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     int mx = 0;
     for (int e = 0; e < E; ++e) mx = max(mx, meta.cnt[e]);
     meta.skewed = (long)mx * E > 2L * meta.off[E];
+    const int kc = 64 * max(1, ceil_div(ceil_div(2 * meta.off[E], max(E, 1)), 64));
+    meta.kc = kc;
+    int pb = 0, ns = 0;
+    for (int e = 0; e < E; ++e) {
+      const int n = meta.skewed ? max(1, ceil_div(meta.cnt[e], kc)) : 1;
+      meta.nch[e] = n;
+      meta.pbase[e] = pb;
+      pb += n - 1;
+      if (n > 1) meta.splitlist[ns++] = e;
+    }
+    meta.nsplit = ns;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int r = 0; r < E; ++r) {
+      meta.cpre[r] = s;
+      s += meta.nch[meta.ord[r]];
+    }
+    meta.cpre[E] = s;
   }
   __syncthreads();
   if (tid < E) base[tid] = meta.off[tid] + sp[tid];
@@ -823,6 +888,55 @@ __device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
 // ===========================================================================
 // P5: dH = (dO W2[e]^T) * G' ; dW2[e] = A_e^T dO ; router-gradient partials
 // ===========================================================================
+// One weight-gradient tile: g[m0.., n0..] (an [M, N] block, ld N) = A^T B
+// over chunk wi.c of expert wi.e's rows, where A = rows of width M (in expert
+// order, or through amap[p] / adiv) and B = rows of width N in expert order.  An unsplit tile writes (or adds to) the
+// gradient and its sum of squares into norm_part[nidx]; chunk 0 of a split
+// tile writes or adds likewise but leaves the sum of squares to the fix-up;
+// chunks 1.. write their partial tile into part.
+template <typename T, int NS>
+__device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Meta& meta, const WItem& wi,
+                                                 const char* abase, const int* amap, int adiv, int M,
+                                                 const char* bbase, int N, int m0, int n0, float* g, float* part,
+                                                 int tpe, bool zero, int nidx) {
+  const int e = wi.e, S = meta.nch[e], kc = meta.kc;
+  const int r0 = S > 1 ? wi.c * kc : 0;
+  const int rows = S > 1 ? min(kc, meta.cnt[e] - r0) : meta.cnt[e];
+  const int pe = meta.off[e] + r0;
+  gemm::Operand A{abase, M, amap, adiv, pe, rows, M, m0};
+  gemm::Operand B{bbase, N, nullptr, 1, pe, rows, N, n0};
+  if (wi.c > 0) {
+    float* pt = part + ((long)(meta.pbase[e] + wi.c - 1) * tpe + wi.t) * (gemm::BM * gemm::BN);
+    gemm::tile<T, NS, true, true>(lds, A, B, rows, p.zero, [&](int r, int c, const float (&v)[8]) {
+      F8 o;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o.v[u] = v[u];
+      st8(pt + r * gemm::BN + c, o);
+    });
+    return;
+  }
+  float sq = 0.f;
+  gemm::tile<T, NS, true, true>(
+      lds, A, B, rows, p.zero,
+      [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
+        if (m0 + r < M && n0 + c < N) {
+          F8 nv = cvt8(old);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) nv.v[u] = zero ? v[u] : nv.v[u] + v[u];
+          st8(g + (long)(m0 + r) * N + n0 + c, nv);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
+        }
+      },
+      [&](int r, int c) {
+        Raw8<float> old{};
+        if (!zero && m0 + r < M && n0 + c < N) old = ldr8(g + (long)(m0 + r) * N + n0 + c);
+        return old;
+      });
+  const float s = block_sum(sq, meta.red);
+  if (S == 1 && threadIdx.x == 0) p.norm_part[nidx] = s;
+}
+
 template <typename T, int NS>
 __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_experts) {
   const int tid = threadIdx.x;
@@ -841,45 +955,25 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 
   // each kind of work is dealt over the XCDs on its own, so every XCD gets the
   // same mix (the kinds differ a lot in cost)
-  const DealW d10 = deal_weight_tiles(meta, n10, MT10 * NT10);
+  const DealW d10 = deal_weight_tiles(meta, E, MT10 * NT10);
   const Span s9 = xcd_span(n9), sr = xcd_span_last(nr);
   const int c10 = d10.count();
   const int c9 = max(0, ceil_div(s9.end - s9.begin, s9.step));
   const int cr = max(0, ceil_div(sr.end - sr.begin, sr.step));
   for (int q = 0; q < c10 + c9 + cr; ++q) {
-    const int item = q < c10 ? d10.item(meta, q)
-                   : q < c10 + c9 ? n10 + s9.begin + (q - c10) * s9.step
-                                  : n10 + n9 + sr.begin + (q - c10 - c9) * sr.step;
-    if (item < n10) {
-      // dW2[e] (f x d) = A_e^T dO_e, contraction over the expert's rows
-      const int e = item / (MT10 * NT10), rem = item % (MT10 * NT10);
-      const int mt = rem / NT10, nt = rem % NT10;
+    if (q < c10) {
+      // dW2[e] (f x d) = A_e^T dO_e, contraction over the expert's rows (chunk c of them)
+      const WItem wi = d10.item(meta, E, q);
+      const int e = wi.e, mt = wi.t / NT10, nt = wi.t % NT10;
       const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
-      const int pe = meta.off[e], ce = meta.cnt[e];
-      gemm::Operand A{reinterpret_cast<const char*>(p.act), f, nullptr, 1, pe, ce, f, m0};
-      gemm::Operand B{reinterpret_cast<const char*>(p.dout), d, nullptr, 1, pe, ce, d, n0};
-      float* g = gw2 + (long)e * f * d;
-      float sq = 0.f;
-      gemm::tile<T, NS, true, true>(
-          lds, A, B, ce, p.zero,
-          [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
-            if (m0 + r < f && n0 + c < d) {
-              F8 nv = cvt8(old);
-#pragma unroll
-              for (int u = 0; u < 8; ++u) nv.v[u] = zero_experts ? v[u] : nv.v[u] + v[u];
-              st8(g + (long)(m0 + r) * d + n0 + c, nv);
-#pragma unroll
-              for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
-            }
-          },
-          [&](int r, int c) {
-            Raw8<float> old{};
-            if (!zero_experts && m0 + r < f && n0 + c < d) old = ldr8(g + (long)(m0 + r) * d + n0 + c);
-            return old;
-          });
-      const float s = block_sum(sq, meta.red);
-      if (tid == 0) p.norm_part[item] = s;
-    } else if (item < n10 + n9) {
+      weight_grad_tile<T, NS>(p, lds, meta, wi, reinterpret_cast<const char*>(p.act), nullptr, 1, f,
+                              reinterpret_cast<const char*>(p.dout), d, m0, n0, gw2 + (long)e * f * d, p.wpart2,
+                              MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
+      continue;
+    }
+    const int item = q < c10 + c9 ? n10 + s9.begin + (q - c10) * s9.step
+                                  : n10 + n9 + sr.begin + (q - c10 - c9) * sr.step;
+    if (item < n10 + n9) {
       const int tI = item - n10;
       const int mg = tI / NTf, nt = tI % NTf;
       const int e = expert_of_tile(meta, E, mg);
@@ -960,7 +1054,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 // ===========================================================================
 template <typename T, int NS>
 __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& meta, bool zero_router, bool zero_experts,
-                                           bool want_dx) {
+                                           bool want_dx, bool fix_dw2) {
   const int tid = threadIdx.x;
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E;
@@ -974,48 +1068,42 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
-  const DealW d11 = deal_weight_tiles(meta, n11, MT11 * NT11);
+  const DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11);
   const Span s12 = xcd_span(n12), srr = xcd_span_last(nrr);
+  // fix-ups of the dW2 tiles whose contraction was split in the previous phase
+  const int tpe10 = ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
+  const int nfx = fix_dw2 ? meta.nsplit * tpe10 : 0;
+  const Span sfx = xcd_span(nfx);
   const int c11 = d11.count();
   const int c12 = max(0, ceil_div(s12.end - s12.begin, s12.step));
   const int crr = max(0, ceil_div(srr.end - srr.begin, srr.step));
-  for (int q = 0; q < c11 + c12 + crr; ++q) {
-    const int item = q < c11 ? d11.item(meta, q)
-                   : q < c11 + c12 ? n11 + s12.begin + (q - c11) * s12.step
-                                   : n11 + n12 + srr.begin + (q - c11 - c12) * srr.step;
-    if (item < n11) {
-      // dW1[e] (d x f) = X_e^T dH_e; X_e rows gathered from x through perm
-      const int e = item / (MT11 * NT11), rem = item % (MT11 * NT11);
-      const int mt = rem / NT11, nt = rem % NT11;
+  const int cfx = max(0, ceil_div(sfx.end - sfx.begin, sfx.step));
+  for (int q = 0; q < c11 + c12 + crr + cfx; ++q) {
+    if (q < c11) {
+      // dW1[e] (d x f) = X_e^T dH_e over chunk c of the expert's rows; bf16: the
+      // token rows gathered in route_order; fp32: x through perm
+      const WItem wi = d11.item(meta, E, q);
+      const int e = wi.e, mt = wi.t / NT11, nt = wi.t % NT11;
       const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
-      const int pe = meta.off[e], ce = meta.cnt[e];
-      // bf16: the token rows gathered in route_order; fp32: x through perm
-      const gemm::Operand A = (sizeof(T) == 2)
-          ? gemm::Operand{reinterpret_cast<const char*>(p.xs), d, nullptr, 1, pe, ce, d, m0}
-          : gemm::Operand{reinterpret_cast<const char*>(p.x), d, p.perm, p.k, pe, ce, d, m0};
-      gemm::Operand B{reinterpret_cast<const char*>(p.dh), f, nullptr, 1, pe, ce, f, n0};
-      float* g = gw1 + (long)e * d * f;
-      float sq = 0.f;
-      gemm::tile<T, NS, true, true>(
-          lds, A, B, ce, p.zero,
-          [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
-            if (m0 + r < d && n0 + c < f) {
-              F8 nv = cvt8(old);
-#pragma unroll
-              for (int u = 0; u < 8; ++u) nv.v[u] = zero_experts ? v[u] : nv.v[u] + v[u];
-              st8(g + (long)(m0 + r) * f + n0 + c, nv);
-#pragma unroll
-              for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
-            }
-          },
-          [&](int r, int c) {
-            Raw8<float> old{};
-            if (!zero_experts && m0 + r < d && n0 + c < f) old = ldr8(g + (long)(m0 + r) * f + n0 + c);
-            return old;
-          });
+      weight_grad_tile<T, NS>(p, lds, meta, wi,
+                              sizeof(T) == 2 ? reinterpret_cast<const char*>(p.xs) : reinterpret_cast<const char*>(p.x),
+                              sizeof(T) == 2 ? nullptr : p.perm, sizeof(T) == 2 ? 1 : p.k, d,
+                              reinterpret_cast<const char*>(p.dh), f, m0, n0, gw1 + (long)e * d * f, p.wpart1,
+                              MT11 * NT11, zero_experts, n10 + e * (MT11 * NT11) + wi.t);
+      continue;
+    }
+    if (q >= c11 + c12 + crr) {
+      const int u = sfx.begin + (q - c11 - c12 - crr) * sfx.step;
+      const int e = meta.splitlist[u / tpe10], t = u % tpe10;
+      const float sq = fix_split_tile(meta, p.grads + (long)d * E + (long)E * d * f + (long)e * f * d, p.wpart2, e, t,
+                                      f, d, ceil_div(d, gemm::BN));
       const float s = block_sum(sq, meta.red);
-      if (tid == 0) p.norm_part[n10 + item] = s;
-    } else if (item < n11 + n12) {
+      if (tid == 0) p.norm_part[e * tpe10 + t] = s;
+      continue;
+    }
+    const int item = q < c11 + c12 ? n11 + s12.begin + (q - c11) * s12.step
+                                   : n11 + n12 + srr.begin + (q - c11 - c12) * srr.step;
+    if (item < n11 + n12) {
       const int tI = item - n11;
       const int mg = tI / NTd, nt = tI % NTd;
       const int e = expert_of_tile(meta, E, mg);
@@ -1330,8 +1418,24 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   if (!(skip & 32u)) phase_bwd2<T, NS>(p, scratch, meta, zero_e);
   MOE_SYNC(5);
   trace_mark(p, 6, 0);
-  if (!(skip & 64u)) phase_bwd1<T, NS>(p, scratch, meta, zero_r, zero_e, want_dx);
+  if (!(skip & 64u)) phase_bwd1<T, NS>(p, scratch, meta, zero_r, zero_e, want_dx, !(skip & 32u));
   MOE_SYNC(6);
+  if (meta.nsplit > 0 && !(skip & 64u)) {
+    // complete the dW1 tiles whose contraction was split, so the global norm
+    // below sees whole gradients; a grid barrier separates the two
+    const int d = p.d, f = p.f, E = p.E;
+    const int tpe = ceil_div(d, gemm::BM) * ceil_div(f, gemm::BN);
+    const int n10 = E * ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
+    const Span sp = xcd_span(meta.nsplit * tpe);
+    for (int u = sp.begin; u < sp.end; u += sp.step) {
+      const int e = meta.splitlist[u / tpe], t = u % tpe;
+      const float sq = fix_split_tile(meta, p.grads + (long)d * E + (long)e * d * f, p.wpart1, e, t, d, f,
+                                      ceil_div(f, gemm::BN));
+      const float s = block_sum(sq, meta.red);
+      if (threadIdx.x == 0) p.norm_part[n10 + e * tpe + t] = s;
+    }
+    if (!grid_barrier(p.ctrl, p.epoch * 8u + 8u, &meta.flag)) return;
+  }
   trace_mark(p, 7, 0);
   if (!(skip & 128u)) phase_final<T, OCC>(p, scratch, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
   __syncthreads();

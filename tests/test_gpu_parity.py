@@ -139,6 +139,21 @@ def test_routing_ties_and_empty_experts():
         run.close()
 
 
+@pytest.mark.parametrize("dtype,T,d,f,E,mb,wg_per_cu", [("f32", 300, 72, 136, 5, 3, 1),
+                                                        ("bf16", 1000, 256, 384, 16, 2, 1),
+                                                        ("bf16", 1000, 256, 384, 16, 2, 2)])
+def test_skewed_routing_split_contractions(dtype, T, d, f, E, mb, wg_per_cu):
+    # a router bias sends most tokens to experts 0 and 1: their weight-gradient
+    # contractions are split into chunks, the partial tiles added back in the
+    # following phase (and the one after it), over accumulated microbatches
+    cfg = synth.small_config("skewed", T, d, f, E, 2, dtype, microbatches=mb)
+    inp = synth.make_inputs(cfg, 8)
+    bias = np.zeros(E, np.float32)
+    bias[0], bias[1] = 4.0, 2.0
+    inp.router_bias = bias
+    _run_and_compare(cfg, inp, F32_TOL if dtype == "f32" else BF16_TOL, steps=1, wg_per_cu=wg_per_cu)
+
+
 def test_gradient_accumulation_f32():
     cfg = synth.small_config("accum_f32", 96, 64, 128, 4, 2, "f32", microbatches=3)
     _run_and_compare(cfg, synth.make_inputs(cfg, 6), F32_TOL, steps=1)
