@@ -1372,7 +1372,7 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
 }
 
 // ===========================================================================
-// The persistent kernel: one cooperative launch per update (or microbatch)
+// The persistent kernel: one launch per update (or microbatch)
 // ===========================================================================
 template <typename T, int OCC>
 __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
