@@ -353,8 +353,14 @@ constexpr int dma_lds_bytes(int NS) { return NS * DMA_STAGE > BM * CROW * 4 ? NS
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// one direct-to-LDS load: 16 bytes per lane from src to LDS byte address
+// lds_off + 16 * lane (lds_off wave-uniform)
+__device__ __forceinline__ void dma16(const char* src, uint32_t lds_off) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(uintptr_t)lds_off, 16, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) for n in {0, 8, 16}; expcnt and lgkmcnt left alone
@@ -370,48 +376,60 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
+// The direct-to-LDS loads of one operand.  Wave w's instruction i (0..3)
+// fills LDS bytes [1024 (4w + i), +1024) of the operand's stage:
+//  * K-rows: LDS row r = 8 (4w + i) + lane / 8 (128 bytes of k), physical
+//    16-byte unit lane % 8, which holds logical k-unit u = (lane % 8) ^
+//    ((4i + lane / 16) % 8) (the swizzle u ^ ((r / 2) % 8));
+//  * MN-rows: k-row kk = 16w + 4i + lane / 16 of the stage, physical slot
+//    lane % 16, which holds columns mn0 + 8 s.. with s = (lane % 16) ^
+//    4 ((lane / 16) % 4) (the swizzle s ^ 4 (kk % 4)).
+// Along k a lane's source only moves by a fixed stride, so each lane keeps
+// its k-tile-0 address per instruction and the number of k-tiles for which
+// that address is in range; later k-tiles, and lanes out of range, load the
+// zero page.  Issuing a k-tile then costs one add and one select per
+// instruction, with no multiplies or branches.
 template <bool MN>
 struct DmaOp {
-  // per lane and instruction i (0..3): K-rows -> source row start (bytes) or
-  // -1, and the logical k-unit this lane carries; MN-rows -> k-row within the
-  // stage and the column byte offset (or -1)
-  long rowbase[4];
-  int unit[4];
-  long coloff;
-  int krow0;
+  const char* ptr[4];  // this lane's source in k-tile 0, per instruction
+  int nv[4];           // k-tiles in which that source is in range
+  long step;           // source bytes per k-tile (wave-uniform)
+  uint32_t wofs;       // this wave's LDS byte offset within an operand stage (wave-uniform)
 
   __device__ __forceinline__ void init(const Operand& o) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wofs = (uint32_t)w * 4096u;
     if constexpr (!MN) {
+      step = 128;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * (4 * w + i) + (lane >> 3);
-        unit[i] = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
-        rowbase[i] = (row < o.nrows) ? map_row(o, o.p0 + row) * o.ld * 2 + unit[i] * 16 : -1;
+        const int unit = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
+        const bool ok = row < o.nrows;
+        ptr[i] = ok ? o.base + map_row(o, o.p0 + row) * o.ld * 2 + unit * 16 : o.base;
+        nv[i] = ok ? max(0, (o.lim - unit * 8 + 63) >> 6) : 0;
       }
     } else {
+      step = 128 * o.ld;
       const int slot = (lane & 15) ^ (4 * ((lane >> 4) & 3));
       const int mn = o.mn0 + slot * 8;
-      coloff = (mn < o.lim) ? (long)mn * 2 : -1;
-      krow0 = 16 * w + (lane >> 4);   // + 4 i
-    }
-  }
-
-  __device__ __forceinline__ void issue(const Operand& o, int kt, char* st, const char* zero) const {
-    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* src = zero;
-      if constexpr (!MN) {
-        if (rowbase[i] >= 0 && kt * 64 + unit[i] * 8 < o.lim) src = o.base + rowbase[i] + (long)kt * 128;
-      } else {
-        const int kk = kt * 64 + krow0 + 4 * i;
-        if (coloff >= 0 && kk < o.nrows) src = o.base + (long)(o.p0 + kk) * o.ld * 2 + coloff;
+      for (int i = 0; i < 4; ++i) {
+        const int kk0 = 16 * w + 4 * i + (lane >> 4);
+        ptr[i] = o.base + ((long)(o.p0 + kk0) * o.ld + mn) * 2;
+        nv[i] = mn < o.lim ? max(0, (o.nrows - kk0 + 63) >> 6) : 0;
       }
-      dma16(src, st + (4 * w + i) * 1024);
     }
   }
 
+  // the loads of k-tile kt into the operand stage at st
+  __device__ __forceinline__ void issue(int kt, char* st, const char* zero) const {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st)) + wofs;
+    const long off = (long)kt * step;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(kt < nv[i] ? ptr[i] + off : zero, base + 1024u * i);
+  }
 };
 
 // LDS reads of data written by the direct-to-LDS loads are issued as inline
@@ -420,10 +438,6 @@ struct DmaOp {
 // otherwise drain every outstanding load before each read.
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
-}
 
 // LDS byte address of this lane's fragment (K-rows: the b128 read; MN-rows:
 // the first of the two transpose reads, the second is 1024 bytes further)
@@ -586,8 +600,8 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
   lds_sync();  // the previous user of this LDS is done (its global stores may still be in flight)
   for (int j = 0; j < NS - 1 && j < nk; ++j) {
     char* st = lds + j * DMA_STAGE;
-    da.issue(A, j, st, zero);
-    db.issue(B, j, st + DMA_OP, zero);
+    da.issue(j, st, zero);
+    db.issue(j, st + DMA_OP, zero);
   }
   if (nk > 0) {
     const int w = threadIdx.x >> 6;
@@ -605,8 +619,8 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
     lds_barrier();
     if (NS - 1 < nk) {
       char* nx = lds + (NS - 1) * DMA_STAGE;
-      da.issue(A, NS - 1, nx, zero);
-      db.issue(B, NS - 1, nx + DMA_OP, zero);
+      da.issue(NS - 1, nx, zero);
+      db.issue(NS - 1, nx + DMA_OP, zero);
     }
     Frags F0, F1, F2, F3;
     P::template step<false, -1>(F0, F0, acc, fa0[0], fa1[0], fb0[0], fb1[0]);
@@ -621,8 +635,8 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
       lds_barrier();
       if (kt + NS < nk) {
         char* nx = lds + so;
-        da.issue(A, kt + NS, nx, zero);
-        db.issue(B, kt + NS, nx + DMA_OP, zero);
+        da.issue(kt + NS, nx, zero);
+        db.issue(kt + NS, nx + DMA_OP, zero);
       }
       P::template step<true, -1>(F0, F2, acc, fa0[0] + sn, fa1[0] + sn, fb0[0] + sn, fb1[0] + sn);
       P::template step<true, 1>(F1, F3, acc, fa0[1] + sn, fa1[1] + sn, fb0[1] + sn, fb1[1] + sn);
