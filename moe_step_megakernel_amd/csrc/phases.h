@@ -124,6 +124,14 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // equal to within one item.  Workgroup b runs on XCD b % 8.
 struct Span {
   int begin, end, step;
+  int begin2 = 0, end2 = 0, step2 = 1;   // an optional second run, taken after the first
+  __device__ __forceinline__ int count() const {
+    return max(0, ceil_div(end - begin, step)) + max(0, ceil_div(end2 - begin2, step2));
+  }
+  __device__ __forceinline__ int item(int i) const {
+    const int c1 = max(0, ceil_div(end - begin, step));
+    return i < c1 ? begin + i * step : begin2 + (i - c1) * step2;
+  }
 };
 __device__ __forceinline__ Span xcd_span(int n) {
   const int G = gridDim.x;
@@ -165,7 +173,7 @@ struct DealW {
   bool snake;
   int G, w, tpe, n;
   __device__ __forceinline__ int count() const {
-    if (!snake) return max(0, ceil_div(sp.end - sp.begin, sp.step));
+    if (!snake) return sp.count();
     const int full = n / G, rem = n % G;   // rounds of G items, then a partial round
     const int last = (full & 1) ? G - 1 - w : w;
     return full + (last < rem ? 1 : 0);
@@ -173,7 +181,7 @@ struct DealW {
   // this workgroup's i-th item
   __device__ __forceinline__ WItem item(const Meta& meta, int E, int i) const {
     if (!snake) {
-      const int q = sp.begin + i * sp.step;
+      const int q = sp.item(i);
       return {q / tpe, 0, q % tpe};
     }
     const int q = i * G + ((i & 1) ? G - 1 - w : w);
@@ -192,6 +200,59 @@ __device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int E, int 
   dl.n = tpe * (dl.snake ? meta.cpre[E] : E);
   dl.sp = xcd_span(dl.n);
   return dl;
+}
+
+// Cost-weighted deal of two kinds of items within each XCD block.  The
+// kind whose items cost more is dealt round-robin as in xcd_span, so the
+// first r workgroups of the XCD get one item more than the others.  The
+// other kind fills up: in fH full rounds every workgroup takes one item
+// (round-robin, as xcd_span), where fH is what the loaded workgroups can take
+// within the XCD's mean cost; the rest goes round-robin to the others only.
+// Within a round the XCD's workgroups take consecutive items, so operands
+// shared by neighbouring tiles stay in L2 together.  Plain round-robin of
+// both kinds gives the extra items of both to the same low-index workgroups.
+// Costs are in k-tile units.
+__device__ __forceinline__ void cost_deal(int n0, int c0, int n1, int c1, Span& s0, Span& s1) {
+  const bool sw = c1 > c0;
+  const int nA = sw ? n1 : n0, cA = sw ? c1 : c0, nB = sw ? n0 : n1, cB = sw ? c0 : c1;
+  const Span sa = xcd_span(nA);
+  Span sb = xcd_span(nB);
+  const int G = gridDim.x;
+  const bool x8 = (G & 7) == 0;
+  const int P = x8 ? G >> 3 : G, j = x8 ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int x = x8 ? (int)(blockIdx.x & 7) : 0, nxcd = x8 ? 8 : 1;
+  const int cha = (nA + nxcd - 1) / nxcd, chb = (nB + nxcd - 1) / nxcd;
+  const int alo = min(nA, x * cha), ahi = min(nA, alo + cha);
+  const int blo = min(nB, x * chb), bhi = min(nB, blo + chb);
+  const int NA = ahi - alo, NB = bhi - blo;
+  const int r = NA % P, q = NA / P;
+  if (r > 0 && cB > 0) {
+    // filler items the r loaded workgroups can take within the mean cost
+    const long S = (long)NA * cA + (long)NB * cB;
+    const long fh = ((S - (long)P * (q + 1) * cA) >= 0) ? (S - (long)P * (q + 1) * cA) / ((long)P * cB) : -1;
+    if (fh >= 0) {
+      // fH rounded down or up, whichever gives the smaller largest cost
+      auto worst = [&](long fq) {
+        const long rest = (long)NB - fq * P;
+        return max((long)(q + 1) * cA + fq * cB, (long)q * cA + (fq + (rest + P - r - 1) / (P - r)) * cB);
+      };
+      long fq = min((long)NB / P, fh);
+      if (fq + 1 <= (long)NB / P && worst(fq + 1) < worst(fq)) ++fq;
+      // plain round-robin: workgroup 0 gets the extra item of both kinds
+      const long plain = (long)(q + 1) * cA + (long)(NB / P + (NB % P > 0 ? 1 : 0)) * cB;
+      if (worst(fq) < plain) {
+        const int fH = (int)fq;
+        sb = {blo + j, blo + fH * P, P};
+        if (j >= r) {
+          sb.begin2 = blo + fH * P + (j - r);
+          sb.end2 = bhi;
+          sb.step2 = P - r;
+        }
+      }
+    }
+  }
+  s0 = sw ? sb : sa;
+  s1 = sw ? sa : sb;
 }
 
 // Completes the weight-gradient tiles whose contraction was split: grads of
@@ -955,10 +1016,12 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
 
   // each kind of work is dealt over the XCDs on its own, so every XCD gets the
   // same mix (the kinds differ a lot in cost)
+  // (a cost-weighted deal as in dW1 + dX measured slower here at 2x1024 and
+  // no faster at 32x1024)
   const DealW d10 = deal_weight_tiles(meta, E, MT10 * NT10);
   const Span s9 = xcd_span(n9), sr = xcd_span_last(nr);
   const int c10 = d10.count();
-  const int c9 = max(0, ceil_div(s9.end - s9.begin, s9.step));
+  const int c9 = s9.count();
   const int cr = max(0, ceil_div(sr.end - sr.begin, sr.step));
   for (int q = 0; q < c10 + c9 + cr; ++q) {
     if (q < c10) {
@@ -971,7 +1034,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
                               MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
       continue;
     }
-    const int item = q < c10 + c9 ? n10 + s9.begin + (q - c10) * s9.step
+    const int item = q < c10 + c9 ? n10 + s9.item(q - c10)
                                   : n10 + n9 + sr.begin + (q - c10 - c9) * sr.step;
     if (item < n10 + n9) {
       const int tI = item - n10;
@@ -1068,14 +1131,17 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
-  const DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11);
-  const Span s12 = xcd_span(n12), srr = xcd_span_last(nrr);
+  DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11);
+  Span s12 = xcd_span(n12);
+  const Span srr = xcd_span_last(nrr);
+  if (!d11.snake)   // dW1 tiles: k-tiles over the mean rows per expert; dX tiles: over f
+    cost_deal(n11, ceil_div(meta.off[E], 64 * E) + 6, n12, ceil_div(f, 64) + 3, d11.sp, s12);
   // fix-ups of the dW2 tiles whose contraction was split in the previous phase
   const int tpe10 = ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
   const int nfx = fix_dw2 ? meta.nsplit * tpe10 : 0;
   const Span sfx = xcd_span(nfx);
   const int c11 = d11.count();
-  const int c12 = max(0, ceil_div(s12.end - s12.begin, s12.step));
+  const int c12 = s12.count();
   const int crr = max(0, ceil_div(srr.end - srr.begin, srr.step));
   const int cfx = max(0, ceil_div(sfx.end - sfx.begin, sfx.step));
   for (int q = 0; q < c11 + c12 + crr + cfx; ++q) {
@@ -1101,7 +1167,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       if (tid == 0) p.norm_part[e * tpe10 + t] = s;
       continue;
     }
-    const int item = q < c11 + c12 ? n11 + s12.begin + (q - c11) * s12.step
+    const int item = q < c11 + c12 ? n11 + s12.item(q - c11)
                                    : n11 + n12 + srr.begin + (q - c11 - c12) * srr.step;
     if (item < n11 + n12) {
       const int tI = item - n11;
