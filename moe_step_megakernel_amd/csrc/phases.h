@@ -285,31 +285,37 @@ __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot
     p.trace[((size_t)blockIdx.x * kPhases + phase) * 3 + slot] = wall_clock64();
 }
 
-// Partial router logits of one token over one column segment (see the
-// router phase): acc[e] = sum over the segment's columns c of x[tok][c] W_r[c][e],
-// for the EGT groups of 4 experts from group EG0 on (padded experts read zero
-// weights).
-// W_r goes through LDS chunk by chunk; the token's 8-column pieces are loaded
-// four at a time, one group ahead of the group being multiplied.
-template <typename T, int EGT, int EG0>
-__device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x, float4* wl, float (&acc)[kMaxExperts],
-                                                    int tok, bool mine, int s_me, int S, int DC, int EG) {
+// Partial router logits of TL tokens over one column segment (see the
+// router phase): acc[u][e] = sum over the segment's columns c of
+// x[tok + u][c] W_r[c][e], for the EGT groups of 4 experts from group EG0 on
+// (padded experts read zero weights).  Each W_r value read from LDS serves
+// all TL tokens.  W_r goes through LDS chunk by chunk; the tokens' 8-column
+// pieces are loaded PG at a time, one group ahead of the group being
+// multiplied.
+template <typename T, int EGT, int EG0, int TL, int PG>
+__device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x, float4* wl,
+                                                    float (&acc)[TL][kMaxExperts], int tok, int nmine, int s_me,
+                                                    int S, int DC, int EG) {
   const int tid = threadIdx.x, d = p.d, E = p.E;
 #pragma unroll
-  for (int e = 4 * EG0; e < 4 * (EG0 + EGT); ++e) acc[e] = 0.f;
+  for (int u = 0; u < TL; ++u)
+#pragma unroll
+    for (int e = 4 * EG0; e < 4 * (EG0 + EGT); ++e) acc[u][e] = 0.f;
   for (int c0 = 0; c0 < d; c0 += DC) {
     const int dc = min(DC, ceil_div(d - c0, 8 * S) * (8 * S));
     const int ni = dc / (8 * S);
-    auto load_group = [&](int i0, Raw8<T> (&xr)[4]) {
+    auto load_group = [&](int i0, Raw8<T> (&xr)[TL][PG]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + (i0 + u) * 8 * S + 8 * s_me;
-        xr[u] = Raw8<T>{};
-        if (mine && i0 + u < ni && c < d) xr[u] = ldr8(x + (long)tok * d + c);
-      }
+      for (int u = 0; u < TL; ++u)
+#pragma unroll
+        for (int v = 0; v < PG; ++v) {
+          const int c = c0 + (i0 + v) * 8 * S + 8 * s_me;
+          xr[u][v] = Raw8<T>{};
+          if (u < nmine && i0 + v < ni && c < d) xr[u][v] = ldr8(x + (long)(tok + u) * d + c);
+        }
     };
-    // the token's first pieces are in flight while W_r is staged
-    Raw8<T> xa[4], xb[4];
+    // the tokens' first pieces are in flight while W_r is staged
+    Raw8<T> xa[TL][PG], xb[TL][PG];
     load_group(0, xa);
     __syncthreads();
     // all of a thread's loads are issued before its LDS stores (16 per batch)
@@ -333,31 +339,40 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
       wl[((i * 8 + j) * EG + eg) * S + s] = w;
     }
     __syncthreads();
-    for (int i0 = 0; i0 < ni; i0 += 4) {
-      load_group(i0 + 4, xb);
+    for (int i0 = 0; i0 < ni; i0 += PG) {
+      load_group(i0 + PG, xb);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (i0 + u < ni) {
-          const F8 xv = cvt8(xa[u]);
+      for (int v = 0; v < PG; ++v) {
+        if (i0 + v < ni) {
+          F8 xv[TL];
+#pragma unroll
+          for (int u = 0; u < TL; ++u) xv[u] = cvt8(xa[u][v]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float4* wr = wl + ((i0 + u) * 8 + j) * EG * S + s_me;
+            // with several tokens per lane, W_r reads are not hoisted across
+            // rows j, so the reads in flight do not outgrow the register file
+            if (TL > 1) asm volatile("" ::: "memory");
+            const float4* wr = wl + ((i0 + v) * 8 + j) * EG * S + s_me;
             float4 w[EGT];
 #pragma unroll
             for (int eg = 0; eg < EGT; ++eg)
               w[eg] = EG0 + eg < EG ? wr[(EG0 + eg) * S] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int eg = 0; eg < EGT; ++eg) {
-              acc[(EG0 + eg) * 4 + 0] += xv.v[j] * w[eg].x;
-              acc[(EG0 + eg) * 4 + 1] += xv.v[j] * w[eg].y;
-              acc[(EG0 + eg) * 4 + 2] += xv.v[j] * w[eg].z;
-              acc[(EG0 + eg) * 4 + 3] += xv.v[j] * w[eg].w;
-            }
+            for (int u = 0; u < TL; ++u)
+#pragma unroll
+              for (int eg = 0; eg < EGT; ++eg) {
+                acc[u][(EG0 + eg) * 4 + 0] += xv[u].v[j] * w[eg].x;
+                acc[u][(EG0 + eg) * 4 + 1] += xv[u].v[j] * w[eg].y;
+                acc[u][(EG0 + eg) * 4 + 2] += xv[u].v[j] * w[eg].z;
+                acc[u][(EG0 + eg) * 4 + 3] += xv[u].v[j] * w[eg].w;
+              }
           }
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xa[u] = xb[u];
+      for (int u = 0; u < TL; ++u)
+#pragma unroll
+        for (int v = 0; v < PG; ++v) xa[u][v] = xb[u][v];
     }
   }
 }
@@ -368,21 +383,25 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
 // a wave spread over the banks), then one thread per (token, expert) adds them
 // up.  The staged W_r chunk is dead by now; its space holds the partials.
 // With one segment per token, or too little LDS, the segments are combined by
-// a butterfly over adjacent lanes instead.
-template <int EG0, int EGT>
-__device__ __forceinline__ void router_reduce(float (&acc)[kMaxExperts], float* zacc, float4* wl, int E, int EP, int S,
-                                              int nb, int t_me, int s_me, int wbudget) {
+// a butterfly over adjacent lanes instead (the same order of additions for
+// every token).  Thread (t_me, s_me) holds tokens t_me TL + u.
+template <int EG0, int EGT, int TL>
+__device__ __forceinline__ void router_reduce(float (&acc)[TL][kMaxExperts], float* zacc, float4* wl, int E, int EP,
+                                              int S, int nb, int t_me, int s_me, int wbudget) {
   const int tid = threadIdx.x;
   const int e0 = 4 * EG0, ne = min(E, 4 * (EG0 + EGT)) - e0;
   const int RW = ceil_div(ne, 4) * 4 + 4;
-  if (S > 1 && kThreads * RW * 4 <= wbudget) {
+  if (S > 1 && kThreads * TL * RW * 4 <= wbudget) {
     float* part = reinterpret_cast<float*>(wl);
     __syncthreads();
 #pragma unroll
-    for (int eg = 0; eg < EGT; ++eg)
-      if (eg * 4 < ne)
-        *reinterpret_cast<float4*>(part + tid * RW + eg * 4) =
-            make_float4(acc[e0 + eg * 4], acc[e0 + eg * 4 + 1], acc[e0 + eg * 4 + 2], acc[e0 + eg * 4 + 3]);
+    for (int u = 0; u < TL; ++u)
+#pragma unroll
+      for (int eg = 0; eg < EGT; ++eg)
+        if (eg * 4 < ne)
+          *reinterpret_cast<float4*>(part + ((t_me * TL + u) * S + s_me) * RW + eg * 4) =
+              make_float4(acc[u][e0 + eg * 4], acc[u][e0 + eg * 4 + 1], acc[u][e0 + eg * 4 + 2],
+                          acc[u][e0 + eg * 4 + 3]);
     __syncthreads();
     for (int o = tid; o < nb * ne; o += kThreads) {
       const int tk = o / ne, e = o % ne;
@@ -392,19 +411,64 @@ __device__ __forceinline__ void router_reduce(float (&acc)[kMaxExperts], float* 
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 4 * EGT; ++e) {
-      if (e < ne) {
-        for (int m = S >> 1; m >= 1; m >>= 1) acc[e0 + e] += __shfl_xor(acc[e0 + e], m, 64);
-      }
-    }
-    __syncthreads();
-    if (t_me < nb && s_me == 0) {
+    for (int u = 0; u < TL; ++u)
 #pragma unroll
-      for (int e = 0; e < 4 * EGT; ++e)
-        if (e < ne) zacc[t_me * EP + e0 + e] = acc[e0 + e];
+      for (int e = 0; e < 4 * EGT; ++e) {
+        if (e < ne) {
+          for (int m = S >> 1; m >= 1; m >>= 1) acc[u][e0 + e] += __shfl_xor(acc[u][e0 + e], m, 64);
+        }
+      }
+    __syncthreads();
+    if (s_me == 0) {
+#pragma unroll
+      for (int u = 0; u < TL; ++u)
+        if (t_me * TL + u < nb) {
+#pragma unroll
+          for (int e = 0; e < 4 * EGT; ++e)
+            if (e < ne) zacc[(t_me * TL + u) * EP + e0 + e] = acc[u][e0 + e];
+        }
     }
   }
   __syncthreads();
+}
+
+// Router logits of a block of nb tokens into zacc ([nb][EP]); thread
+// (t_me, s_me) covers tokens b0 + t_me TL + u of column segment s_me.
+template <typename T, int OCC, int TL>
+__device__ __forceinline__ void router_block(const KParams& p, const T* x, float4* wl, float* zacc, int b0, int nb,
+                                             int t_me, int s_me, int S, int DC, int EG, int EP, int wbudget) {
+  const int E = p.E;
+  const int tok = b0 + t_me * TL;
+  const int nmine = min(TL, max(0, nb - t_me * TL));
+  // pieces per load group: fewer with more tokens per lane, and fewer with
+  // half the register file
+  constexpr int PG = TL == 1 ? 4 : 2;
+  float acc[TL][kMaxExperts];
+  if (EG <= 4) {
+    router_segment_sums<T, 4, 0, TL, PG>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_reduce<0, 4, TL>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+  } else if constexpr (TL == 1 && OCC == 1) {
+    // more than 16 experts: two passes over the columns, 8 expert groups
+    // each (one pass over all 64 would not fit the register file)
+    router_segment_sums<T, 8, 0, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_segment_sums<T, 8, 8, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_reduce<0, 16, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+  } else if constexpr (TL == 1) {
+    // with half the registers: passes of 16 experts, each summed over the
+    // segments before the next one starts
+    router_segment_sums<T, 4, 0, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_reduce<0, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+    router_segment_sums<T, 4, 4, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_reduce<4, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+    if (EG > 8) {
+      router_segment_sums<T, 4, 8, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+      router_reduce<8, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+    }
+    if (EG > 12) {
+      router_segment_sums<T, 4, 12, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+      router_reduce<12, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
+    }
+  }
 }
 
 // ===========================================================================
@@ -440,7 +504,7 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   const T* x = reinterpret_cast<const T*>(p.x);
 
   // Router logits, TP tokens per pass, each split over S column segments
-  // (TP * S <= 256 threads, S a power of two <= 64 so a token's segments are
+  // (TP * S / TL <= 256 threads, S a power of two <= 64 so a token's segments are
   // adjacent lanes of one wave).  Segment s of a token owns the 8-column
   // pieces 8s, 8s + 8S, 8s + 16S, ... and keeps all E partial sums in
   // registers; W_r is staged in LDS in the order the segments read it (for
@@ -449,12 +513,18 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   // distinct consecutive 16-byte words or broadcasts.
   // The logits of a block live in LDS (zacc, [TP][EP]) within a quarter of the
   // scratch; a larger token range takes several blocks.
+  // With 16 or more tokens per pass and at most 16 experts, each lane works
+  // on TL tokens (4 with one workgroup per CU, 2 with half the register
+  // file), so every W_r value it reads from LDS serves TL tokens.
   constexpr int kScratch = scratch_bytes(OCC);
   int TP = 1;
-  while (TP < min(t_hi - t_lo, kThreads) && 2 * TP * EP * 4 <= kScratch / 4) TP <<= 1;
-  int S = min(64, kThreads / TP);
-  while (S > 1 && 8 * S > d) S >>= 1;
+  while (TP < min(t_hi - t_lo, 4 * kThreads) && 2 * TP * EP * 4 <= kScratch / 4) TP <<= 1;
   const int EG = (E + 3) / 4;
+  constexpr int kTL = OCC == 1 ? 4 : 2;
+  const int TL = (TP >= 16 && EG <= 4) ? kTL : 1;
+  TP = min(TP, TL * kThreads);
+  int S = min(64, kThreads * TL / TP);
+  while (S > 1 && 8 * S > d) S >>= 1;
   float* zacc = reinterpret_cast<float*>(smem + 256);                          // [TP][EP]
   float4* wl = reinterpret_cast<float4*>(smem + 256 + TP * EP * 4);           // staged W_r chunk
   // (the reads of padded expert groups may run up to 16 * S float4 past the chunk)
@@ -468,32 +538,8 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
 
   for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
     const int nb = min(TP, t_hi - b0);
-    float acc[kMaxExperts];
-    if (EG <= 4) {
-      router_segment_sums<T, 4, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-      router_reduce<0, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-    } else if constexpr (OCC == 1) {
-      // more than 16 experts: two passes over the columns, 8 expert groups
-      // each (one pass over all 64 would not fit the register file)
-      router_segment_sums<T, 8, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-      router_segment_sums<T, 8, 8>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-      router_reduce<0, 16>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-    } else {
-      // with half the registers: passes of 16 experts, each summed over the
-      // segments before the next one starts
-      router_segment_sums<T, 4, 0>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-      router_reduce<0, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-      router_segment_sums<T, 4, 4>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-      router_reduce<4, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-      if (EG > 8) {
-        router_segment_sums<T, 4, 8>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-        router_reduce<8, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-      }
-      if (EG > 12) {
-        router_segment_sums<T, 4, 12>(p, x, wl, acc, b0 + t_me, t_me < nb, s_me, S, DC, EG);
-        router_reduce<12, 4>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-      }
-    }
+    if (TL > 1) router_block<T, OCC, kTL>(p, x, wl, zacc, b0, nb, t_me, s_me, S, DC, EG, EP, wbudget);
+    else router_block<T, OCC, 1>(p, x, wl, zacc, b0, nb, t_me, s_me, S, DC, EG, EP, wbudget);
     // token_topk over each group of EP lanes (the group never crosses a wave)
     for (int g0 = 0; g0 < nb; g0 += TPI) {
       const int tok = b0 + g0 + slot;

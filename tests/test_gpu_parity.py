@@ -93,6 +93,16 @@ def test_ragged_shapes_bf16_two_workgroups_per_cu(T, d, f, E, k):
     _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1, wg_per_cu=2)
 
 
+@pytest.mark.parametrize("dtype,wg_per_cu,T", [("bf16", 1, 16 * 256 + 352), ("bf16", 2, 16 * 512 + 704),
+                                              ("f32", 1, 16 * 256 + 352)])
+def test_router_several_tokens_per_lane(dtype, wg_per_cu, T):
+    # 17 tokens per workgroup: the router pass covers 32 token slots with
+    # several tokens per lane, and the last lane group holds one live token
+    cfg = synth.small_config(f"router_tl_{dtype}", T, 96, 64, 12, 2, dtype)
+    _run_and_compare(cfg, synth.make_inputs(cfg, 6), BF16_TOL if dtype == "bf16" else F32_TOL, steps=1,
+                     wg_per_cu=wg_per_cu)
+
+
 @pytest.mark.parametrize("wg_per_cu", [1, 2])
 def test_readiness_counters_between_expert_products(wg_per_cu):
     # no grid barrier between GEMM 1 and GEMM 2: per-row-tile ready counters
