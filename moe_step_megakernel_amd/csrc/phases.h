@@ -985,9 +985,145 @@ __device__ __forceinline__ float combine_tokens(const KParams& p) {
   return lsum;
 }
 
-template <typename T>
+// The same for rows of at most 256 CP columns (one chunk), software-pipelined
+// over the half-wave's tokens: the gates and slots are loaded two tokens
+// ahead and the token and expert-output rows one token ahead, all issued
+// before the current token's dO stores.  The vector-memory counter retires
+// in issue order, so a load issued after a store could only be awaited
+// together with the store; issued before it, the next token's rows are in
+// flight while the stores drain.
+template <typename T, int CP>
+__device__ __forceinline__ float combine_tokens_1chunk(const KParams& p) {
+  constexpr int NS = CP * kMaxTopK > 8 ? 8 : CP * kMaxTopK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, hl = lane & 31;
+  const int G = gridDim.x, lwg = logical_wg();
+  const int d = p.d, k = p.k;
+  const T* tg = reinterpret_cast<const T*>(p.t);
+  T* dout = reinterpret_cast<T*>(p.dout);
+  const int stride = G * kWaves * 2;
+  float lsum = 0.f;
+  float g[kMaxTopK], gn[kMaxTopK], gnn[kMaxTopK];
+  int pos[kMaxTopK], pn[kMaxTopK], pnn[kMaxTopK];
+  auto load_idx = [&](int tok, float (&gg)[kMaxTopK], int (&pp)[kMaxTopK]) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      gg[j] = 0.f;
+      pp[j] = 0;
+      if (j < k && tok < p.T) {
+        gg[j] = p.gate[tok * k + j];
+        pp[j] = p.inv[tok * k + j];
+      }
+    }
+  };
+  auto load_rows = [&](int tok, const int (&pp)[kMaxTopK], Raw8<T> (&tr)[CP], Raw8<float> (&o)[NS]) {
+    const bool live = tok < p.T;
+#pragma unroll
+    for (int ch = 0; ch < CP; ++ch) {
+      const int c = ch * 256 + hl * 8;
+      tr[ch] = Raw8<T>{};
+      if (live && c < d) tr[ch] = ldr8(tg + (long)tok * d + c);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = s / CP, ch = s % CP;
+      const int c = ch * 256 + hl * 8;
+      o[s] = Raw8<float>{};
+      if (live && j < k && c < d) o[s] = ldr8(p.out + (long)pp[j] * d + c);
+    }
+  };
+  int base = (lwg * kWaves + wave) * 2;
+  Raw8<T> tr[CP], trn[CP];
+  Raw8<float> o[NS], on[NS];
+  load_idx(base + half, g, pos);
+  load_idx(base + half + stride, gn, pn);
+  load_rows(base + half, pos, tr, o);
+  // the loop bound is uniform over the wave (the half-wave sums need both halves)
+  for (; base < p.T; base += stride) {
+    const int tok = base + half;
+    const bool live = tok < p.T;
+    load_idx(tok + 2 * stride, gnn, pnn);
+    load_rows(tok + stride, pn, trn, on);
+    float dg[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) dg[j] = 0.f;
+    F8 y[CP];
+#pragma unroll
+    for (int ch = 0; ch < CP; ++ch)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[ch].v[q] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = s / CP, ch = s % CP;
+      const F8 ov = cvt8(o[s]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[ch].v[q] += g[j] * ov.v[q];
+    }
+#pragma unroll
+    for (int ch = 0; ch < CP; ++ch) {
+      const F8 tv = cvt8(tr[ch]);
+      const int c = ch * 256 + hl * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float r = y[ch].v[q] - tv.v[q];
+        if (live && c < d) lsum += r * r;
+        y[ch].v[q] = r * p.inv_tupd;   // now dL/dy
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = s / CP, ch = s % CP;
+      const int c = ch * 256 + hl * 8;
+      if (live && j < k && c < d) {
+        const F8 ov = cvt8(o[s]);
+        F8 w;
+        float sdot = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          w.v[q] = g[j] * y[ch].v[q];
+          sdot += y[ch].v[q] * ov.v[q];
+        }
+        dg[j] += sdot;
+        st8(dout + (long)pos[j] * d + c, w);
+      }
+    }
+    float sg = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) dg[j] += __shfl_xor(dg[j], m, 64);
+        sg += g[j] * dg[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (live && j < k && hl == j) p.dzsel[tok * k + j] = g[j] * (dg[j] - sg);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      g[j] = gn[j];
+      pos[j] = pn[j];
+      gn[j] = gnn[j];
+      pn[j] = pnn[j];
+    }
+#pragma unroll
+    for (int ch = 0; ch < CP; ++ch) tr[ch] = trn[ch];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) o[s] = on[s];
+  }
+  return lsum;
+}
+
+// The pipelined form is built into the kernel for two workgroups per CU
+// (large batches), where it measured faster; with one per CU it did not.
+template <typename T, int OCC>
 __device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
-  const float lsum = p.k <= 2 ? combine_tokens<T, 4>(p) : combine_tokens<T, 1>(p);
+  float lsum;
+  if constexpr (OCC == 2)
+    lsum = p.k <= 2 ? (p.d <= 1024 ? combine_tokens_1chunk<T, 4>(p) : combine_tokens<T, 4>(p))
+                    : (p.d <= 256 ? combine_tokens_1chunk<T, 1>(p) : combine_tokens<T, 1>(p));
+  else
+    lsum = p.k <= 2 ? combine_tokens<T, 4>(p) : combine_tokens<T, 1>(p);
   const float s = block_sum(lsum, meta.red);
   if (threadIdx.x == 0) p.loss_part[logical_wg()] = s;
 }
@@ -1180,8 +1316,11 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11);
   Span s12 = xcd_span(n12);
   const Span srr = xcd_span_last(nrr);
-  if (!d11.snake)   // dW1 tiles: k-tiles over the mean rows per expert; dX tiles: over f
-    cost_deal(n11, ceil_div(meta.off[E], 64 * E) + 6, n12, ceil_div(f, 64) + 3, d11.sp, s12);
+  // dW1 tiles: k-tiles over the mean rows per expert; dX tiles: over f.  Built
+  // into the kernel for two workgroups per CU only (large batches), where it
+  // measured faster; in the other kernel its code alone cost more than it saved.
+  if constexpr (NS == 2)
+    if (!d11.snake) cost_deal(n11, ceil_div(meta.off[E], 64 * E) + 6, n12, ceil_div(f, 64) + 3, d11.sp, s12);
   // fix-ups of the dW2 tiles whose contraction was split in the previous phase
   const int tpe10 = ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
   const int nfx = fix_dw2 ? meta.nsplit * tpe10 : 0;
@@ -1524,7 +1663,7 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   if (!(skip & 8u) && !phase_ffn2<T, NS>(p, scratch, meta, ready12 && !(skip & 4u))) return;
   MOE_SYNC(3);
   trace_mark(p, 4, 0);
-  if (!(skip & 16u)) phase_combine<T>(p, meta);
+  if (!(skip & 16u)) phase_combine<T, OCC>(p, meta);
   MOE_SYNC(4);
   trace_mark(p, 5, 0);
   if (!(skip & 32u)) phase_bwd2<T, NS>(p, scratch, meta, zero_e);
