@@ -236,7 +236,10 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const int n10 = E * cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
   const int n11 = E * cdiv(d, moe::gemm::BM) * cdiv(f, moe::gemm::BN);
   const int nrr = cdiv(d * E, moe::kThreads);
-  const size_t rch = (size_t)cdiv(cfg->max_tokens, moe::kRouterTokens);
+  // router-gradient partial chunks: the most any token count up to max_tokens uses
+  size_t rch = 1;
+  for (int t = 1; t <= cfg->max_tokens; ++t)
+    rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h->grid)));
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

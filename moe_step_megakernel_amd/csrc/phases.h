@@ -33,7 +33,16 @@ constexpr int scratch_bytes(int occ) {
 }
 constexpr int smem_bytes(int occ) { return kMetaBytes + scratch_bytes(occ); }
 static_assert(2 * smem_bytes(2) <= 160 * 1024, "two workgroups per compute unit must fit the LDS");
-constexpr int kRouterTokens = 128;   // tokens per router-gradient partial
+// Tokens per router-gradient partial (a chunk of T x a 256-column block is one
+// work item of the dH + dW2 phase): 128, halved down to 32 while the items
+// are fewer than the workgroups, so a small batch spreads them over more
+// workgroups in cheaper pieces.  The same rule sizes the partial buffer.
+__host__ __device__ constexpr int router_chunk_tokens(int T, int d, int G) {
+  const int cch = (d + kThreads - 1) / kThreads;
+  int r = 128;
+  while (r > 32 && ((T + r - 1) / r) * cch < G) r >>= 1;
+  return r;
+}
 constexpr int kRouterBlockTokens = 32;
 
 // Routing metadata kept in LDS for the whole launch (every workgroup computes
@@ -1189,7 +1198,8 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
   const int n9 = meta.moff[E] * NTf;
   const int MT10 = ceil_div(f, gemm::BM), NT10 = ceil_div(d, gemm::BN);
   const int n10 = E * MT10 * NT10;
-  const int RCH = ceil_div(p.T, kRouterTokens), CCH = ceil_div(d, kThreads);
+  const int RT = router_chunk_tokens(p.T, d, gridDim.x);
+  const int RCH = ceil_div(p.T, RT), CCH = ceil_div(d, kThreads);
   const int nr = RCH * CCH;
   const T* gp = reinterpret_cast<const T*>(p.gp);
   T* dh = reinterpret_cast<T*>(p.dh);
@@ -1246,13 +1256,13 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
             return graw;
           });
     } else {
-      // router-gradient partial: tokens [rc*kRouterTokens, +kRouterTokens) x columns [cc*256, +256)
+      // router-gradient partial: tokens [rc*RT, +RT) x columns [cc*256, +256)
       const int ir = item - n10 - n9;
       const int rc = ir / CCH, cc = ir % CCH;
       float* acc = reinterpret_cast<float*>(lds);                      // [E][256]
       int* se = reinterpret_cast<int*>(acc + E * kThreads);            // [64*k] experts
       float* sz = reinterpret_cast<float*>(se + 64 * kMaxTopK);        // [64*k] dL/dlogit
-      const int t0 = rc * kRouterTokens, t1 = min(p.T, t0 + kRouterTokens);
+      const int t0 = rc * RT, t1 = min(p.T, t0 + RT);
       const int c = cc * kThreads + tid;
       __syncthreads();
       for (int i = tid; i < E * kThreads; i += kThreads) acc[i] = 0.f;
@@ -1309,7 +1319,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   const int n12 = want_dx ? meta.moff[E] * NTd : 0;
   const int nrr = ceil_div(d * E, kThreads);
   const int n10 = E * ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
-  const int RCH = ceil_div(p.T, kRouterTokens);
+  const int RCH = ceil_div(p.T, router_chunk_tokens(p.T, d, gridDim.x));
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
