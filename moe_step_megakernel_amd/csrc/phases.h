@@ -43,7 +43,6 @@ __host__ __device__ constexpr int router_chunk_tokens(int T, int d, int G) {
   while (r > 32 && ((T + r - 1) / r) * cch < G) r >>= 1;
   return r;
 }
-constexpr int kRouterBlockTokens = 32;
 
 // Routing metadata kept in LDS for the whole launch (every workgroup computes
 // it in P1 from the global histogram).

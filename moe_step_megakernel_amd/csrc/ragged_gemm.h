@@ -18,10 +18,11 @@
 //    fragment is two ds_read_b64_tr_b16, the gfx950 LDS read that transposes
 //    16-bit data across each group of 16 lanes.  (fp32 mode has no such read;
 //    its MN-rows operands are transposed in registers before the LDS write.)
-// Row indices may go through a map (the dispatch gather: row = perm[p] / k),
-// so no gathered copy of the tokens is ever materialised.  Two LDS stages: the
-// global loads of k-tile i+1 are in flight while the matrix cores work on
-// k-tile i.
+// Row indices may go through a map (the dispatch gather on load: row =
+// perm[p] / k, used by the fp32 path; the bf16 path reads a gathered copy).
+// bf16 tiles stage k-tiles through NS LDS buffers with direct-to-LDS loads
+// (NS - 1 k-tiles in flight while the matrix cores work on one); fp32 tiles
+// use two register-staged buffers.
 #pragma once
 
 #include "device_common.h"
