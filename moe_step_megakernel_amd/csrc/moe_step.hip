@@ -236,10 +236,18 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const int n10 = E * cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
   const int n11 = E * cdiv(d, moe::gemm::BM) * cdiv(f, moe::gemm::BN);
   const int nrr = cdiv(d * E, moe::kThreads);
-  // router-gradient partial chunks: the most any token count up to max_tokens uses
+  // router-gradient partial chunks: the most any token count up to max_tokens
+  // uses.  The chunk is 128, 64 or 32 tokens over three ranges of the token
+  // count, and within each range the chunk count grows with it, so the
+  // largest token count of each range (clipped to max_tokens) gives the bound.
   size_t rch = 1;
-  for (int t = 1; t <= cfg->max_tokens; ++t)
-    rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h->grid)));
+  {
+    const int m = cdiv(h->grid, cdiv(d, moe::kThreads));
+    const int cand[3] = {cfg->max_tokens, std::min(cfg->max_tokens, 128 * (m - 1)),
+                         std::min(cfg->max_tokens, 64 * (m - 1))};
+    for (int t : cand)
+      if (t >= 1) rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h->grid)));
+  }
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
