@@ -93,6 +93,16 @@ def test_ragged_shapes_bf16_two_workgroups_per_cu(T, d, f, E, k):
     _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1, wg_per_cu=2)
 
 
+@pytest.mark.parametrize("dtype,E,k,wg_per_cu", [("f32", 1, 1, 1), ("bf16", 1, 1, 1), ("bf16", 1, 1, 2),
+                                                ("bf16", 2, 2, 1)])
+def test_degenerate_expert_counts(dtype, E, k, wg_per_cu):
+    # one expert (every token routed to it with gate 1, the router gradient
+    # is zero) and top-k = E (every expert chosen by every token)
+    cfg = synth.small_config(f"degenerate_{dtype}_E{E}k{k}", 997, 96, 64, E, k, dtype)
+    _run_and_compare(cfg, synth.make_inputs(cfg, 8), BF16_TOL if dtype == "bf16" else F32_TOL, steps=2,
+                     wg_per_cu=wg_per_cu)
+
+
 @pytest.mark.parametrize("dtype,wg_per_cu,T", [("bf16", 1, 16 * 256 + 352), ("bf16", 2, 16 * 512 + 704),
                                               ("f32", 1, 16 * 256 + 352)])
 def test_router_several_tokens_per_lane(dtype, wg_per_cu, T):
