@@ -93,6 +93,17 @@ def test_ragged_shapes_bf16_two_workgroups_per_cu(T, d, f, E, k):
     _run_and_compare(cfg, synth.make_inputs(cfg, 4), BF16_TOL, steps=1, wg_per_cu=2)
 
 
+@pytest.mark.parametrize("dtype,T,d,f,E,k,wg_per_cu", [("f32", 1, 8, 8, 3, 2, 1), ("bf16", 1, 8, 8, 3, 2, 1),
+                                                       ("bf16", 1, 8, 8, 3, 2, 2), ("bf16", 5, 16, 24, 2, 1, 1),
+                                                       ("f32", 5, 16, 24, 2, 1, 1)])
+def test_minimum_shapes(dtype, T, d, f, E, k, wg_per_cu):
+    # the smallest sizes the boundary accepts: one token, d = f = 8 (a single
+    # valid 8-element piece in every 64-deep k-tile and 128-wide column tile)
+    cfg = synth.small_config(f"minimum_{dtype}_T{T}", T, d, f, E, k, dtype)
+    _run_and_compare(cfg, synth.make_inputs(cfg, 9), BF16_TOL if dtype == "bf16" else F32_TOL, steps=2,
+                     wg_per_cu=wg_per_cu)
+
+
 @pytest.mark.parametrize("dtype,E,k,wg_per_cu", [("f32", 1, 1, 1), ("bf16", 1, 1, 1), ("bf16", 1, 1, 2),
                                                 ("bf16", 2, 2, 1)])
 def test_degenerate_expert_counts(dtype, E, k, wg_per_cu):
