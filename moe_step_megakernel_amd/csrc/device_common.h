@@ -101,9 +101,31 @@ __device__ __forceinline__ void st8(uint16_t* p, const F8& f) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
+// Non-temporal forms, for outputs that are only read again in a later phase
+// and are too large to stay in the caches meanwhile: they do not displace the
+// operand lines the phase is still reusing.  The product phases use them in the
+// two-per-CU kernel (large batches); with one workgroup per CU the outputs are
+// small enough to stay cached and the plain stores measured no slower.
+typedef unsigned ntu4_t __attribute__((ext_vector_type(4)));
+typedef float ntf4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st8nt(uint16_t* p, const F8& f) {
+  const ntu4_t u = {pack_bf16x2(f.v[0], f.v[1]), pack_bf16x2(f.v[2], f.v[3]), pack_bf16x2(f.v[4], f.v[5]),
+                    pack_bf16x2(f.v[6], f.v[7])};
+  __builtin_nontemporal_store(u, reinterpret_cast<ntu4_t*>(p));
+}
+__device__ __forceinline__ void st8nt(float* p, const F8& f) {
+  __builtin_nontemporal_store(ntf4_t{f.v[0], f.v[1], f.v[2], f.v[3]}, reinterpret_cast<ntf4_t*>(p));
+  __builtin_nontemporal_store(ntf4_t{f.v[4], f.v[5], f.v[6], f.v[7]}, reinterpret_cast<ntf4_t*>(p) + 1);
+}
 __device__ __forceinline__ void st8(float* p, const F8& f) {
   reinterpret_cast<float4*>(p)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+}
+
+template <bool NT, typename P>
+__device__ __forceinline__ void st8x(P* p, const F8& f) {
+  if constexpr (NT) st8nt(p, f);
+  else st8(p, f);
 }
 
 __device__ __forceinline__ float to_f32(uint16_t b) { return bf16_to_f32(b); }

@@ -815,8 +815,8 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
 #pragma unroll
         for (int q = 0; q < 8; ++q) gelu_and_grad(h[q], a.v[q], da.v[q]);
         const long o = (long)(p0 + r) * f + n0 + c;
-        st8(act + o, a);
-        st8(gp + o, da);
+        st8x<NS == 2>(act + o, a);
+        st8x<NS == 2>(gp + o, da);
       }
     };
     gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
@@ -867,7 +867,7 @@ __device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& me
         F8 o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) o.v[q] = v[q];
-        st8(p.out + (long)(p0 + r) * d + n0 + c, o);
+        st8x<NS == 2>(p.out + (long)(p0 + r) * d + n0 + c, o);
       }
     });
   }
@@ -1162,7 +1162,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
       F8 o;
 #pragma unroll
       for (int u = 0; u < 8; ++u) o.v[u] = v[u];
-      st8(pt + r * gemm::BN + c, o);
+      st8x<NS == 2>(pt + r * gemm::BN + c, o);
     });
     return;
   }
@@ -1174,7 +1174,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
           F8 nv = cvt8(old);
 #pragma unroll
           for (int u = 0; u < 8; ++u) nv.v[u] = zero ? v[u] : nv.v[u] + v[u];
-          st8(g + (long)(m0 + r) * N + n0 + c, nv);
+          st8x<NS == 2>(g + (long)(m0 + r) * N + n0 + c, nv);
 #pragma unroll
           for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
         }
@@ -1246,7 +1246,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
               F8 g8 = cvt8(graw);
 #pragma unroll
               for (int u = 0; u < 8; ++u) g8.v[u] *= v[u];
-              st8(dh + (long)(p0 + r) * f + n0 + c, g8);
+              st8x<NS == 2>(dh + (long)(p0 + r) * f + n0 + c, g8);
             }
           },
           [&](int r, int c) {
@@ -1382,7 +1382,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
               F8 o;
 #pragma unroll
               for (int u = 0; u < 8; ++u) o.v[u] = v[u];
-              st8(dxs + (long)slot * d + n0 + c, o);
+              st8x<NS == 2>(dxs + (long)slot * d + n0 + c, o);
             }
           },
           [&](int r, int c) { return (r < mrows && n0 + c < d) ? p.perm[p0 + r] : 0; });
