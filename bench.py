@@ -217,7 +217,7 @@ def main(argv=None):
                          "experts after every W (one timed step = one microbatch)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               f"(the update's multi-GPU sharding is described, not built)", file=sys.stderr)
         return 2
 

@@ -22,7 +22,7 @@ be checked against the pages by eye.  Sources (Latch project pages):
   oracle reads; it computes in float64).
 
 The pages do not write the layer's formulas.  The readings adopted where they are
-silent (each also listed in the design doc):
+silent:
 
 * layer output y_i = sum_j g_ij * FFN_{e_ij}(x_i); FFN_e(x) = gelu(x W1[e]) W2[e];
   no biases, residual, norm or auxiliary loss; the skewed-load workload adds a
