@@ -42,17 +42,24 @@ class GpuRun:
     """One layer on cuda:0 with the inputs of ``inp`` (all microbatches)."""
 
     def __init__(self, cfg: synth.LayerConfig, inp: synth.LayerInputs, *, clip_norm=None, wg_per_cu=0,
-                 ready_gemm12=False, cooperative=False):
-        self.cfg, self.inp = cfg, inp
+                 ready_gemm12=False, cooperative=False, max_tokens=None):
         self.ready_gemm12 = ready_gemm12
         self.cooperative = cooperative
         self.dev = torch.device("cuda", 0)
-        self.layer = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, max(1, cfg.tokens), cfg.dtype,
+        if max_tokens is None:
+            max_tokens = max(1, cfg.tokens)
+        self.layer = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, max_tokens, cfg.dtype,
                                   lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.eps,
                                   weight_decay=cfg.weight_decay,
                                   clip_norm=cfg.clip_norm if clip_norm is None else clip_norm,
                                   wg_per_cu=wg_per_cu)
         self.layer.load_params(torch.from_numpy(inp.flat_params()))
+        self.set_inputs(cfg, inp)
+
+    def set_inputs(self, cfg: synth.LayerConfig, inp: synth.LayerInputs):
+        """Switches the token inputs (the layer shape must not change); the
+        weights and moments stay those on the device."""
+        self.cfg, self.inp = cfg, inp
         self.x = device_tokens(inp.x, inp.x_bits, cfg.dtype, self.dev)
         self.t = device_tokens(inp.t, inp.t_bits, cfg.dtype, self.dev)
         self.bias = None if inp.router_bias is None else torch.from_numpy(inp.router_bias).to(self.dev)

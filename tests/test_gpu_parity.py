@@ -16,6 +16,7 @@ import torch
 import oracle
 import synth
 from gpu_helpers import GpuRun, compare_update, oracle_update, rel_l2, say
+from moe_step_megakernel_amd import binding as B
 
 pytestmark = pytest.mark.gpu
 
@@ -217,6 +218,54 @@ def test_zero_tokens_only_decays():
         torch.cuda.synchronize()
         assert np.all(run.layer.grads.cpu().numpy() == 0.0)
         assert rel_l2(run.layer.params.cpu().numpy(), p0 * (1 - cfg.lr * cfg.weight_decay)) < 1e-7
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("dtype,wg_per_cu,tmax,d,f,E,k,token_counts", [
+    ("f32", 1, 1000, 72, 136, 5, 2, (1000, 77, 513, 1)),
+    # d = 1024 over 256 workgroups: the router-gradient partials of 8064 and
+    # 4032 tokens take 126 chunks (64 and 32 tokens each), more than the 71 of
+    # max_tokens = 9000 (chunks of 128)
+    ("bf16", 1, 9000, 1024, 64, 16, 2, (9000, 8064, 4032, 333)),
+    # over 512 workgroups: 8128 tokens take 254 chunks of 32, 9000 take 141 of 64
+    ("bf16", 2, 9000, 1024, 64, 16, 2, (9000, 8128, 1, 2999)),
+    ("bf16", 1, 600, 128, 64, 64, 8, (600, 37, 599)),
+])
+def test_handle_reused_across_token_counts(dtype, wg_per_cu, tmax, d, f, E, k, token_counts):
+    # one handle, sized for max_tokens, runs updates of fewer tokens in turn
+    # (arena, grid and kernel stay those chosen at create); each update is
+    # checked against the oracle from the device state before it
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    cfg0 = synth.small_config(f"reuse_{dtype}", tmax, d, f, E, k, dtype)
+    inp0 = synth.make_inputs(cfg0, 11)
+    say(f"[gpu] handle reuse {dtype} wg_per_cu={wg_per_cu} max_tokens={tmax} d={d} f={f} E={E} k={k} "
+        f"token counts {token_counts}")
+    run = GpuRun(cfg0, inp0, wg_per_cu=wg_per_cu, max_tokens=tmax)
+    try:
+        params = inp0.flat_params().astype(np.float64)
+        m = np.zeros_like(params)
+        v = np.zeros_like(params)
+        for s, T in enumerate(token_counts, start=1):
+            cfg = synth.small_config(f"reuse_{dtype}_T{T}", T, d, f, E, k, dtype)
+            inp = synth.make_inputs(cfg, 20 + s)
+            run.set_inputs(cfg, inp)
+            say(f"  update {s}: {T} tokens")
+            out = run.update(s)
+            _check_routing(cfg, inp, out, params[:d * E].reshape(d, E))
+            ref = oracle_update(cfg, inp, params, m, v, s, out["idx"])
+            errs, bad = compare_update(cfg, out, ref, **tol)
+            assert not bad, f"update {s} ({T} tokens): {bad}: {errs}"
+            params, m, v = (a.astype(np.float64) for a in run.state())
+        if dtype == "f32":
+            # more tokens than max_tokens: refused on the host, the handle keeps working
+            x = torch.zeros(tmax + 1, d, dtype=torch.float32, device=run.dev)
+            with pytest.raises(B.MoeStepError):
+                run.layer.run(x, x, step=len(token_counts) + 1)
+            out = run.update(len(token_counts) + 1)
+            ref = oracle_update(run.cfg, run.inp, params, m, v, len(token_counts) + 1, out["idx"])
+            errs, bad = compare_update(run.cfg, out, ref, **tol)
+            assert not bad, f"update after a refused call: {bad}: {errs}"
     finally:
         run.close()
 
