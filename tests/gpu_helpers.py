@@ -42,8 +42,9 @@ class GpuRun:
     """One layer on cuda:0 with the inputs of ``inp`` (all microbatches)."""
 
     def __init__(self, cfg: synth.LayerConfig, inp: synth.LayerInputs, *, clip_norm=None, wg_per_cu=0,
-                 ready_gemm12=False, cooperative=False, max_tokens=None):
+                 ready_gemm12=False, cooperative=False, max_tokens=None, stream=None):
         self.ready_gemm12 = ready_gemm12
+        self.stream = stream
         self.cooperative = cooperative
         self.dev = torch.device("cuda", 0)
         if max_tokens is None:
@@ -85,7 +86,7 @@ class GpuRun:
             dx = torch.empty(T, d, dtype=torch.float32, device=self.dev) if want_dx else None
             self.layer.run(x, t, tokens_in_update=cfg.tokens_in_update, step=step, zero_grad=(mb == 0),
                            apply=(mb == cfg.microbatches - 1), dx=dx, router_bias=self.bias, debug=dbg,
-                           ready_gemm12=self.ready_gemm12, cooperative=self.cooperative)
+                           ready_gemm12=self.ready_gemm12, cooperative=self.cooperative, stream=self.stream)
             self.layer.status()
             if debug:
                 outs["logits"].append(dbg["router_logits"].cpu().numpy())

@@ -207,6 +207,31 @@ def test_deterministic_reruns():
     assert outs[0]["loss"] == outs[1]["loss"]
 
 
+@pytest.mark.parametrize("wg_per_cu", [1, 2])
+def test_side_stream_matches_default_stream(wg_per_cu):
+    # the update enqueued on a caller's stream instead of the default one: same
+    # bits (the update is deterministic), and the oracle gates on the first run
+    cfg = synth.small_config("side_stream_bf16", 1000, 256, 384, 16, 2, "bf16")
+    inp = synth.make_inputs(cfg, 12)
+    side = torch.cuda.Stream(device=0)
+    outs = []
+    for stream in (None, side):
+        run = GpuRun(cfg, inp, wg_per_cu=wg_per_cu, stream=stream)
+        try:
+            torch.cuda.synchronize()   # inputs and weights were copied on the default stream
+            outs.append(run.update(1))
+        finally:
+            run.close()
+    params = inp.flat_params().astype(np.float64)
+    ref = oracle_update(cfg, inp, params, np.zeros_like(params), np.zeros_like(params), 1, outs[1]["idx"])
+    errs, bad = compare_update(cfg, outs[1], ref, **BF16_TOL)
+    assert not bad, f"side stream: {bad}: {errs}"
+    for key in ("grads", "params", "exp_avg", "exp_avg_sq"):
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+    assert np.array_equal(outs[0]["dx"][0], outs[1]["dx"][0])
+    assert outs[0]["loss"] == outs[1]["loss"]
+
+
 def test_zero_tokens_only_decays():
     cfg = synth.small_config("empty", 0, 64, 128, 4, 2, "f32")
     inp = synth.make_inputs(synth.small_config("empty_src", 1, 64, 128, 4, 2, "f32"), 0)
