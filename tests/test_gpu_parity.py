@@ -186,6 +186,14 @@ def test_skewed_routing_split_contractions(dtype, T, d, f, E, mb, wg_per_cu):
     _run_and_compare(cfg, inp, F32_TOL if dtype == "f32" else BF16_TOL, steps=1, wg_per_cu=wg_per_cu)
 
 
+def test_f32_at_the_layer_shape():
+    # fp32 mode at the bf16 workloads' layer shape (d = 768, f = 1536, 16
+    # experts, top-2, 2048 tokens): contractions of 768 and 1536 terms and
+    # about 256 routed rows per expert, still within 1e-5 over two updates
+    cfg = synth.small_config("f32_2x1024_shape", 2048, 768, 1536, 16, 2, "f32")
+    _run_and_compare(cfg, synth.make_inputs(cfg, 13), F32_TOL, steps=2)
+
+
 def test_gradient_accumulation_f32():
     cfg = synth.small_config("accum_f32", 96, 64, 128, 4, 2, "f32", microbatches=3)
     _run_and_compare(cfg, synth.make_inputs(cfg, 6), F32_TOL, steps=1)
