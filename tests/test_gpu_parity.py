@@ -194,6 +194,16 @@ def test_f32_at_the_layer_shape():
     _run_and_compare(cfg, synth.make_inputs(cfg, 13), F32_TOL, steps=2)
 
 
+@pytest.mark.timeout(900)
+def test_max_tokens_limit():
+    # the most tokens a handle accepts (2^24, with narrow d = f = 8 so the
+    # arena stays near 4 GB): 32,768 tokens per workgroup in routing and
+    # route_order, a weight-gradient contraction over about 8.4 M rows per
+    # expert, 131,072 router-gradient chunks; one update against the oracle
+    cfg = synth.small_config("max_tokens_bf16", 1 << 24, 8, 8, 4, 2, "bf16")
+    _run_and_compare(cfg, synth.make_inputs(cfg, 14), BF16_TOL, steps=1)
+
+
 def test_gradient_accumulation_f32():
     cfg = synth.small_config("accum_f32", 96, 64, 128, 4, 2, "f32", microbatches=3)
     _run_and_compare(cfg, synth.make_inputs(cfg, 6), F32_TOL, steps=1)
