@@ -250,6 +250,32 @@ def test_side_stream_matches_default_stream(wg_per_cu):
     assert outs[0]["loss"] == outs[1]["loss"]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nonfinite_logit_reported_and_handle_recovers(dtype):
+    # a NaN in one token's activations makes its router logits NaN: the kernel
+    # flags it (every index it derives stays in range), moe_step_status reports
+    # it, and after that the same handle runs a clean update that matches
+    cfg = synth.small_config(f"nonfinite_{dtype}", 96, 64, 128, 4, 2, dtype)
+    inp = synth.make_inputs(cfg, 15)
+    run = GpuRun(cfg, inp)
+    try:
+        x = run.x.clone()
+        x[5, 3] = float("nan")
+        run.layer.run(x, run.t, step=1)
+        with pytest.raises(B.MoeStepError) as ei:
+            run.layer.status()
+        assert ei.value.status == B.MOE_ERR_DEVICE
+        assert "non-finite router logit" in str(ei.value)
+        run.layer.load_params(torch.from_numpy(inp.flat_params()))
+        out = run.update(1)
+        params = inp.flat_params().astype(np.float64)
+        ref = oracle_update(cfg, inp, params, np.zeros_like(params), np.zeros_like(params), 1, out["idx"])
+        errs, bad = compare_update(cfg, out, ref, **(BF16_TOL if dtype == "bf16" else F32_TOL))
+        assert not bad, f"update after the reported error: {bad}: {errs}"
+    finally:
+        run.close()
+
+
 def test_zero_tokens_only_decays():
     cfg = synth.small_config("empty", 0, 64, 128, 4, 2, "f32")
     inp = synth.make_inputs(synth.small_config("empty_src", 1, 64, 128, 4, 2, "f32"), 0)
