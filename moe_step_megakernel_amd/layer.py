@@ -42,6 +42,7 @@ class MoeLayerStep:
         expert products by per-row-tile readiness counters (same results).  ``cooperative``
         launches through hipLaunchCooperativeKernel instead of an ordinary launch."""
         n = 0 if x is None else int(x.shape[0])
+        self._check_tensors(n, x, target, dx, router_bias, debug or {}, trace)
         flags = 0
         step_r = step_e = step
         if groups is not None:
@@ -73,6 +74,42 @@ class MoeLayerStep:
         B.moe_step_run_groups(self.handle, io, n, tokens_in_update or max(1, n), step_r, step_e, flags,
                               s.cuda_stream)
         self._shadow_valid = True
+
+    def _check_tensors(self, n, x, target, dx, router_bias, debug, trace):
+        """The C ABI takes bare device pointers, so every tensor is checked here
+        (device, dtype, contiguity, shape) before its pointer goes to the kernel."""
+        d, E, k = self.cfg.d_model, self.cfg.n_experts, self.cfg.top_k
+        act = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+        def check(name, t, dtype, shape):
+            if t is None:
+                return
+            if not isinstance(t, torch.Tensor) or t.device != self.dev:
+                raise ValueError(f"{name} must be a tensor on {self.dev}")
+            if t.dtype != dtype:
+                raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+
+        if (x is None) != (target is None):
+            raise ValueError("x and target are given together or not at all")
+        check("x", x, act, (n, d))
+        check("target", target, act, (n, d))
+        check("dx", dx, torch.float32, (n, d))
+        check("router_bias", router_bias, torch.float32, (E,))
+        shapes = {"router_logits": (torch.float32, (n, E)), "topk_idx": (torch.int32, (n, k)),
+                  "topk_gate": (torch.float32, (n, k)), "expert_counts": (torch.int32, (E,)),
+                  "route_perm": (torch.int32, (n * k,))}
+        for name, t in debug.items():
+            if name not in shapes:
+                raise ValueError(f"unknown debug output {name}")
+            check(name, t, *shapes[name])
+        if trace is not None:
+            check("trace", trace, torch.int64, tuple(trace.shape))
+            if trace.numel() < self.trace_words():
+                raise ValueError(f"trace needs {self.trace_words()} words, got {trace.numel()}")
 
     def status(self):
         B.moe_step_status(self.handle)

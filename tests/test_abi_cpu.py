@@ -87,3 +87,52 @@ def test_null_handle_calls_are_safe():
     assert lib.moe_step_arena_bytes(None) == 0
     lib.moe_step_destroy(None)
     assert isinstance(B.moe_step_last_error(None), str)
+
+
+def _layer_without_handle(dtype):
+    # the tensor checks of MoeLayerStep.run, on a layer object with no device
+    # handle: its "device" is the CPU, so tensors can be made here
+    import torch
+    from moe_step_megakernel_amd.layer import MoeLayerStep
+    layer = object.__new__(MoeLayerStep)
+    layer.cfg = B.make_config(16, 24, 4, 2, 64, dtype)
+    layer.dtype = dtype
+    layer.dev = torch.device("cpu")
+    layer.handle = None
+    layer.trace_words = lambda: 100
+    return layer
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_checks_tensors_before_any_pointer_is_passed(dtype):
+    import torch
+    layer = _layer_without_handle(dtype)
+    act = torch.bfloat16 if dtype == "bf16" else torch.float32
+    other = torch.float32 if dtype == "bf16" else torch.bfloat16
+    x = torch.zeros(10, 16, dtype=act)
+    ok = dict(dx=torch.zeros(10, 16), router_bias=torch.zeros(4),
+              debug={"router_logits": torch.zeros(10, 4), "topk_idx": torch.zeros(10, 2, dtype=torch.int32),
+                     "topk_gate": torch.zeros(10, 2), "expert_counts": torch.zeros(4, dtype=torch.int32),
+                     "route_perm": torch.zeros(20, dtype=torch.int32)},
+              trace=torch.zeros(100, dtype=torch.int64))
+    layer._check_tensors(10, x, x, **ok)
+    layer._check_tensors(0, None, None, None, None, {}, None)
+    bad = [
+        dict(x=x.to(other)),                                   # activation dtype of the other mode
+        dict(target=torch.zeros(10, 8, dtype=act)),            # wrong width
+        dict(x=torch.zeros(16, 10, dtype=act).t()),            # not contiguous
+        dict(target=None),                                     # x without target
+        dict(dx=torch.zeros(10, 16, dtype=torch.float64)),
+        dict(dx=torch.zeros(9, 16)),
+        dict(router_bias=torch.zeros(5)),
+        dict(debug={"topk_idx": torch.zeros(10, 2, dtype=torch.int64)}),
+        dict(debug={"route_perm": torch.zeros(10, dtype=torch.int32)}),
+        dict(debug={"logits": torch.zeros(10, 4)}),            # unknown name
+        dict(trace=torch.zeros(99, dtype=torch.int64)),        # too short
+    ]
+    for change in bad:
+        args = dict(x=x, target=x, **ok)
+        args.update(change)
+        with pytest.raises((TypeError, ValueError)):
+            layer._check_tensors(10, args["x"], args["target"], args["dx"], args["router_bias"], args["debug"],
+                                 args["trace"])
