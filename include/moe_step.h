@@ -4,16 +4,21 @@
  * (gfx950).
  *
  * What one update computes (Latch pages, "How a training megakernel works"):
- *   "One training update": forward pass, loss, backward pass by the chain rule,
- *   then a weight update;
- *   "From two weights to 200 million": a router sends each token to k of E small
- *   feed-forward networks; AdamW updates the weights from running averages of
- *   the gradients and of their squares;
- *   "What Latch does", steps 1, 3 and 4: the routing operations token_topk and
- *   route_order, grouped expert products ragged_mm, global-norm clipping and
- *   AdamW as tensor arithmetic; gradients return to the tokens routed through
- *   each expert; FP32 master weights and Adam moments with BF16 matrix products;
- *   "What Latch does", step 5: the whole update is one cooperative launch.
+ *   "One training update": a forward pass, the loss, gradients by the chain
+ *   rule, then a change of the weights against their gradients;
+ *   "From two weights to 200 million": every token goes to k of the E expert
+ *   feed-forward blocks chosen by a router; the optimizer is AdamW (moving
+ *   averages of the gradient and of its elementwise square);
+ *   "What Latch does", steps 1, 3 and 4: the layer is written with the routing
+ *   operations token_topk and route_order and the grouped expert product
+ *   ragged_mm; clipping by the global gradient norm and AdamW are tensor
+ *   expressions of the update; each expert's gradient flows back to the tokens
+ *   it received; master weights and both Adam moments stay FP32 while the
+ *   matrix products run in BF16;
+ *   "What Latch does", step 5: the pages run each update as one persistent
+ *   kernel.  Here, too, one update (or one microbatch of it) is one launch of
+ *   one persistent kernel; it is an ordinary launch by default (see
+ *   moe_step_run) and a cooperative one on request.
  *
  * Layer (readings where the pages are silent are stated in the design notes):
  *   z = x W_r (+ b)                 router logits, fp32
@@ -154,6 +159,15 @@ typedef struct {
 /* Launch through hipLaunchCooperativeKernel (the runtime guarantees that the
  * whole grid is resident) instead of an ordinary launch. */
 #define MOE_RUN_COOPERATIVE 0x20000u
+/* Test aid for the failure path (never needed in training): the bounded waits
+ * of this launch give up after about 10 us instead of about 2 s, and the last
+ * workgroup first waits for a word that nothing ever sets, so it gives up and
+ * never arrives at the first grid barrier.  Every other workgroup's wait at that
+ * barrier then gives up too; the launch ends with MOE_DEVICE_BARRIER_TIMEOUT,
+ * and every workgroup exits normally.  Only the routing phase runs before that
+ * barrier: it writes arena buffers, the debug outputs that are given, and (with
+ * MOE_RUN_REFRESH_SHADOW) the bf16 weight copy from the unchanged params. */
+#define MOE_RUN_TEST_TIMEOUT 0x40000u
 
 /* Status-word bits reported by moe_step_status as MOE_ERR_DEVICE. */
 #define MOE_DEVICE_BARRIER_TIMEOUT 0x1u
@@ -168,14 +182,20 @@ size_t moe_step_param_count(const moe_step_config* cfg);
 int moe_step_check_config(const moe_step_config* cfg);
 
 /* Creates a handle on cfg->device: validates cfg, allocates the device arena
- * (routing structures, stored activations, bf16 weight copy, barrier words) and
+ * (the planned GPU-memory arena that holds every value passed between phases,
+ * Latch "How a training megakernel works", "What Latch does", step 4: routing
+ * structures, stored activations, bf16 weight copy, barrier words) and
  * checks that the persistent grid fits co-resident.  Synchronous.
  * On failure *out is set to NULL and the reason is available from
  * moe_step_last_error(NULL). */
 int moe_step_create(const moe_step_config* cfg, moe_step_t* out);
 
 /* Enqueues one update on hip_stream (a hipStream_t; NULL = default stream):
- * one launch of the persistent kernel.  Asynchronous.
+ * one launch of the persistent kernel that runs the forward pass, loss,
+ * backward pass and weight update of the layer (Latch "How a training
+ * megakernel works", "What Latch does": one resident program per update, one
+ * launch per microbatch at the published batch in "How GPUs usually run it").
+ * Asynchronous.
  * The kernel needs all of its workgroups resident at once (grid barriers).  Its
  * grid is sized at create to exactly what the device holds (occupancy x CUs),
  * and by default it goes out as an ordinary launch: a cooperative launch costs
@@ -203,9 +223,15 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
 int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
                         int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream);
 
-/* Waits for the handle's last stream and reads the device status word.
- * Returns MOE_ERR_DEVICE (with the bits in last_error) if a kernel reported an
- * error, after resetting the device-side barrier state. */
+/* Waits for the handle's last stream and reads the device status word: the
+ * numerical check of the launch (non-finite router logits) and the bounded
+ * waits of its grid barriers (Latch "How a training megakernel works", "What
+ * Latch does", step 4: a phase waits at a grid-wide barrier; step 5: run the
+ * program's numerical checks).  Returns MOE_ERR_DEVICE (with the bits in
+ * last_error) if a kernel reported an error, after resetting the device-side
+ * barrier state and the abort word.  A launch enqueued after one that failed
+ * and before this call makes no writes (every workgroup finds the abort word
+ * set on entry and returns). */
 int moe_step_status(moe_step_t h);
 
 /* Words of io.trace needed for MOE_RUN_TRACE: workgroups * phases * 3. */
@@ -224,7 +250,9 @@ size_t moe_step_arena_bytes(moe_step_t h);
  * Valid until the next call on the same handle. Never NULL. */
 const char* moe_step_last_error(moe_step_t h);
 
-/* Waits for the last stream, frees the arena and the handle.  NULL-safe. */
+/* Waits for the last stream, frees the arena (the planned GPU-memory arena of
+ * Latch "How a training megakernel works", "What Latch does", step 4) and the
+ * handle.  NULL-safe. */
 void moe_step_destroy(moe_step_t h);
 
 #ifdef __cplusplus

@@ -21,6 +21,7 @@ MOE_RUN_ZERO_GRAD_ROUTER, MOE_RUN_ZERO_GRAD_EXPERTS = 0x10, 0x20
 MOE_RUN_APPLY_ROUTER, MOE_RUN_APPLY_EXPERTS = 0x40, 0x80
 MOE_RUN_READY_GEMM12 = 0x10000
 MOE_RUN_COOPERATIVE = 0x20000
+MOE_RUN_TEST_TIMEOUT = 0x40000
 
 
 def MOE_RUN_SKIP_PHASE(i: int) -> int:

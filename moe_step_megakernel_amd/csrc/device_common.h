@@ -202,13 +202,25 @@ struct Ctrl {
   unsigned* gen;     // last released target
   unsigned* status;  // error bits (MOE_DEVICE_*)
   unsigned* abort;   // nonzero once any workgroup gave up waiting
+  unsigned* never;   // a word nothing writes (the failure-path test waits on it)
+  uint64_t limit;    // bound of every wait, in ticks of the 100 MHz constant clock
 };
 
 // Bounded wait: about two seconds of the 100 MHz constant clock.
 constexpr uint64_t kBarrierTimeoutTicks = 200000000ull;
+// The bound under the failure-path test flag: about 10 us.
+constexpr uint64_t kTestTimeoutTicks = 1000ull;
+
+// A wait that gives up: the timeout bit and the abort word are set, so every
+// other workgroup's waits give up as well and the whole grid exits.
+__device__ __forceinline__ bool give_up(const Ctrl& c) {
+  __hip_atomic_fetch_or(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(c.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
 
 // Polls *p (relaxed, agent scope) until it equals target; false on timeout or
-// when another workgroup already gave up.
+// when another workgroup already gave up (checked every 256 polls).
 __device__ __forceinline__ bool wait_for(const Ctrl& c, const unsigned* p, unsigned target) {
   const uint64_t t0 = wall_clock64();
   unsigned polls = 0;
@@ -216,11 +228,8 @@ __device__ __forceinline__ bool wait_for(const Ctrl& c, const unsigned* p, unsig
     __builtin_amdgcn_s_sleep(2);
     if ((++polls & 255u) == 0u) {
       if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-          wall_clock64() - t0 > kBarrierTimeoutTicks) {
-        __hip_atomic_fetch_or(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(c.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return false;
-      }
+          wall_clock64() - t0 > c.limit)
+        return give_up(c);
     }
   }
   return true;
@@ -235,11 +244,8 @@ __device__ __forceinline__ bool wait_count(const Ctrl& c, const int* p, int targ
     __builtin_amdgcn_s_sleep(1);
     if ((++polls & 255u) == 0u) {
       if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-          wall_clock64() - t0 > kBarrierTimeoutTicks) {
-        __hip_atomic_fetch_or(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(c.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return false;
-      }
+          wall_clock64() - t0 > c.limit)
+        return give_up(c);
     }
   }
   return true;

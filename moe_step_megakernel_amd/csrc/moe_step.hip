@@ -354,7 +354,7 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   }
   if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK |
                     MOE_RUN_ZERO_GRAD_ROUTER | MOE_RUN_ZERO_GRAD_EXPERTS | MOE_RUN_APPLY_ROUTER |
-                    MOE_RUN_APPLY_EXPERTS | MOE_RUN_READY_GEMM12 | MOE_RUN_COOPERATIVE)) {
+                    MOE_RUN_APPLY_EXPERTS | MOE_RUN_READY_GEMM12 | MOE_RUN_COOPERATIVE | MOE_RUN_TEST_TIMEOUT)) {
     set_err(h->err, "unknown run flags 0x%x", run_flags);
     return MOE_ERR_ARG;
   }
@@ -466,6 +466,8 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   p.ctrl.status = h->ctrl + 32;
   p.ctrl.abort = h->ctrl + 64;
   p.ctrl.arrive = h->ctrl + 128;
+  p.ctrl.never = h->ctrl + 96;
+  p.ctrl.limit = (run_flags & MOE_RUN_TEST_TIMEOUT) ? moe::kTestTimeoutTicks : moe::kBarrierTimeoutTicks;
   p.epoch = ++h->epoch;
 
   hipError_t he = hipSetDevice(c.device);
@@ -487,7 +489,8 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   }
   h->last_stream = stream;
   h->launched = true;
-  if (!(run_flags & MOE_RUN_SKIP_MASK)) h->last_full_tokens = n_tokens;
+  if (run_flags & MOE_RUN_TEST_TIMEOUT) h->last_full_tokens = -1;
+  else if (!(run_flags & MOE_RUN_SKIP_MASK)) h->last_full_tokens = n_tokens;
   return MOE_OK;
 }
 

@@ -1,8 +1,9 @@
 // The phases of one MoE-layer training update, as device functions of the
 // persistent kernel.  Each phase is spread over every workgroup; phases that
 // read results produced on other compute units are separated by a grid barrier
-// (Latch pages, "What Latch does", step 4: phases across all SMs, a grid-wide
-// barrier where results cross SMs, values between phases in a planned arena).
+// (Latch pages, "What Latch does", step 4: work is grouped into phases that span
+// every SM, a phase waits at a grid-wide barrier for data made on other SMs, and
+// values that outlive a phase sit in a planned arena in GPU memory).
 //
 //   P0  bf16 weight copy refresh (optional); copy of W_r^T;
 //       router logits, token_topk, gates, per-workgroup expert histogram
@@ -1652,6 +1653,17 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
     trace_mark(p, ph, 2);                                            \
   } while (0)
 
+  // A launch enqueued after one that gave up (before moe_step_status reset the
+  // abort word) writes nothing.
+  if (threadIdx.x == 0) meta.flag = __hip_atomic_load(p.ctrl.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (meta.flag != 0u) return;
+  if ((p.flags & 0x40000u) && blockIdx.x == gridDim.x - 1) {
+    // failure-path test: this workgroup waits for a word nothing sets, gives
+    // up, and never arrives at the first barrier
+    if (threadIdx.x == 0) (void)wait_for(p.ctrl, p.ctrl.never, 1u);
+    return;
+  }
   const unsigned skip = p.flags >> 8;
   trace_mark(p, 0, 0);
   if (!(skip & 1u)) phase_route<T, OCC>(p, scratch, meta);

@@ -33,14 +33,17 @@ class MoeLayerStep:
 
     def run(self, x, target, *, tokens_in_update=None, step=1, zero_grad=True, apply=True, dx=None,
             router_bias=None, debug=None, trace=None, stream=None, groups=None, ready_gemm12=False,
-            cooperative=False):
+            cooperative=False, refresh_shadow=False, test_timeout=False):
         """Enqueues one launch.  ``debug`` is an optional dict of preallocated debug tensors
         (router_logits, topk_idx, topk_gate, expert_counts, route_perm).  ``groups`` (selective
         updates) replaces zero_grad/apply/step by per-group settings: a dict with keys
         zero_router, zero_experts, apply_router, apply_experts (bools) and step_router,
         step_experts (ints).  ``ready_gemm12`` replaces the grid barrier between the two
         expert products by per-row-tile readiness counters (same results).  ``cooperative``
-        launches through hipLaunchCooperativeKernel instead of an ordinary launch."""
+        launches through hipLaunchCooperativeKernel instead of an ordinary launch.
+        ``refresh_shadow`` rebuilds the bf16 weight copy from params even when it is
+        current; ``test_timeout`` sets the failure-path test flag (the launch ends
+        with a grid-barrier timeout)."""
         n = 0 if x is None else int(x.shape[0])
         self._check_tensors(n, x, target, dx, router_bias, debug or {}, trace)
         flags = 0
@@ -56,8 +59,10 @@ class MoeLayerStep:
                 flags |= B.MOE_RUN_ZERO_GRAD
             if apply:
                 flags |= B.MOE_RUN_APPLY
-        if not self._shadow_valid:
+        if refresh_shadow or not self._shadow_valid:
             flags |= B.MOE_RUN_REFRESH_SHADOW
+        if test_timeout:
+            flags |= B.MOE_RUN_TEST_TIMEOUT
         if trace is not None:
             flags |= B.MOE_RUN_TRACE
         if ready_gemm12:

@@ -11,15 +11,18 @@ be checked against the pages by eye.  Sources (Latch project pages):
 * "How a training megakernel works", section "One training update": the chain
   rule, the squared-error loss L = 1/2 (y - t)^2 and the plain SGD step of the
   two-weight example (used here for the worked-example pin).
-* same page, "From two weights to 200 million": a router sends each token to two
-  of sixteen small feed-forward networks; AdamW updates the weights from running
-  averages of the gradients and of their squares.
-* same page, "What Latch does", step 1: the layer is built from the operations
-  ``token_topk``, ``route_order`` and ``ragged_mm``; global-norm clipping and
-  AdamW are plain tensor arithmetic applied to the update.
-* same page, step 3: gradients reach the tokens routed through each expert.
-* same page, step 4: FP32 master weights and Adam moments (the storage the
-  oracle reads; it computes in float64).
+* same page, "From two weights to 200 million": each expert layer of the
+  pages' model routes every token to 2 of its 16 expert feed-forward blocks, and
+  the optimizer is AdamW (exponential moving averages of the gradient and of its
+  elementwise square).
+* same page, "What Latch does", step 1: the layer is expressed with the routing
+  and grouped-product operations ``token_topk``, ``route_order`` and
+  ``ragged_mm``; clipping by the global gradient norm and the AdamW step are
+  ordinary tensor expressions handed to the update rule.
+* same page, step 3: each expert's gradient has to flow back to the tokens that
+  were sent to that expert.
+* same page, step 4: master weights and both Adam moments are stored in FP32
+  (the storage the oracle reads; it computes in float64).
 
 The pages do not write the layer's formulas.  The readings adopted where they are
 silent:

@@ -5,10 +5,10 @@ layer's arithmetic.  Both the FP64 oracle (through the tests) and the HIP path
 (through the tests, ``bench.py`` and ``__graft_entry__.smoke``) read the same
 arrays from here, so the two implementations see bit-identical inputs.
 
-Recipe (Latch "How a training megakernel works", "From two weights to 200
-million": a router sends each token to two of sixteen small feed-forward
-networks; the batch shapes 2x1024, 32x1024 and 16 x 8x1024 come from the same
-page's "Many small routed experts" section and the results table):
+Recipe (Latch "How a training megakernel works": in "From two weights to 200
+million" each expert layer routes a token to 2 of 16 expert feed-forward blocks;
+the batch shapes 2x1024, 32x1024 and 16 x 8x1024 come from the same page's
+"Many small routed experts" section and the results table):
 
 * ``numpy.random.default_rng(seed)`` draws, in this order and as float64
   standard normals: x [T,d], t [T,d], W_r [d,E], W1 [E,d,f], W2 [E,f,d].

@@ -55,7 +55,8 @@ def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, rea
             out = run.update(s)
             _check_routing(cfg, inp, out, params[:cfg.d_model * cfg.n_experts].reshape(cfg.d_model, cfg.n_experts))
             ref = oracle_update(cfg, inp, params, m, v, s, out["idx"], clip_norm=clip_norm)
-            errs, bad = compare_update(cfg, out, ref, **tol)
+            errs, bad = compare_update(cfg, out, ref, **tol,
+                                       prev=(params, m, v, s, cfg.clip_norm if clip_norm is None else clip_norm))
             assert not bad, f"step {s}: {bad}: {errs}"
             # the next step starts from the GPU's state so each step is checked on its own
             params, m, v = (a.astype(np.float64) for a in run.state())
@@ -323,7 +324,7 @@ def test_handle_reused_across_token_counts(dtype, wg_per_cu, tmax, d, f, E, k, t
             out = run.update(s)
             _check_routing(cfg, inp, out, params[:d * E].reshape(d, E))
             ref = oracle_update(cfg, inp, params, m, v, s, out["idx"])
-            errs, bad = compare_update(cfg, out, ref, **tol)
+            errs, bad = compare_update(cfg, out, ref, **tol, prev=(params, m, v, s, cfg.clip_norm))
             assert not bad, f"update {s} ({T} tokens): {bad}: {errs}"
             params, m, v = (a.astype(np.float64) for a in run.state())
         if dtype == "f32":
@@ -359,3 +360,104 @@ def test_zipf_16x8x1024_accumulated_full_size():
     cfg = synth.CONFIGS["zipf_16x8x1024"]
     inp = synth.make_inputs(cfg, 0)
     _run_and_compare(cfg, inp, BF16_TOL, steps=1)
+
+
+@pytest.mark.parametrize("wg_per_cu,T", [(1, 16 * 256 + 352), (2, 16 * 512 + 704)])
+def test_routing_exact_ties_bf16_several_tokens_per_lane(wg_per_cu, T):
+    # bf16 activations on the router path that gives each lane several tokens
+    # (at least 16 tokens per workgroup pass): duplicated router columns give
+    # bitwise-equal logits, so the lower expert index must win every tie
+    cfg = synth.small_config(f"ties_bf16_occ{wg_per_cu}", T, 96, 64, 12, 2, "bf16")
+    inp = synth.make_inputs(cfg, 16)
+    pairs = ((1, 3), (0, 5), (7, 11))
+    for lo, hi in pairs:
+        inp.w_router[:, hi] = inp.w_router[:, lo]
+    run = GpuRun(cfg, inp, wg_per_cu=wg_per_cu)
+    try:
+        out = run.update(1)
+        z, idx = out["logits"][0], out["idx"][0]
+        decided = 0
+        for lo, hi in pairs:
+            assert np.array_equal(z[:, lo], z[:, hi]), "duplicated router columns must give equal logits"
+            sel_lo = (idx == lo).any(axis=1)
+            sel_hi = (idx == hi).any(axis=1)
+            assert not np.any(sel_hi & ~sel_lo), "a tied higher index was chosen over the lower one"
+            decided += int(np.sum(sel_lo & ~sel_hi))
+        say(f"  tokens whose choice was decided by an exact tie: {decided}")
+        assert decided > 0
+        _check_routing(cfg, inp, out, inp.w_router.astype(np.float64))
+        params = inp.flat_params().astype(np.float64)
+        ref = oracle_update(cfg, inp, params, np.zeros_like(params), np.zeros_like(params), 1, out["idx"])
+        errs, bad = compare_update(cfg, out, ref, **BF16_TOL,
+                                   prev=(params, np.zeros_like(params), np.zeros_like(params), 1, cfg.clip_norm))
+        assert not bad, f"{bad}: {errs}"
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("wg_per_cu", [1, 2])
+def test_forced_shadow_refresh_is_bit_identical(wg_per_cu):
+    # AdamW writes the bf16 weight copy with the same round-to-nearest-even
+    # conversion that MOE_RUN_REFRESH_SHADOW uses, so forcing a refresh before
+    # the second update must change no bit of any output
+    cfg = synth.small_config("shadow_bf16", 1000, 256, 384, 16, 2, "bf16")
+    inp = synth.make_inputs(cfg, 17)
+    outs = []
+    for force in (False, True):
+        run = GpuRun(cfg, inp, wg_per_cu=wg_per_cu)
+        try:
+            run.update(1)
+            L = run.layer
+            dx = torch.empty(cfg.tokens, cfg.d_model, dtype=torch.float32, device=run.dev)
+            L.run(run.x, run.t, step=2, dx=dx, refresh_shadow=force)
+            L.status()
+            torch.cuda.synchronize()
+            outs.append({"grads": L.grads.cpu().numpy(), "params": L.params.cpu().numpy(),
+                         "exp_avg": L.exp_avg.cpu().numpy(), "exp_avg_sq": L.exp_avg_sq.cpu().numpy(),
+                         "dx": dx.cpu().numpy(), "stats": L.stats.cpu().numpy()})
+        finally:
+            run.close()
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+
+
+@pytest.mark.parametrize("dtype,wg_per_cu", [("f32", 1), ("bf16", 1), ("bf16", 2)])
+def test_barrier_timeout_reported_and_handle_recovers(dtype, wg_per_cu):
+    # The failure-path test flag makes one workgroup give up before the first
+    # grid barrier (a wait on a word nothing sets, bounded at about 10 us), so
+    # every other workgroup's barrier wait gives up as well and all exit.  A
+    # launch enqueued behind it, before moe_step_status, must write nothing; the
+    # status call reports the timeout bit and resets the barrier state; the
+    # next update on the same handle matches the oracle.
+    cfg = synth.small_config(f"timeout_{dtype}", 1000, 256, 384, 16, 2, dtype)
+    inp = synth.make_inputs(cfg, 18)
+    run = GpuRun(cfg, inp, wg_per_cu=wg_per_cu)
+    try:
+        L = run.layer
+        say(f"  [gpu] test-timeout launch, {dtype} wg_per_cu={wg_per_cu}")
+        L.run(run.x, run.t, step=1, test_timeout=True)
+        sentinel = 12345.0
+        L.grads.fill_(sentinel)
+        torch.cuda.synchronize()
+        p_before = L.params.cpu().numpy()
+        dx = torch.full((cfg.tokens, cfg.d_model), sentinel, dtype=torch.float32, device=run.dev)
+        L.run(run.x, run.t, step=1, dx=dx)   # behind the failed launch: must write nothing
+        with pytest.raises(B.MoeStepError) as ei:
+            L.status()
+        assert ei.value.status == B.MOE_ERR_DEVICE
+        assert "grid-barrier timeout" in str(ei.value)
+        torch.cuda.synchronize()
+        assert np.all(L.grads.cpu().numpy() == sentinel)
+        assert np.all(dx.cpu().numpy() == sentinel)
+        assert np.array_equal(L.params.cpu().numpy(), p_before)
+        L.status()   # the state was reset: no error now
+        L.load_params(torch.from_numpy(inp.flat_params()))
+        out = run.update(1)
+        params = inp.flat_params().astype(np.float64)
+        z = np.zeros_like(params)
+        ref = oracle_update(cfg, inp, params, z, z, 1, out["idx"])
+        errs, bad = compare_update(cfg, out, ref, **(BF16_TOL if dtype == "bf16" else F32_TOL),
+                                   prev=(params, z, z, 1, cfg.clip_norm))
+        assert not bad, f"update after the reported timeout: {bad}: {errs}"
+    finally:
+        run.close()
