@@ -223,6 +223,36 @@ int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t 
 int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
                         int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream);
 
+/* Bytes of the static device array behind moe_step_run_static (per GPU). */
+#define MOE_STEP_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  One update
+ * like moe_step_run, with no handle and no allocation of any kind.
+ *   - The arena lives in a static device array of MOE_STEP_STATIC_SCRATCH_BYTES
+ *     (32 MiB) that every GPU the library runs on holds from the library's load
+ *     until the process ends.  cfg is validated as by moe_step_create and its
+ *     max_tokens sizes the arena; a configuration whose arena (about
+ *     moe_step_arena_bytes of a handle with the same cfg, plus 128 KiB of
+ *     barrier words) does not fit is refused with MOE_ERR_SHAPE.
+ *   - Enqueues three launches on hip_stream: a fill kernel that clears the
+ *     barrier words, the update (the same kernel and grid as a handle with the
+ *     same cfg, so the results are bit-identical to moe_step_run), and a
+ *     one-thread kernel that writes the device status bits of the update into
+ *     io->stats[3] (0 = no error, else the MOE_DEVICE_* bits as a float).  The
+ *     three are ordered on the stream only, so the call can be captured.
+ *   - io->stats is required.  The bf16 weight copy is rebuilt from params on
+ *     every call (MOE_RUN_REFRESH_SHADOW is implied), because the array keeps
+ *     whatever the last call on that GPU left in it.  MOE_RUN_SKIP_PHASE is
+ *     refused (there is no previous launch of this caller to reuse).
+ *   - Every call on a GPU shares that GPU's array: calls that overlap on one
+ *     GPU (different streams without an order between them) race and give
+ *     wrong results.
+ *   - Host errors return as from moe_step_run, with the text in
+ *     moe_step_last_error(NULL). */
+int moe_step_run_static(const moe_step_config* cfg, const moe_step_io* io, int32_t n_tokens,
+                        int64_t tokens_in_update, int64_t step, uint32_t run_flags, void* hip_stream);
+
 /* Waits for the handle's last stream and reads the device status word: the
  * numerical check of the launch (non-finite router logits) and the bounded
  * waits of its grid barriers (Latch "How a training megakernel works", "What
@@ -246,7 +276,8 @@ int moe_step_grid_size(moe_step_t h);
  * memory rule of the pages' "Open problems", Generality 2. */
 size_t moe_step_arena_bytes(moe_step_t h);
 
-/* Text of the last error on h (or of the last failed create if h is NULL).
+/* Text of the last error on h (or, if h is NULL, of the last failed create or
+ * moe_step_run_static call on this thread).
  * Valid until the next call on the same handle. Never NULL. */
 const char* moe_step_last_error(moe_step_t h);
 

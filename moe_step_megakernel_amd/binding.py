@@ -28,6 +28,7 @@ def MOE_RUN_SKIP_PHASE(i: int) -> int:
     return 0x100 << i
 
 MOE_DEVICE_BARRIER_TIMEOUT, MOE_DEVICE_NONFINITE_LOGIT, MOE_DEVICE_BAD_ROUTE = 0x1, 0x2, 0x4
+MOE_STEP_STATIC_SCRATCH_BYTES = 32 << 20
 N_PHASES = 8
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_HIP", -4: "MOE_ERR_NOMEM",
@@ -80,6 +81,9 @@ def load_library():
     lib.moe_step_run_groups.argtypes = [ctypes.c_void_p, P(moe_step_io), ctypes.c_int32, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
     lib.moe_step_run_groups.restype = ctypes.c_int
+    lib.moe_step_run_static.argtypes = [P(moe_step_config), P(moe_step_io), ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    lib.moe_step_run_static.restype = ctypes.c_int
     lib.moe_step_status.argtypes = [ctypes.c_void_p]
     lib.moe_step_status.restype = ctypes.c_int
     lib.moe_step_trace_words.argtypes = [ctypes.c_void_p]
@@ -140,6 +144,14 @@ def moe_step_run_groups(handle, io: moe_step_io, n_tokens: int, tokens_in_update
                                             step_experts, run_flags, stream)
     if rc != MOE_OK:
         raise MoeStepError("moe_step_run_groups", rc, moe_step_last_error(handle))
+
+
+def moe_step_run_static(cfg: moe_step_config, io: moe_step_io, n_tokens: int, tokens_in_update: int, step: int,
+                        run_flags: int, stream=None) -> None:
+    rc = load_library().moe_step_run_static(ctypes.byref(cfg), ctypes.byref(io), n_tokens, tokens_in_update, step,
+                                            run_flags, stream)
+    if rc != MOE_OK:
+        raise MoeStepError("moe_step_run_static", rc, moe_step_last_error(None))
 
 
 def moe_step_status(handle) -> None:

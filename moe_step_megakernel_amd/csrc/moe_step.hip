@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe_step.h"
@@ -136,103 +137,49 @@ struct moe_step {
   unsigned* ctrl;
 };
 
-extern "C" {
-
-size_t moe_step_param_count(const moe_step_config* c) {
-  if (!c) return 0;
-  return (size_t)c->d_model * c->n_experts + 2ull * c->n_experts * c->d_model * c->d_ff;
-}
-
-int moe_step_check_config(const moe_step_config* cfg) {
-  char err[512];
-  return check_config(cfg, err);
-}
-
-const char* moe_step_last_error(moe_step_t h) { return h ? h->err : g_create_error; }
-
-int moe_step_grid_size(moe_step_t h) { return h ? h->grid : 0; }
-
-size_t moe_step_arena_bytes(moe_step_t h) { return h ? h->arena_bytes : 0; }
-
-size_t moe_step_trace_words(moe_step_t h) { return h ? (size_t)h->grid * moe::kPhases * 3 : 0; }
-
-int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
-  if (!out) {
-    set_err(g_create_error, "out is NULL");
-    return MOE_ERR_ARG;
-  }
-  *out = nullptr;
-  int rc = check_config(cfg, g_create_error);
-  if (rc != MOE_OK) return rc;
-
-  int ndev = 0;
-  hipError_t he = hipGetDeviceCount(&ndev);
-  if (he != hipSuccess || ndev <= 0) {
-    set_err(g_create_error, "no HIP device (%s)", hipGetErrorString(he));
-    return MOE_ERR_HIP;
-  }
-  if (cfg->device < 0 || cfg->device >= ndev) {
-    set_err(g_create_error, "device %d out of range (%d devices)", cfg->device, ndev);
-    return MOE_ERR_ARG;
-  }
-  if ((he = hipSetDevice(cfg->device)) != hipSuccess) {
-    set_err(g_create_error, "hipSetDevice: %s", hipGetErrorString(he));
-    return MOE_ERR_HIP;
-  }
-  hipDeviceProp_t prop;
-  if ((he = hipGetDeviceProperties(&prop, cfg->device)) != hipSuccess) {
-    set_err(g_create_error, "hipGetDeviceProperties: %s", hipGetErrorString(he));
-    return MOE_ERR_HIP;
-  }
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-    set_err(g_create_error, "device %d is %s; this library is built for gfx950 only", cfg->device,
-            prop.gcnArchName);
-    return MOE_ERR_DEVICE;
-  }
-  if (!prop.cooperativeLaunch) {
-    set_err(g_create_error, "device does not support cooperative launches");
-    return MOE_ERR_DEVICE;
-  }
-
+// Chooses the kernel (element type, workgroups per compute unit), sets its LDS
+// attribute and sizes the persistent grid to what the device holds at once.
+// No allocation.
+static int select_kernel(const moe_step_config& c, int cus, moe_step& h, char* err) {
   // Two workgroups per compute unit pay off once the expert products have
   // many tiles (each workgroup's waits are covered by the other's matrix
   // work); small batches keep one, with the deeper pipeline and fewer
   // workgroups at every grid barrier.  The fp32 kernel is built for one.
-  int want = cfg->wg_per_cu;
-  if (want == 0) want = (cfg->dtype == MOE_DTYPE_BF16 && (long)cfg->max_tokens * cfg->top_k >= kTwoPerCuRows) ? 2 : 1;
-  const int occ = (cfg->dtype == MOE_DTYPE_BF16 && want == 2) ? 2 : 1;
-  const void* kern = cfg->dtype == MOE_DTYPE_F32 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<float, 1>)
-                     : occ == 2                   ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t, 2>)
-                                                  : reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t, 1>);
+  int want = c.wg_per_cu;
+  if (want == 0) want = (c.dtype == MOE_DTYPE_BF16 && (long)c.max_tokens * c.top_k >= kTwoPerCuRows) ? 2 : 1;
+  const int occ = (c.dtype == MOE_DTYPE_BF16 && want == 2) ? 2 : 1;
+  const void* kern = c.dtype == MOE_DTYPE_F32 ? reinterpret_cast<const void*>(&moe::moe_step_kernel<float, 1>)
+                     : occ == 2               ? reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t, 2>)
+                                              : reinterpret_cast<const void*>(&moe::moe_step_kernel<uint16_t, 1>);
   const int smem = moe::smem_bytes(occ);
-  he = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  hipError_t he = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (he != hipSuccess) {
-    set_err(g_create_error, "hipFuncSetAttribute(shared memory %d): %s", smem, hipGetErrorString(he));
+    set_err(err, "hipFuncSetAttribute(shared memory %d): %s", smem, hipGetErrorString(he));
     return MOE_ERR_HIP;
   }
   int per_cu = 0;
   he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, moe::kThreads, smem);
   if (he != hipSuccess || per_cu < 1) {
-    set_err(g_create_error, "occupancy query failed or zero (%s, %d)", hipGetErrorString(he), per_cu);
+    set_err(err, "occupancy query failed or zero (%s, %d)", hipGetErrorString(he), per_cu);
     return MOE_ERR_HIP;
   }
-  const int use = occ < per_cu ? occ : per_cu;
+  h.cus = cus;
+  h.grid = cus * (occ < per_cu ? occ : per_cu);
+  h.occ = occ;
+  h.kern = kern;
+  h.smem = smem;
+  return MOE_OK;
+}
 
-  moe_step* h = new (std::nothrow) moe_step();
-  if (!h) {
-    set_err(g_create_error, "host allocation failed");
-    return MOE_ERR_NOMEM;
-  }
-  h->cfg = *cfg;
-  h->cus = prop.multiProcessorCount;
-  h->grid = h->cus * use;
-  h->occ = occ;
-  h->kern = kern;
-  h->smem = smem;
-
-  const int d = cfg->d_model, f = cfg->d_ff, E = cfg->n_experts, k = cfg->top_k;
-  const size_t Tm = (size_t)cfg->max_tokens, N = Tm * k;
-  const size_t es = cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+// Lays out the arena of h (h.cfg and h.grid set) and returns its size in
+// bytes; with a base address, also points h's sub-buffers into it.  The
+// barrier words (ctrl_words of them) come first and the 256-byte zero page
+// right after them.
+static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
+  const moe_step_config& c = h.cfg;
+  const int d = c.d_model, f = c.d_ff, E = c.n_experts, k = c.top_k;
+  const size_t Tm = (size_t)c.max_tokens, N = Tm * k;
+  const size_t es = c.dtype == MOE_DTYPE_BF16 ? 2 : 4;
   const int n10 = E * cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
   const int n11 = E * cdiv(d, moe::gemm::BM) * cdiv(f, moe::gemm::BN);
   const int nrr = cdiv(d * E, moe::kThreads);
@@ -242,23 +189,21 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   // largest token count of each range (clipped to max_tokens) gives the bound.
   size_t rch = 1;
   {
-    const int m = cdiv(h->grid, cdiv(d, moe::kThreads));
-    const int cand[3] = {cfg->max_tokens, std::min(cfg->max_tokens, 128 * (m - 1)),
-                         std::min(cfg->max_tokens, 64 * (m - 1))};
+    const int m = cdiv(h.grid, cdiv(d, moe::kThreads));
+    const int cand[3] = {c.max_tokens, std::min(c.max_tokens, 128 * (m - 1)), std::min(c.max_tokens, 64 * (m - 1))};
     for (int t : cand)
-      if (t >= 1) rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h->grid)));
+      if (t >= 1) rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h.grid)));
   }
-
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = align_up(off + (bytes ? bytes : 1), 256);
     return o;
   };
-  const size_t ctrl_words = (size_t)(h->grid + 4) * 32;
   const size_t o_ctrl = take(ctrl_words * sizeof(unsigned));
+  const size_t o_zero = take(256);
   const size_t o_idx = take(N * 4), o_gate = take(N * 4), o_dz = take(N * 4);
-  const size_t o_hist = take((size_t)h->grid * E * 4);
+  const size_t o_hist = take((size_t)h.grid * E * 4);
   const size_t o_perm = take(N * 4), o_inv = take(N * 4);
   // Stored activations share memory where their lifetimes (phases between the
   // grid barriers) do not overlap:
@@ -271,11 +216,10 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const size_t o_gp = take(N * f * es), o_dout = take(N * d * es);
   const size_t o_wrt = take((size_t)E * d * 4);
   const size_t o_rpart = take(rch * E * d * 4);
-  const size_t o_loss = take((size_t)h->grid * 4);
+  const size_t o_loss = take((size_t)h.grid * 4);
   const size_t o_norm = take((size_t)(n10 + n11 + nrr) * 4);
-  const size_t o_shadow = cfg->dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
-  const size_t o_xs = cfg->dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
-  const size_t o_zero = take(256);
+  const size_t o_shadow = c.dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
+  const size_t o_xs = c.dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
   // partial weight-gradient tiles of split contractions (skewed routing): at most
   // E/2 extra chunks over all experts, each a 128 x 128 fp32 tile per gradient tile
   const size_t wtiles = (size_t)cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
@@ -283,79 +227,118 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
   const size_t o_wpart1 = take(((size_t)E / 2 + 1) * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
   const int nrb = (int)((N + moe::gemm::BM - 1) / moe::gemm::BM) + E;   // row tiles of GEMM 1 (upper bound)
   const size_t o_ready = take((size_t)nrb * 4);
-  h->arena_bytes = off;
-
-  he = hipMalloc(reinterpret_cast<void**>(&h->arena), h->arena_bytes);
-  if (he != hipSuccess) {
-    set_err(g_create_error, "hipMalloc(%zu bytes): %s", h->arena_bytes, hipGetErrorString(he));
-    delete h;
-    return MOE_ERR_NOMEM;
+  if (base) {
+    char* a = base;
+    h.ctrl = reinterpret_cast<unsigned*>(a + o_ctrl);
+    h.zero = a + o_zero;
+    h.idx = reinterpret_cast<int*>(a + o_idx);
+    h.gate = reinterpret_cast<float*>(a + o_gate);
+    h.dzsel = reinterpret_cast<float*>(a + o_dz);
+    h.hist = reinterpret_cast<int*>(a + o_hist);
+    h.ready = reinterpret_cast<int*>(a + o_ready);
+    h.nrb = nrb;
+    h.perm = reinterpret_cast<int*>(a + o_perm);
+    h.inv = reinterpret_cast<int*>(a + o_inv);
+    h.act = a + o_act_dxs;
+    h.gp = a + o_gp;
+    h.out = reinterpret_cast<float*>(a + o_out_dh);
+    h.dout = a + o_dout;
+    h.dh = a + o_out_dh;
+    h.dxs = a + o_act_dxs;
+    h.wrt = reinterpret_cast<float*>(a + o_wrt);
+    h.rpart = reinterpret_cast<float*>(a + o_rpart);
+    h.loss_part = reinterpret_cast<float*>(a + o_loss);
+    h.norm_part = reinterpret_cast<float*>(a + o_norm);
+    h.shadow = c.dtype == MOE_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a + o_shadow) : nullptr;
+    h.xs = c.dtype == MOE_DTYPE_BF16 ? a + o_xs : nullptr;
+    h.wpart2 = reinterpret_cast<float*>(a + o_wpart2);
+    h.wpart1 = reinterpret_cast<float*>(a + o_wpart1);
   }
-  char* a = h->arena;
-  h->ctrl = reinterpret_cast<unsigned*>(a + o_ctrl);
-  h->idx = reinterpret_cast<int*>(a + o_idx);
-  h->gate = reinterpret_cast<float*>(a + o_gate);
-  h->dzsel = reinterpret_cast<float*>(a + o_dz);
-  h->hist = reinterpret_cast<int*>(a + o_hist);
-  h->ready = reinterpret_cast<int*>(a + o_ready);
-  h->nrb = nrb;
-  h->perm = reinterpret_cast<int*>(a + o_perm);
-  h->inv = reinterpret_cast<int*>(a + o_inv);
-  h->act = a + o_act_dxs;
-  h->gp = a + o_gp;
-  h->out = reinterpret_cast<float*>(a + o_out_dh);
-  h->dout = a + o_dout;
-  h->dh = a + o_out_dh;
-  h->dxs = a + o_act_dxs;
-  h->wrt = reinterpret_cast<float*>(a + o_wrt);
-  h->rpart = reinterpret_cast<float*>(a + o_rpart);
-  h->loss_part = reinterpret_cast<float*>(a + o_loss);
-  h->norm_part = reinterpret_cast<float*>(a + o_norm);
-  h->shadow = cfg->dtype == MOE_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a + o_shadow) : nullptr;
-  h->xs = cfg->dtype == MOE_DTYPE_BF16 ? a + o_xs : nullptr;
-  h->wpart2 = reinterpret_cast<float*>(a + o_wpart2);
-  h->wpart1 = reinterpret_cast<float*>(a + o_wpart1);
-  h->zero = a + o_zero;
+  return off;
+}
 
-  // the arena starts zeroed (every stored index is then in range) and so do
-  // the barrier words and status (synchronous; not part of any run)
-  he = hipMemset(h->arena, 0, h->arena_bytes);
-  if (he == hipSuccess) he = hipDeviceSynchronize();
-  if (he != hipSuccess) {
-    set_err(g_create_error, "clearing barrier words: %s", hipGetErrorString(he));
-    (void)hipFree(h->arena);
-    delete h;
-    return MOE_ERR_HIP;
+// ---------------------------------------------------------------------------
+// The arena of the allocation-free entry point: a static device array (each
+// GPU the library runs on holds its own copy until the process ends).  The
+// barrier words (for grids of up to 1020 workgroups) and the zero page sit at
+// fixed offsets at its start, so no other call's buffers overlap them.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MOE_STEP_STATIC_SCRATCH_BYTES];
+constexpr size_t kStaticCtrlWords = 1024 * 32;
+
+// Before a static-arena launch: the barrier words, status and abort word of
+// the previous call are cleared and the zero page is zeroed (a fill kernel,
+// so the call stays one stream-ordered sequence of launches).
+__global__ void static_clear(unsigned* ctrl, int words, uint32_t* zero) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) ctrl[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < 64) zero[threadIdx.x] = 0u;
+}
+
+// After it: the device status bits of the launch into stats[3].
+__global__ void static_report(const unsigned* status, float* stats) {
+  if (threadIdx.x == 0) stats[3] = (float)*status;
+}
+
+struct StaticDevice {
+  bool ready = false;
+  char* ptr = nullptr;   // device address of this GPU's copy of `scratch`
+  int cus = 0;
+};
+static std::mutex g_static_mu;
+static StaticDevice g_static[64];
+
+// Once per device, with that device current: the device address of its copy
+// of the scratch array, its compute-unit count and architecture.
+static int static_setup(int dev, char* err, StaticDevice** out) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDevice& sd = g_static[dev];
+  if (!sd.ready) {
+    hipDeviceProp_t prop;
+    hipError_t he = hipGetDeviceProperties(&prop, dev);
+    if (he != hipSuccess) {
+      set_err(err, "hipGetDeviceProperties: %s", hipGetErrorString(he));
+      return MOE_ERR_HIP;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      set_err(err, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+      return MOE_ERR_DEVICE;
+    }
+    void* ptr = nullptr;
+    he = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (he != hipSuccess || !ptr) {
+      set_err(err, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(he));
+      return MOE_ERR_HIP;
+    }
+    sd.ptr = static_cast<char*>(ptr);
+    sd.cus = prop.multiProcessorCount;
+    sd.ready = true;
   }
-  *out = h;
+  *out = &sd;
   return MOE_OK;
 }
 
-int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update, int64_t step,
-                 uint32_t run_flags, void* hip_stream) {
-  return moe_step_run_groups(h, io, n_tokens, tokens_in_update, step, step, run_flags, hip_stream);
-}
-
-int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
-                        int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream) {
-  if (!h) return MOE_ERR_ARG;
+// Validates one launch's arguments (text into err) and enqueues the persistent
+// kernel with h's arena.  Shared by the handle and static entry points.
+static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
+                    int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream,
+                    bool static_arena = false) {
   if (!io) {
-    set_err(h->err, "io is NULL");
+    set_err(err, "io is NULL");
     return MOE_ERR_ARG;
   }
   const moe_step_config& c = h->cfg;
   if (n_tokens < 0 || n_tokens > c.max_tokens) {
-    set_err(h->err, "n_tokens %d outside [0, max_tokens=%d]", n_tokens, c.max_tokens);
+    set_err(err, "n_tokens %d outside [0, max_tokens=%d]", n_tokens, c.max_tokens);
     return MOE_ERR_ARG;
   }
   if (tokens_in_update < 1 || tokens_in_update < n_tokens) {
-    set_err(h->err, "tokens_in_update %lld must be >= max(1, n_tokens)", (long long)tokens_in_update);
+    set_err(err, "tokens_in_update %lld must be >= max(1, n_tokens)", (long long)tokens_in_update);
     return MOE_ERR_ARG;
   }
   if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK |
                     MOE_RUN_ZERO_GRAD_ROUTER | MOE_RUN_ZERO_GRAD_EXPERTS | MOE_RUN_APPLY_ROUTER |
                     MOE_RUN_APPLY_EXPERTS | MOE_RUN_READY_GEMM12 | MOE_RUN_COOPERATIVE | MOE_RUN_TEST_TIMEOUT)) {
-    set_err(h->err, "unknown run flags 0x%x", run_flags);
+    set_err(err, "unknown run flags 0x%x", run_flags);
     return MOE_ERR_ARG;
   }
   // the whole-update bits stand for both groups
@@ -364,29 +347,29 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   run_flags &= ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY);
   const bool apply_r = (run_flags & MOE_RUN_APPLY_ROUTER) != 0u, apply_e = (run_flags & MOE_RUN_APPLY_EXPERTS) != 0u;
   if ((run_flags & MOE_RUN_SKIP_MASK) && h->last_full_tokens != n_tokens) {
-    set_err(h->err, "skipping phases needs a previous full launch with the same n_tokens (%d, last %d)", n_tokens,
+    set_err(err, "skipping phases needs a previous full launch with the same n_tokens (%d, last %d)", n_tokens,
             h->last_full_tokens);
     return MOE_ERR_STATE;
   }
   if ((apply_r && step_router < 1) || (apply_e && step_experts < 1)) {
-    set_err(h->err, "the AdamW step of an applied group must be >= 1 (router %lld, experts %lld)",
+    set_err(err, "the AdamW step of an applied group must be >= 1 (router %lld, experts %lld)",
             (long long)step_router, (long long)step_experts);
     return MOE_ERR_ARG;
   }
   if (n_tokens > 0 && (!io->x || !io->target)) {
-    set_err(h->err, "x and target are required");
+    set_err(err, "x and target are required");
     return MOE_ERR_ARG;
   }
   if (!io->params || !io->grads) {
-    set_err(h->err, "params and grads are required");
+    set_err(err, "params and grads are required");
     return MOE_ERR_ARG;
   }
   if ((apply_r || apply_e) && (!io->exp_avg || !io->exp_avg_sq)) {
-    set_err(h->err, "exp_avg and exp_avg_sq are required with MOE_RUN_APPLY");
+    set_err(err, "exp_avg and exp_avg_sq are required with MOE_RUN_APPLY");
     return MOE_ERR_ARG;
   }
   if ((run_flags & MOE_RUN_TRACE) && !io->trace) {
-    set_err(h->err, "MOE_RUN_TRACE needs io.trace");
+    set_err(err, "MOE_RUN_TRACE needs io.trace");
     return MOE_ERR_ARG;
   }
   const uintptr_t mis = reinterpret_cast<uintptr_t>(io->x) | reinterpret_cast<uintptr_t>(io->target) |
@@ -394,7 +377,7 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
                         reinterpret_cast<uintptr_t>(io->exp_avg) | reinterpret_cast<uintptr_t>(io->exp_avg_sq) |
                         reinterpret_cast<uintptr_t>(io->dx);
   if (mis & 15u) {
-    set_err(h->err, "x, target, params, grads, exp_avg, exp_avg_sq and dx must be 16-byte aligned");
+    set_err(err, "x, target, params, grads, exp_avg, exp_avg_sq and dx must be 16-byte aligned");
     return MOE_ERR_ARG;
   }
 
@@ -472,7 +455,7 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
 
   hipError_t he = hipSetDevice(c.device);
   if (he != hipSuccess) {
-    set_err(h->err, "hipSetDevice: %s", hipGetErrorString(he));
+    set_err(err, "hipSetDevice: %s", hipGetErrorString(he));
     return MOE_ERR_HIP;
   }
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
@@ -481,17 +464,185 @@ int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, i
   // makes it resident on an otherwise idle device; the cooperative launch
   // guarantees it but costs about 19 us more per update.
   const bool coop = (run_flags & MOE_RUN_COOPERATIVE) != 0u;
+  if (static_arena) {
+    hipLaunchKernelGGL(static_clear, dim3(16), dim3(256), 0, stream, h->ctrl, (h->grid + 4) * 32,
+                       reinterpret_cast<uint32_t*>(h->zero));
+    if ((he = hipGetLastError()) != hipSuccess) {
+      set_err(err, "clearing the barrier words: %s", hipGetErrorString(he));
+      return MOE_ERR_HIP;
+    }
+  }
   he = coop ? hipLaunchCooperativeKernel(h->kern, dim3(h->grid), dim3(moe::kThreads), args, h->smem, stream)
             : hipLaunchKernel(h->kern, dim3(h->grid), dim3(moe::kThreads), args, h->smem, stream);
   if (he != hipSuccess) {
-    set_err(h->err, "%s: %s", coop ? "hipLaunchCooperativeKernel" : "hipLaunchKernel", hipGetErrorString(he));
+    set_err(err, "%s: %s", coop ? "hipLaunchCooperativeKernel" : "hipLaunchKernel", hipGetErrorString(he));
     return MOE_ERR_HIP;
+  }
+  if (static_arena) {
+    hipLaunchKernelGGL(static_report, dim3(1), dim3(64), 0, stream, h->ctrl + 32, io->stats);
+    if ((he = hipGetLastError()) != hipSuccess) {
+      set_err(err, "reporting the device status: %s", hipGetErrorString(he));
+      return MOE_ERR_HIP;
+    }
   }
   h->last_stream = stream;
   h->launched = true;
   if (run_flags & MOE_RUN_TEST_TIMEOUT) h->last_full_tokens = -1;
   else if (!(run_flags & MOE_RUN_SKIP_MASK)) h->last_full_tokens = n_tokens;
   return MOE_OK;
+}
+
+extern "C" {
+
+size_t moe_step_param_count(const moe_step_config* c) {
+  if (!c) return 0;
+  return (size_t)c->d_model * c->n_experts + 2ull * c->n_experts * c->d_model * c->d_ff;
+}
+
+int moe_step_check_config(const moe_step_config* cfg) {
+  char err[512];
+  return check_config(cfg, err);
+}
+
+const char* moe_step_last_error(moe_step_t h) { return h ? h->err : g_create_error; }
+
+int moe_step_grid_size(moe_step_t h) { return h ? h->grid : 0; }
+
+size_t moe_step_arena_bytes(moe_step_t h) { return h ? h->arena_bytes : 0; }
+
+size_t moe_step_trace_words(moe_step_t h) { return h ? (size_t)h->grid * moe::kPhases * 3 : 0; }
+
+int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
+  if (!out) {
+    set_err(g_create_error, "out is NULL");
+    return MOE_ERR_ARG;
+  }
+  *out = nullptr;
+  int rc = check_config(cfg, g_create_error);
+  if (rc != MOE_OK) return rc;
+
+  int ndev = 0;
+  hipError_t he = hipGetDeviceCount(&ndev);
+  if (he != hipSuccess || ndev <= 0) {
+    set_err(g_create_error, "no HIP device (%s)", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  if (cfg->device < 0 || cfg->device >= ndev) {
+    set_err(g_create_error, "device %d out of range (%d devices)", cfg->device, ndev);
+    return MOE_ERR_ARG;
+  }
+  if ((he = hipSetDevice(cfg->device)) != hipSuccess) {
+    set_err(g_create_error, "hipSetDevice: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  hipDeviceProp_t prop;
+  if ((he = hipGetDeviceProperties(&prop, cfg->device)) != hipSuccess) {
+    set_err(g_create_error, "hipGetDeviceProperties: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    set_err(g_create_error, "device %d is %s; this library is built for gfx950 only", cfg->device,
+            prop.gcnArchName);
+    return MOE_ERR_DEVICE;
+  }
+  if (!prop.cooperativeLaunch) {
+    set_err(g_create_error, "device does not support cooperative launches");
+    return MOE_ERR_DEVICE;
+  }
+
+  moe_step* h = new (std::nothrow) moe_step();
+  if (!h) {
+    set_err(g_create_error, "host allocation failed");
+    return MOE_ERR_NOMEM;
+  }
+  h->cfg = *cfg;
+  if ((rc = select_kernel(*cfg, prop.multiProcessorCount, *h, g_create_error)) != MOE_OK) {
+    delete h;
+    return rc;
+  }
+  h->arena_bytes = plan_arena(*h, nullptr, (size_t)(h->grid + 4) * 32);
+
+  he = hipMalloc(reinterpret_cast<void**>(&h->arena), h->arena_bytes);
+  if (he != hipSuccess) {
+    set_err(g_create_error, "hipMalloc(%zu bytes): %s", h->arena_bytes, hipGetErrorString(he));
+    delete h;
+    return MOE_ERR_NOMEM;
+  }
+  plan_arena(*h, h->arena, (size_t)(h->grid + 4) * 32);
+
+  // the arena starts zeroed (every stored index is then in range) and so do
+  // the barrier words and status (synchronous; not part of any run)
+  he = hipMemset(h->arena, 0, h->arena_bytes);
+  if (he == hipSuccess) he = hipDeviceSynchronize();
+  if (he != hipSuccess) {
+    set_err(g_create_error, "clearing barrier words: %s", hipGetErrorString(he));
+    (void)hipFree(h->arena);
+    delete h;
+    return MOE_ERR_HIP;
+  }
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_step_run(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update, int64_t step,
+                 uint32_t run_flags, void* hip_stream) {
+  return moe_step_run_groups(h, io, n_tokens, tokens_in_update, step, step, run_flags, hip_stream);
+}
+
+int moe_step_run_groups(moe_step_t h, const moe_step_io* io, int32_t n_tokens, int64_t tokens_in_update,
+                        int64_t step_router, int64_t step_experts, uint32_t run_flags, void* hip_stream) {
+  if (!h) return MOE_ERR_ARG;
+  return run_impl(h, h->err, io, n_tokens, tokens_in_update, step_router, step_experts, run_flags, hip_stream);
+}
+
+int moe_step_run_static(const moe_step_config* cfg, const moe_step_io* io, int32_t n_tokens,
+                        int64_t tokens_in_update, int64_t step, uint32_t run_flags, void* hip_stream) {
+  char* err = g_create_error;
+  int rc = check_config(cfg, err);
+  if (rc != MOE_OK) return rc;
+  if (!io || !io->stats) {
+    set_err(err, "io and io->stats are required (stats[3] receives the device status)");
+    return MOE_ERR_ARG;
+  }
+  if (run_flags & MOE_RUN_SKIP_MASK) {
+    set_err(err, "phase skipping needs a handle (it reuses the previous launch's arena)");
+    return MOE_ERR_ARG;
+  }
+  int ndev = 0;
+  hipError_t he = hipGetDeviceCount(&ndev);
+  if (he != hipSuccess || ndev <= 0) {
+    set_err(err, "no HIP device (%s)", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  if (cfg->device < 0 || cfg->device >= ndev || cfg->device >= 64) {
+    set_err(err, "device %d out of range (%d devices)", cfg->device, ndev);
+    return MOE_ERR_ARG;
+  }
+  if ((he = hipSetDevice(cfg->device)) != hipSuccess) {
+    set_err(err, "hipSetDevice: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  StaticDevice* sd = nullptr;
+  if ((rc = static_setup(cfg->device, err, &sd)) != MOE_OK) return rc;
+  moe_step h;   // on the stack: the handle state of this one call
+  h.cfg = *cfg;
+  if ((rc = select_kernel(*cfg, sd->cus, h, err)) != MOE_OK) return rc;
+  if ((size_t)(h.grid + 4) * 32 > kStaticCtrlWords) {
+    set_err(err, "grid of %d workgroups exceeds the static barrier words", h.grid);
+    return MOE_ERR_SHAPE;
+  }
+  const size_t need = plan_arena(h, nullptr, kStaticCtrlWords);
+  if (need > (size_t)MOE_STEP_STATIC_SCRATCH_BYTES) {
+    set_err(err, "this configuration needs %zu bytes of arena; the static scratch holds %zu", need,
+            (size_t)MOE_STEP_STATIC_SCRATCH_BYTES);
+    return MOE_ERR_SHAPE;
+  }
+  plan_arena(h, sd->ptr, kStaticCtrlWords);
+  h.arena_bytes = need;
+  // the array is shared by every call on this GPU, so the bf16 weight copy is
+  // always rebuilt from params
+  return run_impl(&h, err, io, n_tokens, tokens_in_update, step, step, run_flags | MOE_RUN_REFRESH_SHADOW,
+                  hip_stream, true);
 }
 
 int moe_step_status(moe_step_t h) {

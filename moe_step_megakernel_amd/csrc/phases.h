@@ -1640,7 +1640,7 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   constexpr int NS = dma_stages(OCC);
   extern __shared__ __align__(16) char smem_raw[];
   Meta& meta = *reinterpret_cast<Meta*>(smem_raw);
-  char* scratch = smem_raw + kMetaBytes;
+  char* work = smem_raw + kMetaBytes;   // LDS after the routing metadata
   // the host has expanded the whole-update bits into the per-group ones
   const bool zero_r = (p.flags & 0x10u) != 0u, zero_e = (p.flags & 0x20u) != 0u;
   const bool apply_r = (p.flags & 0x40u) != 0u, apply_e = (p.flags & 0x80u) != 0u;
@@ -1666,14 +1666,14 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   }
   const unsigned skip = p.flags >> 8;
   trace_mark(p, 0, 0);
-  if (!(skip & 1u)) phase_route<T, OCC>(p, scratch, meta);
+  if (!(skip & 1u)) phase_route<T, OCC>(p, work, meta);
   MOE_SYNC(0);
   trace_mark(p, 1, 0);
-  phase_order<T>(p, scratch, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
+  phase_order<T>(p, work, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
   MOE_SYNC(1);
   trace_mark(p, 2, 0);
   const bool ready12 = (p.flags & 0x10000u) != 0u;
-  if (!(skip & 4u)) phase_ffn1<T, NS>(p, scratch, meta, ready12);
+  if (!(skip & 4u)) phase_ffn1<T, NS>(p, work, meta, ready12);
   if (ready12) {   // readiness counters instead of a grid barrier
     trace_mark(p, 2, 1);
     trace_mark(p, 2, 2);
@@ -1681,16 +1681,16 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
     MOE_SYNC(2);
   }
   trace_mark(p, 3, 0);
-  if (!(skip & 8u) && !phase_ffn2<T, NS>(p, scratch, meta, ready12 && !(skip & 4u))) return;
+  if (!(skip & 8u) && !phase_ffn2<T, NS>(p, work, meta, ready12 && !(skip & 4u))) return;
   MOE_SYNC(3);
   trace_mark(p, 4, 0);
   if (!(skip & 16u)) phase_combine<T, OCC>(p, meta);
   MOE_SYNC(4);
   trace_mark(p, 5, 0);
-  if (!(skip & 32u)) phase_bwd2<T, NS>(p, scratch, meta, zero_e);
+  if (!(skip & 32u)) phase_bwd2<T, NS>(p, work, meta, zero_e);
   MOE_SYNC(5);
   trace_mark(p, 6, 0);
-  if (!(skip & 64u)) phase_bwd1<T, NS>(p, scratch, meta, zero_r, zero_e, want_dx, !(skip & 32u));
+  if (!(skip & 64u)) phase_bwd1<T, NS>(p, work, meta, zero_r, zero_e, want_dx, !(skip & 32u));
   MOE_SYNC(6);
   if (meta.nsplit > 0 && !(skip & 64u)) {
     // complete the dW1 tiles whose contraction was split, so the global norm
@@ -1709,7 +1709,7 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
     if (!grid_barrier(p.ctrl, p.epoch * 8u + 8u, &meta.flag)) return;
   }
   trace_mark(p, 7, 0);
-  if (!(skip & 128u)) phase_final<T, OCC>(p, scratch, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
+  if (!(skip & 128u)) phase_final<T, OCC>(p, work, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
   __syncthreads();
   trace_mark(p, 7, 1);
   trace_mark(p, 7, 2);
