@@ -208,6 +208,8 @@ def main(argv=None):
                     help="launch through hipLaunchCooperativeKernel instead of an ordinary launch")
     ap.add_argument("--ready-gemm12", action="store_true",
                     help="per-row-tile readiness counters instead of the grid barrier between the expert products")
+    ap.add_argument("--recompute", action="store_true",
+                    help="memory rule: store H only and recompute gelu(H) / gelu'(H) where they are read")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
@@ -234,7 +236,8 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     layer = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.tokens, cfg.dtype, lr=cfg.lr,
                          beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.eps, weight_decay=cfg.weight_decay,
-                         clip_norm=cfg.clip_norm, wg_per_cu=args.wg_per_cu)
+                         clip_norm=cfg.clip_norm, wg_per_cu=args.wg_per_cu,
+                         memory_rules=1 if args.recompute else 0)
     layer.load_params(torch.from_numpy(inp.flat_params()))
 
     def tok(a, bits):
@@ -371,7 +374,8 @@ def main(argv=None):
                                f"d_model={cfg.d_model}, d_ff={cfg.d_ff}, E={cfg.n_experts}, top-{cfg.top_k}",
                    "tokens_per_update": cfg.tokens_in_update, "global_batch": cfg.tokens_in_update,
                    "seq_len": 1024, "parallelism": "single-gpu",
-                   **({"ready_gemm12": True} if args.ready_gemm12 else {})},
+                   **({"ready_gemm12": True} if args.ready_gemm12 else {}),
+                   **({"memory_rules": "recompute"} if args.recompute else {})},
         "ms_per_update_median": float(np.median(upd_ms)), "ms_per_update_p10": float(np.percentile(upd_ms, 10)),
         "ms_per_update_p90": float(np.percentile(upd_ms, 90)),
         "ms_per_update_fresh_median": float(np.median(fresh_ms)),

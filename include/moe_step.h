@@ -93,7 +93,18 @@ typedef struct {
                              router dot products over lanes and the loss's
                              per-workgroup partial sums follow the workgroup
                              count. */
+  uint32_t memory_rules;  /* opt-in rules that trade time for arena memory (the
+                             pages' "Open problems", Generality 2); 0 = none.
+                             MOE_MEM_RECOMPUTE: of the first expert product only
+                             H = x W1 is stored; gelu(H) is recomputed on the
+                             operand fragments of the second product and of the
+                             dW2 product, gelu'(H) in the dH epilogue.  The arena
+                             loses one [tokens * top_k, d_ff] tensor; the update
+                             is slower (each H element passes through GELU once
+                             per output column tile that reads it). */
 } moe_step_config;
+
+#define MOE_MEM_RECOMPUTE 0x1u
 
 /* Buffers of one launch.  Shapes use T = n_tokens, P = moe_step_param_count. */
 typedef struct {

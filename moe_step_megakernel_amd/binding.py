@@ -29,6 +29,7 @@ def MOE_RUN_SKIP_PHASE(i: int) -> int:
 
 MOE_DEVICE_BARRIER_TIMEOUT, MOE_DEVICE_NONFINITE_LOGIT, MOE_DEVICE_BAD_ROUTE = 0x1, 0x2, 0x4
 MOE_STEP_STATIC_SCRATCH_BYTES = 32 << 20
+MOE_MEM_RECOMPUTE = 0x1
 N_PHASES = 8
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_HIP", -4: "MOE_ERR_NOMEM",
@@ -42,7 +43,7 @@ class moe_step_config(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
         ("adam_eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("clip_norm", ctypes.c_double),
-        ("device", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32),
+        ("device", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32), ("memory_rules", ctypes.c_uint32),
     ]
 
 
@@ -101,11 +102,12 @@ def load_library():
 
 
 def make_config(d_model, d_ff, n_experts, top_k, max_tokens, dtype="bf16", lr=1e-3, beta1=0.9, beta2=0.999,
-                adam_eps=1e-8, weight_decay=0.01, clip_norm=1.0, device=0, wg_per_cu=0) -> moe_step_config:
+                adam_eps=1e-8, weight_decay=0.01, clip_norm=1.0, device=0, wg_per_cu=0,
+                memory_rules=0) -> moe_step_config:
     return moe_step_config(
         ctypes.sizeof(moe_step_config), MOE_STEP_ABI_VERSION, d_model, d_ff, n_experts, top_k, max_tokens,
         MOE_DTYPE_BF16 if dtype == "bf16" else MOE_DTYPE_F32, lr, beta1, beta2, adam_eps, weight_decay,
-        clip_norm, device, wg_per_cu)
+        clip_norm, device, wg_per_cu, memory_rules)
 
 
 # --- the C entry points, same names -------------------------------------------------------------

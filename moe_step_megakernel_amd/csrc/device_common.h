@@ -180,14 +180,26 @@ constexpr float kSqrt2OverPi = 0.7978845608028654f;
 constexpr float kGeluCubic = 0.044715f;
 constexpr float kTwoLog2e = 2.8853900817779268f;   // 2 / ln 2
 
-__device__ __forceinline__ void gelu_and_grad(float h, float& a, float& da) {
-  const float h2 = h * h;
+// r and 1 - r = e^{2u} r of the identity above
+__device__ __forceinline__ void gelu_parts(float h, float h2, float& r, float& s) {
   const float t = fminf(kTwoLog2e * kSqrt2OverPi * h * (1.f + kGeluCubic * h2), 64.f);   // 2u log2(e)
   const float e = __builtin_amdgcn_exp2f(t);
-  const float r = __builtin_amdgcn_rcpf(1.f + e);
-  const float s = e * r;   // 1 - r
+  r = __builtin_amdgcn_rcpf(1.f + e);
+  s = e * r;   // 1 - r
+}
+
+__device__ __forceinline__ void gelu_and_grad(float h, float& a, float& da) {
+  const float h2 = h * h;
+  float r, s;
+  gelu_parts(h, h2, r, s);
   a = h * s;
   da = s + 2.f * kSqrt2OverPi * h * r * s * (1.f + 3.f * kGeluCubic * h2);
+}
+
+__device__ __forceinline__ float gelu_only(float h) {
+  float r, s;
+  gelu_parts(h, h * h, r, s);
+  return h * s;
 }
 
 // ---------------------------------------------------------------------------

@@ -53,6 +53,10 @@ int check_config(const moe_step_config* c, char* err) {
     set_err(err, "optimizer hyper-parameters out of range");
     return MOE_ERR_ARG;
   }
+  if (c->memory_rules & ~MOE_MEM_RECOMPUTE) {
+    set_err(err, "unknown memory rules 0x%x", c->memory_rules);
+    return MOE_ERR_ARG;
+  }
   if (c->wg_per_cu < 0 || c->wg_per_cu > 2) {
     set_err(err, "wg_per_cu must be 0, 1 or 2");
     return MOE_ERR_ARG;
@@ -213,7 +217,9 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
   //   dXs [N, d]:     written by the dX tiles after that phase's barrier.
   const size_t o_out_dh = take(std::max(N * d * 4, N * f * es));
   const size_t o_act_dxs = take(std::max(N * f * es, N * d * es));
-  const size_t o_gp = take(N * f * es), o_dout = take(N * d * es);
+  // G' [N, f]: not kept under the recomputation rule (the dH epilogue forms it from H)
+  const bool recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) != 0u;
+  const size_t o_gp = take(recompute ? 0 : N * f * es), o_dout = take(N * d * es);
   const size_t o_wrt = take((size_t)E * d * 4);
   const size_t o_rpart = take(rch * E * d * 4);
   const size_t o_loss = take((size_t)h.grid * 4);
@@ -240,7 +246,7 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
     h.perm = reinterpret_cast<int*>(a + o_perm);
     h.inv = reinterpret_cast<int*>(a + o_inv);
     h.act = a + o_act_dxs;
-    h.gp = a + o_gp;
+    h.gp = recompute ? a + o_act_dxs : a + o_gp;   // never read under the rule
     h.out = reinterpret_cast<float*>(a + o_out_dh);
     h.dout = a + o_dout;
     h.dh = a + o_out_dh;
@@ -452,6 +458,7 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.ctrl.never = h->ctrl + 96;
   p.ctrl.limit = (run_flags & MOE_RUN_TEST_TIMEOUT) ? moe::kTestTimeoutTicks : moe::kBarrierTimeoutTicks;
   p.epoch = ++h->epoch;
+  p.recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) ? 1 : 0;
 
   hipError_t he = hipSetDevice(c.device);
   if (he != hipSuccess) {

@@ -105,7 +105,7 @@ int run_copy(int mib, int steps) {
 int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024";
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
-  bool ready = false, coop = false;
+  bool ready = false, coop = false, recompute = false;
   std::vector<unsigned> skips{0u};
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -134,6 +134,7 @@ int main(int argc, char** argv) {
     else if (a == "--wg-per-cu") wg_per_cu = std::atoi(next());
     else if (a == "--ready") ready = true;
     else if (a == "--coop") coop = true;
+    else if (a == "--recompute") recompute = true;
     else {
       std::fprintf(stderr, "unknown argument %s\n", a.c_str());
       return 1;
@@ -165,6 +166,7 @@ int main(int argc, char** argv) {
   cfg.weight_decay = 0.01;
   cfg.clip_norm = 1.0;
   cfg.wg_per_cu = wg_per_cu;
+  cfg.memory_rules = recompute ? MOE_MEM_RECOMPUTE : 0u;
   moe_step_t h = nullptr;
   if (moe_step_create(&cfg, &h) != MOE_OK) {
     std::fprintf(stderr, "moe_step_create: %s\n", moe_step_last_error(nullptr));

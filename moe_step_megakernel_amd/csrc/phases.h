@@ -75,6 +75,7 @@ struct KParams {
   float lr, beta1, beta2, omb1, omb2, eps, wd, clip;
   float inv_bc1[2], inv_sqrt_bc2[2];   // AdamW bias corrections: [0] router, [1] experts
   unsigned epoch;     // launch number on this handle (barrier targets)
+  int recompute;      // memory rule: act holds H (not gelu(H)) and there is no G' buffer
   // caller buffers
   const void* x;
   const void* t;
@@ -100,8 +101,8 @@ struct KParams {
   int nrb;
   int* perm;       // [T*k] sorted position -> flat id
   int* inv;        // [T*k] flat id -> sorted position
-  void* act;       // [N, f] gelu(H)            (T-typed)
-  void* gp;        // [N, f] gelu'(H)           (T-typed)
+  void* act;       // [N, f] gelu(H), or H under the recomputation rule   (T-typed)
+  void* gp;        // [N, f] gelu'(H); unused under the recomputation rule (T-typed)
   float* out;      // [N, d] expert outputs O
   void* dout;      // [N, d] dL/dO              (T-typed)
   void* dh;        // [N, f] dL/dH              (T-typed)
@@ -812,10 +813,17 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
     const int n0 = nt * gemm::BN;
     auto epi = [&](int r, int c, const float (&h)[8]) {
       if (r < mrows && n0 + c < f) {
+        const long o = (long)(p0 + r) * f + n0 + c;
+        if (p.recompute) {   // memory rule: keep H only
+          F8 hv;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) hv.v[q] = h[q];
+          st8x<NS == 2>(act + o, hv);
+          return;
+        }
         F8 a, da;
 #pragma unroll
         for (int q = 0; q < 8; ++q) gelu_and_grad(h[q], a.v[q], da.v[q]);
-        const long o = (long)(p0 + r) * f + n0 + c;
         st8x<NS == 2>(act + o, a);
         st8x<NS == 2>(gp + o, da);
       }
@@ -863,14 +871,17 @@ __device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& me
     gemm::Operand B{reinterpret_cast<const char*>(w2_ptr<T>(p) + (long)e * f * d), d, nullptr, 1, 0, f, d,
                     nt * gemm::BN};
     const int n0 = nt * gemm::BN;
-    gemm::tile<T, NS, false, true>(lds, A, B, f, p.zero, [&](int r, int c, const float (&v)[8]) {
+    auto epi = [&](int r, int c, const float (&v)[8]) {
       if (r < mrows && n0 + c < d) {
         F8 o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) o.v[q] = v[q];
         st8x<NS == 2>(p.out + (long)(p0 + r) * d + n0 + c, o);
       }
-    });
+    };
+    // under the recomputation rule act holds H and the A fragments pass through GELU
+    if (p.recompute) gemm::tile<T, NS, false, true, true>(lds, A, B, f, p.zero, epi);
+    else gemm::tile<T, NS, false, true, false>(lds, A, B, f, p.zero, epi);
   }
   return true;
 }
@@ -1146,7 +1157,7 @@ __device__ __forceinline__ void phase_combine(const KParams& p, Meta& meta) {
 // gradient and its sum of squares into norm_part[nidx]; chunk 0 of a split
 // tile writes or adds likewise but leaves the sum of squares to the fix-up;
 // chunks 1.. write their partial tile into part.
-template <typename T, int NS>
+template <typename T, int NS, bool GA = false>
 __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Meta& meta, const WItem& wi,
                                                  const char* abase, const int* amap, int adiv, int M,
                                                  const char* bbase, int N, int m0, int n0, float* g, float* part,
@@ -1159,7 +1170,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
   gemm::Operand B{bbase, N, nullptr, 1, pe, rows, N, n0};
   if (wi.c > 0) {
     float* pt = part + ((long)(meta.pbase[e] + wi.c - 1) * tpe + wi.t) * (gemm::BM * gemm::BN);
-    gemm::tile<T, NS, true, true>(lds, A, B, rows, p.zero, [&](int r, int c, const float (&v)[8]) {
+    gemm::tile<T, NS, true, true, GA>(lds, A, B, rows, p.zero, [&](int r, int c, const float (&v)[8]) {
       F8 o;
 #pragma unroll
       for (int u = 0; u < 8; ++u) o.v[u] = v[u];
@@ -1168,7 +1179,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
     return;
   }
   float sq = 0.f;
-  gemm::tile<T, NS, true, true>(
+  gemm::tile<T, NS, true, true, GA>(
       lds, A, B, rows, p.zero,
       [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
         if (m0 + r < M && n0 + c < N) {
@@ -1201,7 +1212,8 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
   const int RT = router_chunk_tokens(p.T, d, gridDim.x);
   const int RCH = ceil_div(p.T, RT), CCH = ceil_div(d, kThreads);
   const int nr = RCH * CCH;
-  const T* gp = reinterpret_cast<const T*>(p.gp);
+  // G' as stored, or H (the recomputation rule) from which the epilogue forms it
+  const T* gsrc = reinterpret_cast<const T*>(p.recompute ? p.act : p.gp);
   T* dh = reinterpret_cast<T*>(p.dh);
   float* gw2 = p.grads + (long)d * E + (long)E * d * f;
   const T* x = reinterpret_cast<const T*>(p.x);
@@ -1221,9 +1233,15 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       const WItem wi = d10.item(meta, E, q);
       const int e = wi.e, mt = wi.t / NT10, nt = wi.t % NT10;
       const int m0 = mt * gemm::BM, n0 = nt * gemm::BN;
-      weight_grad_tile<T, NS>(p, lds, meta, wi, reinterpret_cast<const char*>(p.act), nullptr, 1, f,
-                              reinterpret_cast<const char*>(p.dout), d, m0, n0, gw2 + (long)e * f * d, p.wpart2,
-                              MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
+      // under the recomputation rule act holds H: A = gelu(H) on the fragments
+      if (p.recompute)
+        weight_grad_tile<T, NS, true>(p, lds, meta, wi, reinterpret_cast<const char*>(p.act), nullptr, 1, f,
+                                      reinterpret_cast<const char*>(p.dout), d, m0, n0, gw2 + (long)e * f * d,
+                                      p.wpart2, MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
+      else
+        weight_grad_tile<T, NS, false>(p, lds, meta, wi, reinterpret_cast<const char*>(p.act), nullptr, 1, f,
+                                       reinterpret_cast<const char*>(p.dout), d, m0, n0, gw2 + (long)e * f * d,
+                                       p.wpart2, MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
       continue;
     }
     const int item = q < c10 + c9 ? n10 + s9.item(q - c10)
@@ -1245,6 +1263,14 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
           [&](int r, int c, const float (&v)[8], const Raw8<T>& graw) {
             if (r < mrows && n0 + c < f) {
               F8 g8 = cvt8(graw);
+              if (p.recompute) {   // graw holds H: gelu'(H) recomputed here
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                  float a, da;
+                  gelu_and_grad(g8.v[u], a, da);
+                  g8.v[u] = da;
+                }
+              }
 #pragma unroll
               for (int u = 0; u < 8; ++u) g8.v[u] *= v[u];
               st8x<NS == 2>(dh + (long)(p0 + r) * f + n0 + c, g8);
@@ -1252,7 +1278,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
           },
           [&](int r, int c) {
             Raw8<T> graw{};
-            if (r < mrows && n0 + c < f) graw = ldr8(gp + (long)(p0 + r) * f + n0 + c);
+            if (r < mrows && n0 + c < f) graw = ldr8(gsrc + (long)(p0 + r) * f + n0 + c);
             return graw;
           });
     } else {

@@ -179,7 +179,22 @@ struct Stager {
   }
 };
 
-template <typename T, bool MN_A, bool MN_B>
+// GELU applied to the 16 bytes of an A fragment as they come out of LDS (the
+// recomputation rule: the stored tensor is H and the product needs gelu(H)):
+// 8 bf16 values rounded back to bf16, or 4 fp32 values.
+template <typename T>
+__device__ __forceinline__ void gelu_frag(uint4& v) {
+  uint32_t* w = &v.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (sizeof(T) == 2)
+      w[q] = pack_bf16x2(gelu_only(bf16_to_f32(w[q] & 0xffffu)), gelu_only(bf16_to_f32(w[q] >> 16)));
+    else
+      w[q] = __float_as_uint(gelu_only(__uint_as_float(w[q])));
+  }
+}
+
+template <typename T, bool MN_A, bool MN_B, bool GA>
 __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16_t (&acc)[2][2]) {
   using SA = Stager<T, MN_A>;
   using SB = Stager<T, MN_B>;
@@ -192,6 +207,7 @@ __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16
     for (int i = 0; i < 2; ++i) {
       a[i] = SA::frag(As, wm * 64 + i * 32, chunk);
       b[i] = SB::frag(Bs, wn * 64 + i * 32, chunk);
+      if constexpr (GA) gelu_frag<T>(a[i]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -284,7 +300,7 @@ __device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2],
   }
 }
 
-template <typename T, bool MN_A, bool MN_B, class Epi, class Pre>
+template <typename T, bool MN_A, bool MN_B, bool GA, class Epi, class Pre>
 __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi, Pre&& pre) {
   using SA = Stager<T, MN_A>;
   using SB = Stager<T, MN_B>;
@@ -317,7 +333,7 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
         sa.load(A, kt + 1, ra);
         sb.load(B, kt + 1, rb);
       }
-      mma_stage<T, MN_A, MN_B>(cur, cur + A_BYTES, acc);
+      mma_stage<T, MN_A, MN_B, GA>(cur, cur + A_BYTES, acc);
       if (more) {
         SA::store(nxt, ra);
         SB::store(nxt + A_BYTES, rb);
@@ -463,6 +479,15 @@ struct Frags {
   u32x4_t a0, a1, b0, b1;
 };
 
+// GELU on both A fragments of a chunk (bf16, the direct-to-LDS path)
+__device__ __forceinline__ void gelu_a(Frags& f) {
+  uint4 a0 = {f.a0[0], f.a0[1], f.a0[2], f.a0[3]}, a1 = {f.a1[0], f.a1[1], f.a1[2], f.a1[3]};
+  gelu_frag<uint16_t>(a0);
+  gelu_frag<uint16_t>(a1);
+  f.a0 = u32x4_t{a0.x, a0.y, a0.z, a0.w};
+  f.a1 = u32x4_t{a1.x, a1.y, a1.z, a1.w};
+}
+
 __device__ __forceinline__ u32x4_t join(const u32x2_t& lo, const u32x2_t& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
 }
@@ -581,7 +606,7 @@ __device__ __forceinline__ void pipe_mma(const Frags& c, f32x16_t (&acc)[2][2]) 
 // LDS read has at least one block of matrix work to hide behind.  NS = 4 with
 // one workgroup per compute unit; NS = 2 when two workgroups share one (each
 // then has half the LDS, and the other workgroup's work covers the waits).
-template <int NS, bool MN_A, bool MN_B, class Epi, class Pre>
+template <int NS, bool MN_A, bool MN_B, bool GA, class Epi, class Pre>
 __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
                                          Epi&& epi, Pre&& pre) {
   static_assert(NS >= 2 && NS <= 4, "wait_vm covers up to two k-tiles in flight behind the one awaited");
@@ -624,13 +649,22 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
       db.issue(NS - 1, nx + DMA_OP, zero);
     }
     Frags F0, F1, F2, F3;
+    // With GA, the A fragments of each chunk pass through GELU once their
+    // reads have completed (after the wait that covers them) and before the
+    // MFMAs that use them.
     P::template step<false, -1>(F0, F0, acc, fa0[0], fa1[0], fb0[0], fb1[0]);
     P::template step<false, 0>(F1, F1, acc, fa0[1], fa1[1], fb0[1], fb1[1]);
+    if constexpr (GA) gelu_a(F0);
     for (int kt = 0; kt < nk - 1; ++kt) {
       const uint32_t so = (uint32_t)(kt % NS) * DMA_STAGE;
       const uint32_t sn = (uint32_t)((kt + 1) % NS) * DMA_STAGE;
       P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
+      if constexpr (GA) gelu_a(F1);
       P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
+      if constexpr (GA) {
+        gelu_a(F2);
+        gelu_a(F3);
+      }
       // every stage up to min(kt + NS - 1, nk - 1) has all its loads issued
       wait_vm(min(NS - 2, nk - 2 - kt));
       lds_barrier();
@@ -641,12 +675,18 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
       }
       P::template step<true, -1>(F0, F2, acc, fa0[0] + sn, fa1[0] + sn, fb0[0] + sn, fb1[0] + sn);
       P::template step<true, 1>(F1, F3, acc, fa0[1] + sn, fa1[1] + sn, fb0[1] + sn, fb1[1] + sn);
+      if constexpr (GA) gelu_a(F0);
     }
     {
       // last k-tile: its chunks 0 and 1 are in flight or landed
       const uint32_t so = (uint32_t)((nk - 1) % NS) * DMA_STAGE;
       P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
+      if constexpr (GA) gelu_a(F1);
       P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
+      if constexpr (GA) {
+        gelu_a(F2);
+        gelu_a(F3);
+      }
       pipe_mma<MN_A, MN_B>(F2, acc);
       pipe_mma<MN_A, MN_B>(F3, acc);
     }
@@ -663,11 +703,12 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
 
 // One tile: bf16 through the DMA pipeline (NS stages), fp32 through register
 // staging.
-template <typename T, int NS, bool MN_A, bool MN_B, class Epi, class Pre = NoPre>
+// GA: the A operand holds H and the product uses gelu(H) (recomputation rule).
+template <typename T, int NS, bool MN_A, bool MN_B, bool GA = false, class Epi, class Pre = NoPre>
 __device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
                                      Epi&& epi, Pre&& pre = Pre()) {
-  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B>(lds, A, B, K, zero, epi, pre);
-  else tile_reg<T, MN_A, MN_B>(lds, A, B, K, epi, pre);
+  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B, GA>(lds, A, B, K, zero, epi, pre);
+  else tile_reg<T, MN_A, MN_B, GA>(lds, A, B, K, epi, pre);
 }
 
 }  // namespace gemm

@@ -42,11 +42,13 @@ def _check_routing(cfg, inp, out, w_router):
                 f"rows per expert min {counts.min()} max {counts.max()}")
 
 
-def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, ready_gemm12=False, cooperative=False):
+def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, ready_gemm12=False, cooperative=False,
+                     memory_rules=0):
     say(f"[gpu] {cfg.name} T={cfg.tokens}x{cfg.microbatches} d={cfg.d_model} f={cfg.d_ff} E={cfg.n_experts} "
-        f"k={cfg.top_k} {cfg.dtype} clip={cfg.clip_norm if clip_norm is None else clip_norm}")
+        f"k={cfg.top_k} {cfg.dtype} clip={cfg.clip_norm if clip_norm is None else clip_norm} "
+        f"wg_per_cu={wg_per_cu} memory_rules={memory_rules}")
     run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu, ready_gemm12=ready_gemm12,
-                 cooperative=cooperative)
+                 cooperative=cooperative, memory_rules=memory_rules)
     try:
         params = inp.flat_params().astype(np.float64)
         m = np.zeros_like(params)
@@ -461,3 +463,45 @@ def test_barrier_timeout_reported_and_handle_recovers(dtype, wg_per_cu):
         assert not bad, f"update after the reported timeout: {bad}: {errs}"
     finally:
         run.close()
+
+
+# ----------------------------------------------------------------------------
+# Memory rule: recomputation (only H of the first expert product is stored)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,T,d,f,E,k,wg_per_cu,mb,skew", [
+    ("f32", 333, 72, 136, 5, 2, 1, 1, False),
+    ("bf16", 333, 72, 136, 5, 2, 1, 1, False),
+    ("bf16", 1000, 256, 384, 16, 2, 1, 1, False),
+    ("bf16", 1000, 256, 384, 16, 2, 2, 1, False),
+    ("bf16", 300, 128, 64, 64, 8, 2, 1, False),
+    # split weight-gradient contractions (partial dW2 tiles also recompute gelu(H))
+    ("bf16", 1000, 256, 384, 16, 2, 1, 2, True),
+    ("f32", 300, 72, 136, 5, 2, 1, 3, True),
+])
+def test_recompute_rule(dtype, T, d, f, E, k, wg_per_cu, mb, skew):
+    # GEMM 1 keeps H only; GEMM 2 and dW2 apply GELU to their A fragments, the
+    # dH epilogue forms gelu'(H): the same update within the same gates
+    cfg = synth.small_config(f"recompute_{dtype}", T, d, f, E, k, dtype, microbatches=mb)
+    inp = synth.make_inputs(cfg, 19)
+    if skew:
+        bias = np.zeros(E, np.float32)
+        bias[0], bias[1] = 4.0, 2.0
+        inp.router_bias = bias
+    _run_and_compare(cfg, inp, BF16_TOL if dtype == "bf16" else F32_TOL, steps=2, wg_per_cu=wg_per_cu,
+                     memory_rules=B.MOE_MEM_RECOMPUTE)
+
+
+def test_recompute_rule_arena_and_2x1024():
+    # the 2x1024 workload under the rule, and the arena it saves: one
+    # [tokens * top_k, d_ff] bf16 tensor
+    cfg = synth.CONFIGS["bf16_2x1024"]
+    sizes = []
+    for rules in (0, B.MOE_MEM_RECOMPUTE):
+        from moe_step_megakernel_amd.layer import MoeLayerStep
+        L = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.tokens, "bf16", memory_rules=rules)
+        sizes.append(L.arena_bytes())
+        L.close()
+    saved = sizes[0] - sizes[1]
+    say(f"  arena {sizes[0]} -> {sizes[1]} bytes")
+    assert saved >= cfg.tokens * cfg.top_k * cfg.d_ff * 2 - 256   # less one 256-byte alignment unit
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL, steps=1, memory_rules=B.MOE_MEM_RECOMPUTE)
