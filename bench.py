@@ -208,6 +208,8 @@ def main(argv=None):
                     help="launch through hipLaunchCooperativeKernel instead of an ordinary launch")
     ap.add_argument("--ready-gemm12", action="store_true",
                     help="per-row-tile readiness counters instead of the grid barrier between the expert products")
+    ap.add_argument("--barrier-per-workgroup", action="store_true",
+                    help="every workgroup writes its XCD's L2 back at each grid barrier (instead of one per XCD)")
     ap.add_argument("--recompute", action="store_true",
                     help="memory rule: store H only and recompute gelu(H) / gelu'(H) where they are read")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -259,7 +261,8 @@ def main(argv=None):
                 events[mb][0].record(stream)
             layer.run(X[mb * T:(mb + 1) * T], Tg[mb * T:(mb + 1) * T], tokens_in_update=cfg.tokens_in_update,
                       step=step_no[0], zero_grad=(mb == 0), apply=(mb == M - 1), dx=dx, router_bias=bias,
-                      trace=trace, ready_gemm12=args.ready_gemm12, cooperative=args.cooperative)
+                      trace=trace, ready_gemm12=args.ready_gemm12, cooperative=args.cooperative,
+                      barrier_per_workgroup=args.barrier_per_workgroup)
             if events is not None:
                 events[mb][1].record(stream)
 

@@ -179,6 +179,10 @@ typedef struct {
  * barrier: it writes arena buffers, the debug outputs that are given, and (with
  * MOE_RUN_REFRESH_SHADOW) the bf16 weight copy from the unchanged params. */
 #define MOE_RUN_TEST_TIMEOUT 0x40000u
+/* Grid barriers in which every workgroup writes its XCD's L2 back to memory
+ * itself, instead of the last workgroup of each XCD doing it once for all
+ * (same results; for comparison). */
+#define MOE_RUN_BARRIER_PER_WORKGROUP 0x80000u
 
 /* Status-word bits reported by moe_step_status as MOE_ERR_DEVICE. */
 #define MOE_DEVICE_BARRIER_TIMEOUT 0x1u

@@ -22,6 +22,7 @@ MOE_RUN_APPLY_ROUTER, MOE_RUN_APPLY_EXPERTS = 0x40, 0x80
 MOE_RUN_READY_GEMM12 = 0x10000
 MOE_RUN_COOPERATIVE = 0x20000
 MOE_RUN_TEST_TIMEOUT = 0x40000
+MOE_RUN_BARRIER_PER_WORKGROUP = 0x80000
 
 
 def MOE_RUN_SKIP_PHASE(i: int) -> int:

@@ -210,18 +210,48 @@ __device__ __forceinline__ float gelu_only(float h) {
 // between launches.
 // ---------------------------------------------------------------------------
 struct Ctrl {
-  unsigned* arrive;  // [grid][32]: slot w at arrive[w * 32]
+  unsigned* arrive;  // [grid][32]: slot w at arrive[w * 32]; word 1 holds w's XCD
   unsigned* gen;     // last released target
   unsigned* status;  // error bits (MOE_DEVICE_*)
   unsigned* abort;   // nonzero once any workgroup gave up waiting
   unsigned* never;   // a word nothing writes (the failure-path test waits on it)
+  unsigned* xcd;     // per-XCD words (kXcdWords): members of XCD x at xcd[x], its
+                     // arrival counter at xcd[32 (1 + x)], its arrival slot at xcd[32 (9 + x)]
   uint64_t limit;    // bound of every wait, in ticks of the 100 MHz constant clock
+  int per_wg;        // 1: every barrier writes back each workgroup's L2 itself
+};
+constexpr int kMaxXcd = 8;
+constexpr int kXcdWords = 32 * (1 + 2 * kMaxXcd);
+
+// Barrier bookkeeping a workgroup keeps in LDS for the whole launch.
+struct BarrierState {
+  unsigned flag;              // result broadcast to the workgroup
+  unsigned xcc;               // this workgroup's XCD (hardware register)
+  unsigned xmem;              // workgroups on that XCD in this launch
+  unsigned xall[kMaxXcd];     // workgroup 0: workgroups on every XCD
 };
 
 // Bounded wait: about two seconds of the 100 MHz constant clock.
 constexpr uint64_t kBarrierTimeoutTicks = 200000000ull;
 // The bound under the failure-path test flag: about 10 us.
 constexpr uint64_t kTestTimeoutTicks = 1000ull;
+
+// The XCD (and so the L2) this wave runs on.
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+  return x;
+}
+
+// Release at agent scope (the XCD's dirty L2 lines are written back to
+// memory), completed before the caller's next memory operation.  The fence
+// emits the L2 write-back; the compiler does not always follow it with a wait
+// on the vector-memory counter (it dropped it after an earlier explicit wait),
+// so the wait is issued here as an instruction it cannot remove.
+__device__ __forceinline__ void release_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // A wait that gives up: the timeout bit and the abort word are set, so every
 // other workgroup's waits give up as well and the whole grid exits.
@@ -263,46 +293,98 @@ __device__ __forceinline__ bool wait_count(const Ctrl& c, const int* p, int targ
   return true;
 }
 
-// Grid-wide barrier.  Every wave first waits until its own stores have
-// reached L2; after a workgroup barrier one wave releases at agent scope for
-// the whole workgroup (writes the XCD's dirty L2 lines back, so the other XCDs
-// see them) -- one L2 write-back per workgroup instead of one per wave.  A
-// workgroup other than 0 then stores `target` into its arrival slot (relaxed:
-// the fence before it orders the data) and polls the generation word;
-// workgroup 0 polls all arrival slots in parallel (one per thread), acquires,
-// and stores `target` into the generation word.  Polling uses plain relaxed
-// loads with a sleep in between, and each poller acquires once afterwards, so
-// waiting does not keep invalidating the caches under the workgroups still
-// working.  Returns false if a wait timed out or another workgroup already
-// gave up; the caller then skips all further phases so that every workgroup
-// still exits.
-__device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, unsigned* lds_flag) {
-  // release once per workgroup: every wave's stores have reached L2 before the
-  // barrier; one wave then writes the XCD's dirty L2 lines back
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// Grid-wide barrier.  Every wave first waits until its own stores have reached
+// its XCD's L2 (vmcnt), then:
+//
+// * Per-workgroup release (the first barrier of every launch, and every
+//   barrier with Ctrl::per_wg): one wave releases at agent scope for the whole
+//   workgroup (its XCD's dirty L2 lines are written back), then the workgroup
+//   stores `target` into its arrival slot.  Workgroup 0 polls all slots in
+//   parallel (one per thread), acquires, and stores `target` into the
+//   generation word.  At the first barrier each workgroup also records the XCD
+//   it runs on (HW_REG_XCC_ID) in its slot; workgroup 0 counts the workgroups
+//   of each XCD and publishes the counts and zeroed XCD counters with the
+//   generation.
+// * One release per XCD (every later barrier, hk = 1, 2, ...): a workgroup adds
+//   1 to its XCD's arrival counter (an atomic, performed where all XCDs see
+//   it).  The workgroup that brings the counter to members * hk arrived last on
+//   its XCD: all its XCD's workgroups had their stores in that L2 before they
+//   counted, so its one write-back covers them all; it then stores `target`
+//   into the XCD's arrival slot.  Workgroup 0 polls the XCD slots and stores the
+//   generation.  The membership comes from the hardware register in this very
+//   launch, so it holds whatever the dispatch order was.
+//
+// Everyone polls the generation word with relaxed loads (a sleep between polls)
+// and acquires once afterwards.  Returns false if a wait timed out or another
+// workgroup already gave up; the caller then skips all further phases so that
+// every workgroup still exits.
+__device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, BarrierState* bs, int hk) {
+  const int tid = threadIdx.x;
+  const bool per_wg = hk == 0 || c.per_wg != 0;
+  if (hk == 0 && tid == 0) {
+    bs->xcc = xcc_id();
+    if (blockIdx.x != 0) c.arrive[(size_t)blockIdx.x * 32 + 1] = bs->xcc;   // written back with the data
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are in L2
   __syncthreads();
-  if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  if (threadIdx.x == 0) *lds_flag = 1u;
+  if (per_wg) {
+    if (tid < 64) release_agent();
+    if (tid == 0) bs->flag = 1u;
+  } else if (tid == 0) {
+    bs->flag = 1u;
+    const unsigned x = bs->xcc & (kMaxXcd - 1);
+    const unsigned old = __hip_atomic_fetch_add(c.xcd + 32 * (1 + x), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == bs->xmem * (unsigned)hk) {
+      release_agent();   // the last of its XCD: one write-back for all of them
+      __hip_atomic_store(c.xcd + 32 * (9 + x), target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   __syncthreads();
   if (blockIdx.x == 0) {
     bool ok = true;
-    for (int w = threadIdx.x; w < (int)gridDim.x; w += kThreads)
-      if (w != 0 && !wait_for(c, c.arrive + (size_t)w * 32, target)) {
-        ok = false;
-        break;
+    if (per_wg) {
+      for (int w = tid; w < (int)gridDim.x; w += kThreads)
+        if (w != 0 && !wait_for(c, c.arrive + (size_t)w * 32, target)) {
+          ok = false;
+          break;
+        }
+    } else if (tid < kMaxXcd && bs->xall[tid] > 0u) {
+      ok = wait_for(c, c.xcd + 32 * (9 + tid), target);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!ok) bs->flag = 0u;
+    if (hk == 0) {
+      // XCD membership of this launch
+      __syncthreads();
+      if (tid < kMaxXcd) bs->xall[tid] = 0u;
+      __syncthreads();
+      for (int w = tid; w < (int)gridDim.x; w += kThreads) {
+        const unsigned x = w == 0 ? bs->xcc
+                                  : __hip_atomic_load(c.arrive + (size_t)w * 32 + 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        atomicAdd(&bs->xall[x & (kMaxXcd - 1)], 1u);
       }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (!ok) *lds_flag = 0u;
+      __syncthreads();
+      if (tid < kMaxXcd) {
+        __hip_atomic_store(c.xcd + tid, bs->xall[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(c.xcd + 32 * (1 + tid), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid == 0) bs->xmem = bs->xall[bs->xcc & (kMaxXcd - 1)];
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // these stores are performed before the generation
+    }
     __syncthreads();
-    if (threadIdx.x == 0 && *lds_flag != 0u)
-      __hip_atomic_store(c.gen, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  } else if (threadIdx.x == 0) {
-    __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!wait_for(c, c.gen, target)) *lds_flag = 0u;
+    if (tid == 0 && bs->flag != 0u)
+      __hip_atomic_store(c.gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (tid == 0) {
+    if (per_wg) __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (!wait_for(c, c.gen, target)) bs->flag = 0u;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (hk == 0)
+      bs->xmem = __hip_atomic_load(c.xcd + (bs->xcc & (kMaxXcd - 1)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  return *lds_flag != 0u;
+  return bs->flag != 0u;
 }
 
 }  // namespace moe

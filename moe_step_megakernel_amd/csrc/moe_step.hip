@@ -96,6 +96,10 @@ int check_config(const moe_step_config* c, char* err) {
 
 }  // namespace
 
+// Barrier words of a grid of G workgroups: generation, status, abort, an unused
+// word, one arrival slot per workgroup, then the per-XCD words; 128 bytes each.
+static size_t ctrl_words(int G) { return (size_t)(G + 4) * 32 + moe::kXcdWords; }
+
 // Routed rows (max_tokens * top_k) from which a bf16 handle runs two workgroups
 // per compute unit by default.
 constexpr long kTwoPerCuRows = 16384;
@@ -266,11 +270,11 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
 // ---------------------------------------------------------------------------
 // The arena of the allocation-free entry point: a static device array (each
 // GPU the library runs on holds its own copy until the process ends).  The
-// barrier words (for grids of up to 1020 workgroups) and the zero page sit at
+// barrier words (for grids of up to 1003 workgroups) and the zero page sit at
 // fixed offsets at its start, so no other call's buffers overlap them.
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) char scratch[MOE_STEP_STATIC_SCRATCH_BYTES];
-constexpr size_t kStaticCtrlWords = 1024 * 32;
+constexpr size_t kStaticCtrlWords = 1024 * 32;   // grids of up to 1003 workgroups
 
 // Before a static-arena launch: the barrier words, status and abort word of
 // the previous call are cleared and the zero page is zeroed (a fill kernel,
@@ -343,7 +347,8 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   }
   if (run_flags & ~(MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | MOE_RUN_REFRESH_SHADOW | MOE_RUN_TRACE | MOE_RUN_SKIP_MASK |
                     MOE_RUN_ZERO_GRAD_ROUTER | MOE_RUN_ZERO_GRAD_EXPERTS | MOE_RUN_APPLY_ROUTER |
-                    MOE_RUN_APPLY_EXPERTS | MOE_RUN_READY_GEMM12 | MOE_RUN_COOPERATIVE | MOE_RUN_TEST_TIMEOUT)) {
+                    MOE_RUN_APPLY_EXPERTS | MOE_RUN_READY_GEMM12 | MOE_RUN_COOPERATIVE | MOE_RUN_TEST_TIMEOUT |
+                    MOE_RUN_BARRIER_PER_WORKGROUP)) {
     set_err(err, "unknown run flags 0x%x", run_flags);
     return MOE_ERR_ARG;
   }
@@ -456,6 +461,8 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.ctrl.abort = h->ctrl + 64;
   p.ctrl.arrive = h->ctrl + 128;
   p.ctrl.never = h->ctrl + 96;
+  p.ctrl.xcd = h->ctrl + (size_t)(h->grid + 4) * 32;
+  p.ctrl.per_wg = (run_flags & MOE_RUN_BARRIER_PER_WORKGROUP) ? 1 : 0;
   p.ctrl.limit = (run_flags & MOE_RUN_TEST_TIMEOUT) ? moe::kTestTimeoutTicks : moe::kBarrierTimeoutTicks;
   p.epoch = ++h->epoch;
   p.recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) ? 1 : 0;
@@ -472,7 +479,7 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   // guarantees it but costs about 19 us more per update.
   const bool coop = (run_flags & MOE_RUN_COOPERATIVE) != 0u;
   if (static_arena) {
-    hipLaunchKernelGGL(static_clear, dim3(16), dim3(256), 0, stream, h->ctrl, (h->grid + 4) * 32,
+    hipLaunchKernelGGL(static_clear, dim3(16), dim3(256), 0, stream, h->ctrl, (int)ctrl_words(h->grid),
                        reinterpret_cast<uint32_t*>(h->zero));
     if ((he = hipGetLastError()) != hipSuccess) {
       set_err(err, "clearing the barrier words: %s", hipGetErrorString(he));
@@ -567,7 +574,7 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
     delete h;
     return rc;
   }
-  h->arena_bytes = plan_arena(*h, nullptr, (size_t)(h->grid + 4) * 32);
+  h->arena_bytes = plan_arena(*h, nullptr, ctrl_words(h->grid));
 
   he = hipMalloc(reinterpret_cast<void**>(&h->arena), h->arena_bytes);
   if (he != hipSuccess) {
@@ -575,7 +582,7 @@ int moe_step_create(const moe_step_config* cfg, moe_step_t* out) {
     delete h;
     return MOE_ERR_NOMEM;
   }
-  plan_arena(*h, h->arena, (size_t)(h->grid + 4) * 32);
+  plan_arena(*h, h->arena, ctrl_words(h->grid));
 
   // the arena starts zeroed (every stored index is then in range) and so do
   // the barrier words and status (synchronous; not part of any run)
@@ -634,7 +641,7 @@ int moe_step_run_static(const moe_step_config* cfg, const moe_step_io* io, int32
   moe_step h;   // on the stack: the handle state of this one call
   h.cfg = *cfg;
   if ((rc = select_kernel(*cfg, sd->cus, h, err)) != MOE_OK) return rc;
-  if ((size_t)(h.grid + 4) * 32 > kStaticCtrlWords) {
+  if (ctrl_words(h.grid) > kStaticCtrlWords) {
     set_err(err, "grid of %d workgroups exceeds the static barrier words", h.grid);
     return MOE_ERR_SHAPE;
   }
@@ -670,7 +677,7 @@ int moe_step_status(moe_step_t h) {
     set_err(h->err, "device error 0x%x:%s%s%s", st, (st & MOE_DEVICE_BARRIER_TIMEOUT) ? " grid-barrier timeout" : "",
             (st & MOE_DEVICE_NONFINITE_LOGIT) ? " non-finite router logit" : "",
             (st & MOE_DEVICE_BAD_ROUTE) ? " expert index out of range" : "");
-    he = hipMemset(h->ctrl, 0, (size_t)(h->grid + 4) * 32 * sizeof(unsigned));
+    he = hipMemset(h->ctrl, 0, ctrl_words(h->grid) * sizeof(unsigned));
     if (he == hipSuccess) he = hipDeviceSynchronize();
     h->epoch = 0;
     return MOE_ERR_DEVICE;

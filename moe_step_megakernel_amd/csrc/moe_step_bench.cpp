@@ -105,7 +105,7 @@ int run_copy(int mib, int steps) {
 int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024";
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
-  bool ready = false, coop = false, recompute = false;
+  bool ready = false, coop = false, recompute = false, per_wg = false;
   std::vector<unsigned> skips{0u};
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -135,6 +135,7 @@ int main(int argc, char** argv) {
     else if (a == "--ready") ready = true;
     else if (a == "--coop") coop = true;
     else if (a == "--recompute") recompute = true;
+    else if (a == "--per-wg-barrier") per_wg = true;
     else {
       std::fprintf(stderr, "unknown argument %s\n", a.c_str());
       return 1;
@@ -226,7 +227,8 @@ int main(int argc, char** argv) {
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
   const uint32_t base =
-      MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | (ready ? MOE_RUN_READY_GEMM12 : 0u) | (coop ? MOE_RUN_COOPERATIVE : 0u);
+      MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | (ready ? MOE_RUN_READY_GEMM12 : 0u) | (coop ? MOE_RUN_COOPERATIVE : 0u) |
+      (per_wg ? MOE_RUN_BARRIER_PER_WORKGROUP : 0u);
   int64_t step = 1;
   for (int i = 0; i < warmup; ++i, ++step) {
     if (moe_step_run(h, &io, sh->T, sh->T, step, base | (i == 0 ? MOE_RUN_REFRESH_SHADOW : 0u), stream) != MOE_OK) {

@@ -62,7 +62,7 @@ struct Meta {
   int nsplit;                   // experts with more than one chunk
   int splitlist[kMaxExperts];   // those experts, ascending
   float red[8];                 // block reductions
-  unsigned flag;                // barrier result broadcast
+  BarrierState bar;             // grid-barrier bookkeeping (result broadcast, XCD membership)
 };
 static_assert(sizeof(Meta) <= kMetaBytes, "meta");
 
@@ -834,7 +834,10 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
       // release for the workgroup (the XCD's L2 is written back), then the count
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(p.ready + mg, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) {
+        release_agent();
+        __hip_atomic_fetch_add(p.ready + mg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -858,10 +861,10 @@ __device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& me
       if (threadIdx.x == 0) {
         const bool ok = wait_count(p.ctrl, p.ready + mg, ceil_div(f, gemm::BN));
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        meta.flag = ok ? 1u : 0u;
+        meta.bar.flag = ok ? 1u : 0u;
       }
       __syncthreads();
-      if (meta.flag == 0u) return false;
+      if (meta.bar.flag == 0u) return false;
     }
     const int e = expert_of_tile(meta, p.E, mg);
     const int m0 = (mg - meta.moff[e]) * gemm::BM;
@@ -1672,18 +1675,19 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
   const bool apply_r = (p.flags & 0x40u) != 0u, apply_e = (p.flags & 0x80u) != 0u;
   const bool want_dx = p.dx != nullptr;
 
-#define MOE_SYNC(ph)                                                 \
-  do {                                                               \
-    trace_mark(p, ph, 1);                                            \
-    if (!grid_barrier(p.ctrl, p.epoch * 8u + (ph) + 1u, &meta.flag)) return; \
-    trace_mark(p, ph, 2);                                            \
+  int hk = 0;   // barriers passed in this launch (the first one learns the XCD membership)
+#define MOE_SYNC(ph)                                                               \
+  do {                                                                             \
+    trace_mark(p, ph, 1);                                                          \
+    if (!grid_barrier(p.ctrl, p.epoch * 8u + (ph) + 1u, &meta.bar, hk++)) return;  \
+    trace_mark(p, ph, 2);                                                          \
   } while (0)
 
   // A launch enqueued after one that gave up (before moe_step_status reset the
   // abort word) writes nothing.
-  if (threadIdx.x == 0) meta.flag = __hip_atomic_load(p.ctrl.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) meta.bar.flag = __hip_atomic_load(p.ctrl.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (meta.flag != 0u) return;
+  if (meta.bar.flag != 0u) return;
   if ((p.flags & 0x40000u) && blockIdx.x == gridDim.x - 1) {
     // failure-path test: this workgroup waits for a word nothing sets, gives
     // up, and never arrives at the first barrier
@@ -1732,7 +1736,7 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
       const float s = block_sum(sq, meta.red);
       if (threadIdx.x == 0) p.norm_part[n10 + e * tpe + t] = s;
     }
-    if (!grid_barrier(p.ctrl, p.epoch * 8u + 8u, &meta.flag)) return;
+    if (!grid_barrier(p.ctrl, p.epoch * 8u + 8u, &meta.bar, hk++)) return;
   }
   trace_mark(p, 7, 0);
   if (!(skip & 128u)) phase_final<T, OCC>(p, work, meta, zero_r || zero_e, apply_r, apply_e, want_dx);

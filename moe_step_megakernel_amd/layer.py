@@ -34,7 +34,7 @@ class MoeLayerStep:
 
     def run(self, x, target, *, tokens_in_update=None, step=1, zero_grad=True, apply=True, dx=None,
             router_bias=None, debug=None, trace=None, stream=None, groups=None, ready_gemm12=False,
-            cooperative=False, refresh_shadow=False, test_timeout=False):
+            cooperative=False, refresh_shadow=False, test_timeout=False, barrier_per_workgroup=False):
         """Enqueues one launch.  ``debug`` is an optional dict of preallocated debug tensors
         (router_logits, topk_idx, topk_gate, expert_counts, route_perm).  ``groups`` (selective
         updates) replaces zero_grad/apply/step by per-group settings: a dict with keys
@@ -44,7 +44,8 @@ class MoeLayerStep:
         launches through hipLaunchCooperativeKernel instead of an ordinary launch.
         ``refresh_shadow`` rebuilds the bf16 weight copy from params even when it is
         current; ``test_timeout`` sets the failure-path test flag (the launch ends
-        with a grid-barrier timeout)."""
+        with a grid-barrier timeout); ``barrier_per_workgroup`` makes every workgroup write its
+        XCD's L2 back at each grid barrier instead of one workgroup per XCD (same results)."""
         n = 0 if x is None else int(x.shape[0])
         self._check_tensors(n, x, target, dx, router_bias, debug or {}, trace)
         flags = 0
@@ -64,6 +65,8 @@ class MoeLayerStep:
             flags |= B.MOE_RUN_REFRESH_SHADOW
         if test_timeout:
             flags |= B.MOE_RUN_TEST_TIMEOUT
+        if barrier_per_workgroup:
+            flags |= B.MOE_RUN_BARRIER_PER_WORKGROUP
         if trace is not None:
             flags |= B.MOE_RUN_TRACE
         if ready_gemm12:
