@@ -86,7 +86,7 @@ typedef struct {
   int32_t device;         /* HIP device ordinal */
   int32_t wg_per_cu;      /* persistent workgroups per compute unit: 1, 2, or 0 =
                              automatic (2 for bf16 when max_tokens * top_k >=
-                             16384, else 1).  Two per unit runs a kernel built for
+                             4096, else 1).  Two per unit runs a kernel built for
                              half the registers and LDS per workgroup; fp32
                              handles always run one.  Results differ between the
                              settings at rounding level only: the split of the
@@ -156,7 +156,12 @@ typedef struct {
  * 4 combine/loss, 5 dH + dW2 + router partials, 6 dW1 + dX + router gradient,
  * 7 dx sum + norm + clip/AdamW. */
 #define MOE_RUN_SKIP_PHASE(i) (0x100u << (i))
-#define MOE_RUN_SKIP_MASK 0xff00u
+/* The same for two steps inside phases, so each gets a figure of its own: the
+ * dispatch gather (copy of the token rows into expert order, in phase 1) and
+ * the k-way sum of the per-slot input gradients (dx, in phase 7). */
+#define MOE_RUN_SKIP_GATHER 0x100000u
+#define MOE_RUN_SKIP_ROWSUM 0x200000u
+#define MOE_RUN_SKIP_MASK (0xff00u | MOE_RUN_SKIP_GATHER | MOE_RUN_SKIP_ROWSUM)
 /* Readiness-driven scheduling between expert GEMM 1 and GEMM 2 (the pages'
  * "Open problems", Performance 1: replace whole-grid barriers by finer
  * dependencies).  Without it a grid barrier separates the two products.  With

@@ -16,7 +16,8 @@ MOE_STEP_ABI_VERSION = 1
 MOE_OK, MOE_ERR_ARG, MOE_ERR_SHAPE, MOE_ERR_HIP, MOE_ERR_NOMEM, MOE_ERR_DEVICE, MOE_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_RUN_ZERO_GRAD, MOE_RUN_APPLY, MOE_RUN_REFRESH_SHADOW, MOE_RUN_TRACE = 0x1, 0x2, 0x4, 0x8
-MOE_RUN_SKIP_MASK = 0xFF00
+MOE_RUN_SKIP_GATHER, MOE_RUN_SKIP_ROWSUM = 0x100000, 0x200000
+MOE_RUN_SKIP_MASK = 0xFF00 | MOE_RUN_SKIP_GATHER | MOE_RUN_SKIP_ROWSUM
 MOE_RUN_ZERO_GRAD_ROUTER, MOE_RUN_ZERO_GRAD_EXPERTS = 0x10, 0x20
 MOE_RUN_APPLY_ROUTER, MOE_RUN_APPLY_EXPERTS = 0x40, 0x80
 MOE_RUN_READY_GEMM12 = 0x10000

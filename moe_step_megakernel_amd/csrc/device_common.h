@@ -304,7 +304,9 @@ __device__ __forceinline__ bool wait_count(const Ctrl& c, const int* p, int targ
 //   generation word.  At the first barrier each workgroup also records the XCD
 //   it runs on (HW_REG_XCC_ID) in its slot; workgroup 0 counts the workgroups
 //   of each XCD and publishes the counts and zeroed XCD counters with the
-//   generation.
+//   generation.  (A first barrier without any write-back, with the routing
+//   histogram stored at agent scope instead, measured 15 us slower per update:
+//   the next barrier and the acquires then meet those dirty lines.)
 // * One release per XCD (every later barrier, hk = 1, 2, ...): a workgroup adds
 //   1 to its XCD's arrival counter (an atomic, performed where all XCDs see
 //   it).  The workgroup that brings the counter to members * hk arrived last on
@@ -323,9 +325,10 @@ __device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, Bar
   const bool per_wg = hk == 0 || c.per_wg != 0;
   if (hk == 0 && tid == 0) {
     bs->xcc = xcc_id();
-    if (blockIdx.x != 0) c.arrive[(size_t)blockIdx.x * 32 + 1] = bs->xcc;   // written back with the data
+    if (blockIdx.x != 0)
+      __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32 + 1, bs->xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are in L2
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are in L2 (agent-scope ones in memory)
   __syncthreads();
   if (per_wg) {
     if (tid < 64) release_agent();

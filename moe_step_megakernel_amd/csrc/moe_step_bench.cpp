@@ -1,17 +1,22 @@
 // moe_step_bench: drives the C ABI of libmoe_step from C++ alone (no Python),
 // for profiling runs under rocprofv3 and as an example of the ABI.
 //
-// Inputs are synthetic and shaped like the layer workloads: x, t ~ N(0,1) and
-// weights ~ N(0, 0.02^2), drawn with a splitmix64 generator and a Box-Muller
-// transform (a different stream from the Python generator; timings do not
-// depend on the exact values).  Prints one line per run with ms/update.
+// Inputs: with --inputs FILE, exactly the seeded inputs of the tests and the
+// Python bench (written by `python -m synth.dump`), including the number of
+// microbatches of the update and the router bias; otherwise synthetic inputs
+// shaped like the layer workloads (x, t ~ N(0,1), weights ~ N(0, 0.02^2) from a
+// splitmix64 generator and a Box-Muller transform).  One timed unit is one
+// update: its microbatches in order, the first with MOE_RUN_ZERO_GRAD, the
+// last with MOE_RUN_APPLY.  Prints one line per skip mask with ms/update.
 //
-//   moe_step_bench [--config NAME] [--steps K] [--warmup W] [--skip MASK[,MASK...]] [--wg-per-cu N] [--ready]
-//                  [--coop] [--copy-mib N]
-//     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024
-//     --skip MASK: after the warm-up, time K launches that skip the phases in MASK
-//                  (bit i = phase i), for per-phase timing and counter collection;
-//                  a comma-separated list times K launches per mask, in order
+//   moe_step_bench [--config NAME | --inputs FILE] [--steps K] [--warmup W] [--skip MASK[,MASK...]]
+//                  [--wg-per-cu N] [--ready] [--coop] [--recompute] [--per-wg-barrier] [--copy-mib N]
+//     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024 (--tokens N changes its token count)
+//     --skip MASK: after the warm-up, time K updates whose launches skip the
+//                  phases in MASK (bit i = phase i, 0..7; bit 8 = the dispatch
+//                  gather inside phase 1; bit 9 = the k-way row sum of dx inside
+//                  phase 7), for per-phase timing and counter collection; a
+//                  comma-separated list times K updates per mask, in order
 //     --copy-mib N: instead, time a plain device copy of N MiB (read N, write N),
 //                  the reference for scaling memory counters
 #include <hip/hip_runtime.h>
@@ -41,6 +46,7 @@ struct Shape {
   const char* name;
   int T, d, f, E, k;
   int dtype;
+  int M = 1;   // microbatches per update
 };
 
 const Shape kShapes[] = {
@@ -103,7 +109,8 @@ int run_copy(int mib, int steps) {
 }  // namespace
 
 int main(int argc, char** argv) {
-  std::string cfg_name = "bf16_2x1024";
+  std::string cfg_name = "bf16_2x1024", inputs;
+  int tokens = 0;   // --tokens: tokens per launch for a built-in shape (0 = the shape's own)
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
   bool ready = false, coop = false, recompute = false, per_wg = false;
   std::vector<unsigned> skips{0u};
@@ -117,6 +124,8 @@ int main(int argc, char** argv) {
       return argv[++i];
     };
     if (a == "--config") cfg_name = next();
+    else if (a == "--inputs") inputs = next();
+    else if (a == "--tokens") tokens = std::atoi(next());
     else if (a == "--steps") steps = std::atoi(next());
     else if (a == "--warmup") warmup = std::atoi(next());
     else if (a == "--skip") {
@@ -143,13 +152,57 @@ int main(int argc, char** argv) {
   }
   if (copy_mib > 0) return run_copy(copy_mib, steps);
 
+  Shape file_shape{"inputs", 0, 0, 0, 0, 0, 0};
+  std::vector<char> hx, ht;
+  std::vector<float> hp, hbias;
   const Shape* sh = nullptr;
-  for (const Shape& s : kShapes)
-    if (cfg_name == s.name) sh = &s;
-  if (!sh) {
-    std::fprintf(stderr, "unknown config %s\n", cfg_name.c_str());
-    return 1;
+  if (!inputs.empty()) {
+    // the seeded inputs of the tests (synth.dump)
+    FILE* fh = std::fopen(inputs.c_str(), "rb");
+    if (!fh) {
+      std::fprintf(stderr, "cannot open %s\n", inputs.c_str());
+      return 1;
+    }
+    char magic[8];
+    int32_t hd[8];
+    if (std::fread(magic, 1, 8, fh) != 8 || std::memcmp(magic, "MOEIN001", 8) != 0 ||
+        std::fread(hd, 4, 8, fh) != 8) {
+      std::fprintf(stderr, "%s is not an input file of synth.dump\n", inputs.c_str());
+      return 1;
+    }
+    file_shape = Shape{"inputs", hd[0], hd[2], hd[3], hd[4], hd[5], hd[6] ? MOE_DTYPE_BF16 : MOE_DTYPE_F32, hd[1]};
+    const size_t es = hd[6] ? 2 : 4;
+    const size_t nx = (size_t)hd[0] * hd[1] * hd[2];
+    const size_t P = (size_t)hd[2] * hd[4] + 2ull * hd[4] * hd[2] * hd[3];
+    hx.resize(nx * es);
+    ht.resize(nx * es);
+    hp.resize(P);
+    bool ok = std::fread(hx.data(), 1, hx.size(), fh) == hx.size() && std::fread(ht.data(), 1, ht.size(), fh) == ht.size() &&
+              std::fread(hp.data(), 4, P, fh) == P;
+    if (ok && hd[7]) {
+      hbias.resize(hd[4]);
+      ok = std::fread(hbias.data(), 4, hbias.size(), fh) == hbias.size();
+    }
+    std::fclose(fh);
+    if (!ok) {
+      std::fprintf(stderr, "%s is truncated\n", inputs.c_str());
+      return 1;
+    }
+    sh = &file_shape;
+  } else {
+    for (const Shape& s : kShapes)
+      if (cfg_name == s.name) sh = &s;
+    if (!sh) {
+      std::fprintf(stderr, "unknown config %s\n", cfg_name.c_str());
+      return 1;
+    }
+    if (tokens > 0) {
+      file_shape = *sh;
+      file_shape.T = tokens;
+      sh = &file_shape;
+    }
   }
+  const int M = sh->M;
   moe_step_config cfg;
   std::memset(&cfg, 0, sizeof(cfg));
   cfg.struct_size = sizeof(cfg);
@@ -174,68 +227,78 @@ int main(int argc, char** argv) {
     return 2;
   }
   const size_t P = moe_step_param_count(&cfg);
-  const size_t nx = (size_t)sh->T * sh->d;
+  const size_t nt = (size_t)sh->T * sh->d;   // elements of one microbatch's x
   const size_t es = sh->dtype == MOE_DTYPE_BF16 ? 2 : 4;
-  Rng rng{0x5eedull};
-  std::vector<float> hp(P);
-  for (size_t i = 0; i < P; ++i) hp[i] = (float)(0.02 * rng.normal());
-  std::vector<char> hx(nx * es), ht(nx * es);
-  for (size_t i = 0; i < nx; ++i) {
-    const float a = (float)rng.normal();
-    if (es == 2) {
-      const uint16_t b = to_bf16(a);
-      std::memcpy(&hx[i * 2], &b, 2);
-    } else {
-      std::memcpy(&hx[i * 4], &a, 4);
-    }
+  if (inputs.empty()) {
+    Rng rng{0x5eedull};
+    hp.resize(P);
+    for (size_t i = 0; i < P; ++i) hp[i] = (float)(0.02 * rng.normal());
+    hx.resize(nt * es);
+    ht.resize(nt * es);
+    for (std::vector<char>* v : {&hx, &ht})
+      for (size_t i = 0; i < nt; ++i) {
+        const float a = (float)rng.normal();
+        if (es == 2) {
+          const uint16_t b = to_bf16(a);
+          std::memcpy(&(*v)[i * 2], &b, 2);
+        } else {
+          std::memcpy(&(*v)[i * 4], &a, 4);
+        }
+      }
   }
-  for (size_t i = 0; i < nx; ++i) {
-    const float a = (float)rng.normal();
-    if (es == 2) {
-      const uint16_t b = to_bf16(a);
-      std::memcpy(&ht[i * 2], &b, 2);
-    } else {
-      std::memcpy(&ht[i * 4], &a, 4);
-    }
-  }
-  void *dx_in, *dt;
-  float *params, *grads, *m, *v, *dxg, *stats;
-  CHECK_HIP(hipMalloc(&dx_in, nx * es));
-  CHECK_HIP(hipMalloc(&dt, nx * es));
+  char *dx_in, *dt;
+  float *params, *grads, *m, *v, *dxg, *stats, *bias = nullptr;
+  CHECK_HIP(hipMalloc(&dx_in, hx.size()));
+  CHECK_HIP(hipMalloc(&dt, ht.size()));
   CHECK_HIP(hipMalloc(&params, P * 4));
   CHECK_HIP(hipMalloc(&grads, P * 4));
   CHECK_HIP(hipMalloc(&m, P * 4));
   CHECK_HIP(hipMalloc(&v, P * 4));
-  CHECK_HIP(hipMalloc(&dxg, nx * 4));
+  CHECK_HIP(hipMalloc(&dxg, nt * 4));
   CHECK_HIP(hipMalloc(&stats, 16));
-  CHECK_HIP(hipMemcpy(dx_in, hx.data(), nx * es, hipMemcpyHostToDevice));
-  CHECK_HIP(hipMemcpy(dt, ht.data(), nx * es, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dx_in, hx.data(), hx.size(), hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dt, ht.data(), ht.size(), hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(params, hp.data(), P * 4, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemset(m, 0, P * 4));
   CHECK_HIP(hipMemset(v, 0, P * 4));
+  if (!hbias.empty()) {
+    CHECK_HIP(hipMalloc(&bias, hbias.size() * 4));
+    CHECK_HIP(hipMemcpy(bias, hbias.data(), hbias.size() * 4, hipMemcpyHostToDevice));
+  }
 
   moe_step_io io;
   std::memset(&io, 0, sizeof(io));
-  io.x = dx_in;
-  io.target = dt;
   io.params = params;
   io.grads = grads;
   io.exp_avg = m;
   io.exp_avg_sq = v;
   io.dx = dxg;
   io.stats = stats;
+  io.router_bias = bias;
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
-  const uint32_t base =
-      MOE_RUN_ZERO_GRAD | MOE_RUN_APPLY | (ready ? MOE_RUN_READY_GEMM12 : 0u) | (coop ? MOE_RUN_COOPERATIVE : 0u) |
-      (per_wg ? MOE_RUN_BARRIER_PER_WORKGROUP : 0u);
+  const uint32_t base = (ready ? MOE_RUN_READY_GEMM12 : 0u) | (coop ? MOE_RUN_COOPERATIVE : 0u) |
+                        (per_wg ? MOE_RUN_BARRIER_PER_WORKGROUP : 0u);
   int64_t step = 1;
-  for (int i = 0; i < warmup; ++i, ++step) {
-    if (moe_step_run(h, &io, sh->T, sh->T, step, base | (i == 0 ? MOE_RUN_REFRESH_SHADOW : 0u), stream) != MOE_OK) {
-      std::fprintf(stderr, "moe_step_run: %s\n", moe_step_last_error(h));
-      return 2;
+  bool first = true;
+  // one update: the microbatches in order (x and t of microbatch mb at offset mb * T)
+  auto update = [&](uint32_t extra) -> int {
+    for (int mb = 0; mb < M; ++mb) {
+      io.x = dx_in + (size_t)mb * nt * es;
+      io.target = dt + (size_t)mb * nt * es;
+      uint32_t fl = base | extra | (mb == 0 ? MOE_RUN_ZERO_GRAD : 0u) | (mb == M - 1 ? MOE_RUN_APPLY : 0u);
+      if (first) fl |= MOE_RUN_REFRESH_SHADOW;
+      first = false;
+      if (moe_step_run(h, &io, sh->T, (int64_t)sh->T * M, step, fl, stream) != MOE_OK) {
+        std::fprintf(stderr, "moe_step_run: %s\n", moe_step_last_error(h));
+        return 2;
+      }
     }
-  }
+    ++step;
+    return 0;
+  };
+  for (int i = 0; i < warmup; ++i)
+    if (update(0u)) return 2;
   if (moe_step_status(h) != MOE_OK) {
     std::fprintf(stderr, "moe_step_status: %s\n", moe_step_last_error(h));
     return 2;
@@ -244,13 +307,11 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipEventCreate(&e0));
   CHECK_HIP(hipEventCreate(&e1));
   for (const unsigned skip : skips) {
+    const uint32_t sk = ((skip & 0xffu) << 8) | ((skip & 0x100u) ? MOE_RUN_SKIP_GATHER : 0u) |
+                        ((skip & 0x200u) ? MOE_RUN_SKIP_ROWSUM : 0u);
     CHECK_HIP(hipEventRecord(e0, stream));
-    for (int i = 0; i < steps; ++i, ++step) {
-      if (moe_step_run(h, &io, sh->T, sh->T, step, base | (skip << 8), stream) != MOE_OK) {
-        std::fprintf(stderr, "moe_step_run: %s\n", moe_step_last_error(h));
-        return 2;
-      }
-    }
+    for (int i = 0; i < steps; ++i)
+      if (update(sk)) return 2;
     CHECK_HIP(hipEventRecord(e1, stream));
     CHECK_HIP(hipEventSynchronize(e1));
     if (moe_step_status(h) != MOE_OK) {
@@ -259,13 +320,15 @@ int main(int argc, char** argv) {
     }
     float ms = 0.f;
     CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
-    std::printf("%s skip=0x%02x grid=%d: %d updates, %.4f ms/update, %.0f tokens/s\n", sh->name, skip,
-                moe_step_grid_size(h), steps, ms / steps, sh->T * steps / (ms * 1e-3));
+    std::printf("%s skip=0x%03x grid=%d: %d updates of %d launch(es), %.4f ms/update, %.0f tokens/s\n",
+                inputs.empty() ? sh->name : inputs.c_str(), skip, moe_step_grid_size(h), steps, M, ms / steps,
+                (double)sh->T * M * steps / (ms * 1e-3));
     std::fflush(stdout);
   }
   moe_step_destroy(h);
-  for (void* p : {dx_in, dt, (void*)params, (void*)grads, (void*)m, (void*)v, (void*)dxg, (void*)stats})
+  for (void* p : {(void*)dx_in, (void*)dt, (void*)params, (void*)grads, (void*)m, (void*)v, (void*)dxg, (void*)stats})
     CHECK_HIP(hipFree(p));
+  if (bias) CHECK_HIP(hipFree(bias));
   CHECK_HIP(hipStreamDestroy(stream));
   return 0;
 }

@@ -746,7 +746,7 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
       posl[tid] = pos;
     }
     __syncthreads();
-    if constexpr (sizeof(T) == 2) {
+    if (sizeof(T) == 2 && !(p.flags & 0x100000u)) {
       // dispatch gather: the token row of each routed row of this block is
       // copied to its sorted position (xs, [N, d] in expert order), so the
       // expert products read contiguous rows
@@ -1542,7 +1542,7 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E, k = p.k;
 
-  if (want_dx) p.k <= 2 ? dx_tokens<T, 4>(p) : dx_tokens<T, 1>(p);
+  if (want_dx && !(p.flags & 0x200000u)) p.k <= 2 ? dx_tokens<T, 4>(p) : dx_tokens<T, 1>(p);
 
   // loss of this launch, summed over workgroups in index order
   if (lwg == 0 && p.stats) {
