@@ -479,8 +479,15 @@ struct Frags {
   u32x4_t a0, a1, b0, b1;
 };
 
-// GELU on both A fragments of a chunk (bf16, the direct-to-LDS path)
+// GELU on both A fragments of a chunk (bf16, the direct-to-LDS path).  It is
+// called right after the pipeline block whose wait completes the fragments'
+// LDS reads.  To the compiler those registers were written by an earlier asm
+// statement, so it could hoist this arithmetic above the waiting block and read
+// them before the data lands; the empty volatile asm with in/out operands
+// stays after that block (volatile asm statements keep their order) and the
+// arithmetic depends on its outputs.
 __device__ __forceinline__ void gelu_a(Frags& f) {
+  asm volatile("" : "+v"(f.a0), "+v"(f.a1));
   uint4 a0 = {f.a0[0], f.a0[1], f.a0[2], f.a0[3]}, a1 = {f.a1[0], f.a1[1], f.a1[2], f.a1[3]};
   gelu_frag<uint16_t>(a0);
   gelu_frag<uint16_t>(a1);
