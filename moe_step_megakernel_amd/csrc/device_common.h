@@ -277,6 +277,24 @@ __device__ __forceinline__ bool wait_for(const Ctrl& c, const unsigned* p, unsig
   return true;
 }
 
+// Polls *p (relaxed, agent scope) until it is at least target (barrier
+// targets only grow: within a launch with the barrier index, across launches
+// with the launch number); false on timeout or when another workgroup already
+// gave up.
+__device__ __forceinline__ bool wait_reached(const Ctrl& c, const unsigned* p, unsigned target) {
+  const uint64_t t0 = wall_clock64();
+  unsigned polls = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if ((++polls & 255u) == 0u) {
+      if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+          wall_clock64() - t0 > c.limit)
+        return give_up(c);
+    }
+  }
+  return true;
+}
+
 // Polls *p (relaxed, agent scope) until it is at least target; false on
 // timeout or when another workgroup already gave up.
 __device__ __forceinline__ bool wait_count(const Ctrl& c, const int* p, int target) {
@@ -312,12 +330,13 @@ __device__ __forceinline__ bool wait_count(const Ctrl& c, const int* p, int targ
 //   it).  The workgroup that brings the counter to members * hk arrived last on
 //   its XCD: all its XCD's workgroups had their stores in that L2 before they
 //   counted, so its one write-back covers them all; it then stores `target`
-//   into the XCD's arrival slot.  Workgroup 0 polls the XCD slots and stores the
-//   generation.  The membership comes from the hardware register in this very
+//   into the XCD's arrival slot.  Every workgroup polls the slots of the XCDs
+//   that have members (one lane each) and acquires once all eight hold the
+//   target.  The membership comes from the hardware register in this very
 //   launch, so it holds whatever the dispatch order was.
 //
-// Everyone polls the generation word with relaxed loads (a sleep between polls)
-// and acquires once afterwards.  Returns false if a wait timed out or another
+// Polling uses relaxed loads with a sleep between polls, and each poller
+// acquires once afterwards.  Returns false if a wait timed out or another
 // workgroup already gave up; the caller then skips all further phases so that
 // every workgroup still exits.
 __device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, BarrierState* bs, int hk) {
@@ -343,17 +362,24 @@ __device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, Bar
     }
   }
   __syncthreads();
+  if (!per_wg) {
+    // every workgroup polls the arrival slots of the XCDs that have members
+    // itself (eight lines, one lane each): no relay through a generation word.
+    // "At least": an XCD whose workgroups have all passed this barrier may
+    // already have stored the next barrier's target before a slow poller saw
+    // this one.
+    if (tid < kMaxXcd && bs->xall[tid] > 0u && !wait_reached(c, c.xcd + 32 * (9 + tid), target)) bs->flag = 0u;
+    if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    return bs->flag != 0u;
+  }
   if (blockIdx.x == 0) {
     bool ok = true;
-    if (per_wg) {
-      for (int w = tid; w < (int)gridDim.x; w += kThreads)
-        if (w != 0 && !wait_for(c, c.arrive + (size_t)w * 32, target)) {
-          ok = false;
-          break;
-        }
-    } else if (tid < kMaxXcd && bs->xall[tid] > 0u) {
-      ok = wait_for(c, c.xcd + 32 * (9 + tid), target);
-    }
+    for (int w = tid; w < (int)gridDim.x; w += kThreads)
+      if (w != 0 && !wait_for(c, c.arrive + (size_t)w * 32, target)) {
+        ok = false;
+        break;
+      }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (!ok) bs->flag = 0u;
     if (hk == 0) {
@@ -372,21 +398,26 @@ __device__ __forceinline__ bool grid_barrier(const Ctrl& c, unsigned target, Bar
         __hip_atomic_store(c.xcd + tid, bs->xall[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(c.xcd + 32 * (1 + tid), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (tid == 0) bs->xmem = bs->xall[bs->xcc & (kMaxXcd - 1)];
       __builtin_amdgcn_s_waitcnt(0x0F70);   // these stores are performed before the generation
     }
     __syncthreads();
     if (tid == 0 && bs->flag != 0u)
       __hip_atomic_store(c.gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else if (tid == 0) {
-    if (per_wg) __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(c.arrive + (size_t)blockIdx.x * 32, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!wait_for(c, c.gen, target)) bs->flag = 0u;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (hk == 0)
-      bs->xmem = __hip_atomic_load(c.xcd + (bs->xcc & (kMaxXcd - 1)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (hk == 0) {
+    // every workgroup keeps the membership counts (which XCD slots to poll,
+    // and how many arrivals complete its own XCD)
+    if (blockIdx.x != 0 && tid < kMaxXcd)
+      bs->xall[tid] = __hip_atomic_load(c.xcd + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) bs->xmem = bs->xall[bs->xcc & (kMaxXcd - 1)];
+    __syncthreads();
+  }
   return bs->flag != 0u;
 }
 
