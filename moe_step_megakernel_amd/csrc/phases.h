@@ -24,7 +24,7 @@
 namespace moe {
 
 constexpr int kPhases = 8;
-constexpr int kMetaBytes = 2560;
+constexpr int kMetaBytes = 3072;
 // OCC workgroups per compute unit: the kernel is built for one (all of a
 // SIMD's registers per wave, 4-stage GEMM pipeline) or two (at most 256
 // registers per wave, 2-stage pipeline, half the LDS each).
@@ -61,6 +61,11 @@ struct Meta {
   int cpre[kMaxExperts + 1];    // chunks of the experts before rank r, in ord order
   int nsplit;                   // experts with more than one chunk
   int splitlist[kMaxExperts];   // those experts, ascending
+  // skewed routing on a grid of 8 x P workgroups: the (expert, chunk) units of
+  // the weight-gradient products dealt to this workgroup's XCD (x = b % 8),
+  // packed as expert | chunk << 8, in the order its workgroups take them
+  int nxu;
+  int xunit[kMaxExperts + kMaxExperts / 2 + 1];
   float red[8];                 // block reductions
   BarrierState bar;             // grid-barrier bookkeeping (result broadcast, XCD membership)
 };
@@ -178,9 +183,13 @@ __device__ __forceinline__ Span xcd_span_last(int n) {
 struct WItem {
   int e, c, t;   // expert, chunk, tile within the expert
 };
+// With a grid of 8 x P workgroups, skewed routing keeps each (expert, chunk)
+// unit on one XCD (route_order assigns the units to XCDs, longest first, to the
+// least loaded one), so the unit's operand rows are fetched into one L2 only;
+// the XCD's P workgroups take its tiles in a snake in that unit order.
 struct DealW {
   Span sp;
-  bool snake;
+  bool snake, xl;
   int G, w, tpe, n;
   __device__ __forceinline__ int count() const {
     if (!snake) return sp.count();
@@ -195,6 +204,10 @@ struct DealW {
       return {q / tpe, 0, q % tpe};
     }
     const int q = i * G + ((i & 1) ? G - 1 - w : w);
+    if (xl) {
+      const int u = meta.xunit[q / tpe];
+      return {u & 0xff, u >> 8, q % tpe};
+    }
     int r = 0;
     while (r + 1 < E && meta.cpre[r + 1] * tpe <= q) ++r;
     const int rem = q - meta.cpre[r] * tpe;
@@ -204,10 +217,11 @@ struct DealW {
 __device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int E, int tpe) {
   DealW dl;
   dl.snake = meta.skewed != 0;
-  dl.G = gridDim.x;
-  dl.w = blockIdx.x;
+  dl.xl = dl.snake && (gridDim.x & 7) == 0;
+  dl.G = dl.xl ? (int)(gridDim.x >> 3) : (int)gridDim.x;   // the snake runs over the XCD's workgroups
+  dl.w = dl.xl ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   dl.tpe = tpe;
-  dl.n = tpe * (dl.snake ? meta.cpre[E] : E);
+  dl.n = tpe * (dl.xl ? meta.nxu : dl.snake ? meta.cpre[E] : E);
   dl.sp = xcd_span(dl.n);
   return dl;
 }
@@ -305,12 +319,18 @@ __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot
 template <typename T, int EGT, int EG0, int TL, int PG>
 __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x, float4* wl,
                                                     float (&acc)[TL][kMaxExperts], int tok, int nmine, int s_me,
-                                                    int S, int DC, int EG) {
+                                                    int S, int wbudget, int EG) {
   const int tid = threadIdx.x, d = p.d, E = p.E;
 #pragma unroll
   for (int u = 0; u < TL; ++u)
 #pragma unroll
     for (int e = 4 * EG0; e < 4 * (EG0 + EGT); ++e) acc[u][e] = 0.f;
+  // only this pass's expert groups are staged, so a chunk holds as many
+  // columns as the budget allows for NG groups
+  const int NG = min(EGT, EG - EG0);
+  if (NG <= 0) return;
+  int DC = (wbudget / (NG * 16)) / (8 * S) * (8 * S);
+  DC = min(max(DC, 8 * S), ceil_div(d, 8 * S) * (8 * S));
   for (int c0 = 0; c0 < d; c0 += DC) {
     const int dc = min(DC, ceil_div(d - c0, 8 * S) * (8 * S));
     const int ni = dc / (8 * S);
@@ -330,8 +350,8 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
     __syncthreads();
     // all of a thread's loads are issued before its LDS stores (16 per batch)
 #pragma unroll 16
-    for (int q = tid; q < dc * EG; q += kThreads) {
-      const int cl = q / EG, eg = q % EG;
+    for (int q = tid; q < dc * NG; q += kThreads) {
+      const int cl = q / NG, gl = q % NG, eg = EG0 + gl;
       const int i = cl / (8 * S), rem = cl % (8 * S), s = rem >> 3, j = rem & 7;
       const int c = c0 + cl;
       float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -346,7 +366,7 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
         }
         w = make_float4(v[0], v[1], v[2], v[3]);
       }
-      wl[((i * 8 + j) * EG + eg) * S + s] = w;
+      wl[((i * 8 + j) * NG + gl) * S + s] = w;
     }
     __syncthreads();
     for (int i0 = 0; i0 < ni; i0 += PG) {
@@ -362,11 +382,10 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
             // with several tokens per lane, W_r reads are not hoisted across
             // rows j, so the reads in flight do not outgrow the register file
             if (TL > 1) asm volatile("" ::: "memory");
-            const float4* wr = wl + ((i0 + v) * 8 + j) * EG * S + s_me;
+            const float4* wr = wl + ((i0 + v) * 8 + j) * NG * S + s_me;
             float4 w[EGT];
 #pragma unroll
-            for (int eg = 0; eg < EGT; ++eg)
-              w[eg] = EG0 + eg < EG ? wr[(EG0 + eg) * S] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int eg = 0; eg < EGT; ++eg) w[eg] = eg < NG ? wr[eg * S] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < TL; ++u)
 #pragma unroll
@@ -446,7 +465,7 @@ __device__ __forceinline__ void router_reduce(float (&acc)[TL][kMaxExperts], flo
 // (t_me, s_me) covers tokens b0 + t_me TL + u of column segment s_me.
 template <typename T, int OCC, int TL>
 __device__ __forceinline__ void router_block(const KParams& p, const T* x, float4* wl, float* zacc, int b0, int nb,
-                                             int t_me, int s_me, int S, int DC, int EG, int EP, int wbudget) {
+                                             int t_me, int s_me, int S, int EG, int EP, int wbudget) {
   const int E = p.E;
   const int tok = b0 + t_me * TL;
   const int nmine = min(TL, max(0, nb - t_me * TL));
@@ -455,27 +474,27 @@ __device__ __forceinline__ void router_block(const KParams& p, const T* x, float
   constexpr int PG = TL == 1 ? 4 : 2;
   float acc[TL][kMaxExperts];
   if (EG <= 4) {
-    router_segment_sums<T, 4, 0, TL, PG>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_segment_sums<T, 4, 0, TL, PG>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
     router_reduce<0, 4, TL>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
   } else if constexpr (TL == 1 && OCC == 1) {
     // more than 16 experts: two passes over the columns, 8 expert groups
     // each (one pass over all 64 would not fit the register file)
-    router_segment_sums<T, 8, 0, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
-    router_segment_sums<T, 8, 8, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_segment_sums<T, 8, 0, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
+    router_segment_sums<T, 8, 8, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
     router_reduce<0, 16, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
   } else if constexpr (TL == 1) {
     // with half the registers: passes of 16 experts, each summed over the
     // segments before the next one starts
-    router_segment_sums<T, 4, 0, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_segment_sums<T, 4, 0, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
     router_reduce<0, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
-    router_segment_sums<T, 4, 4, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+    router_segment_sums<T, 4, 4, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
     router_reduce<4, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
     if (EG > 8) {
-      router_segment_sums<T, 4, 8, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+      router_segment_sums<T, 4, 8, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
       router_reduce<8, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
     }
     if (EG > 12) {
-      router_segment_sums<T, 4, 12, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, DC, EG);
+      router_segment_sums<T, 4, 12, 1, 4>(p, x, wl, acc, tok, nmine, s_me, S, wbudget, EG);
       router_reduce<12, 4, 1>(acc, zacc, wl, E, EP, S, nb, t_me, s_me, wbudget);
     }
   }
@@ -540,16 +559,17 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   // (the reads of padded expert groups may run up to 16 * S float4 past the chunk)
   const int wbudget = kScratch - 256 - TP * EP * 4 - 16 * 64 * 16;
   // a chunk holds at least one 8-column piece per segment for every expert
-  // group (8 EG 16 <= 2 KB always fits, so this ends with DC >= 8 S)
-  while (S > 1 && 8 * S * EG * 16 > wbudget) S >>= 1;
-  int DC = (wbudget / (EG * 16)) / (8 * S) * (8 * S);                           // columns per chunk
-  DC = min(DC, ceil_div(d, 8 * S) * (8 * S));
+  // group a pass stages (all EG groups in one pass up to 16 experts, else 8
+  // groups per pass with a whole register file, 4 with half of it; 8 * 8 * 16
+  // bytes always fit, so this ends with chunks of at least 8 S columns)
+  const int NGmax = EG <= 4 ? EG : (OCC == 1 ? 8 : 4);
+  while (S > 1 && 8 * S * NGmax * 16 > wbudget) S >>= 1;
   const int t_me = tid / S, s_me = tid % S;
 
   for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
     const int nb = min(TP, t_hi - b0);
-    if (TL > 1) router_block<T, OCC, kTL>(p, x, wl, zacc, b0, nb, t_me, s_me, S, DC, EG, EP, wbudget);
-    else router_block<T, OCC, 1>(p, x, wl, zacc, b0, nb, t_me, s_me, S, DC, EG, EP, wbudget);
+    if (TL > 1) router_block<T, OCC, kTL>(p, x, wl, zacc, b0, nb, t_me, s_me, S, EG, EP, wbudget);
+    else router_block<T, OCC, 1>(p, x, wl, zacc, b0, nb, t_me, s_me, S, EG, EP, wbudget);
     // token_topk over each group of EP lanes (the group never crosses a wave)
     for (int g0 = 0; g0 < nb; g0 += TPI) {
       const int tok = b0 + g0 + slot;
@@ -714,6 +734,47 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     meta.cpre[E] = s;
   }
   __syncthreads();
+  if (meta.skewed && (G & 7) == 0) {
+    // (expert, chunk) units of the weight-gradient products, costed by their
+    // rows; ranked longest first (ties: expert order, then chunk), then each
+    // goes to the least loaded of the 8 XCDs (lowest index on ties).  Every
+    // workgroup computes the same assignment and keeps its own XCD's units.
+    int* ucost = posl + kThreads;            // [kThreads] unit costs, in expert-rank order
+    int* uid = ucost + kThreads;             // [kThreads] the units
+    int* scost = uid + kThreads;             // [kThreads] costs, longest first
+    int* suid = scost + kThreads;            // [kThreads] units, longest first
+    const int nu = meta.cpre[E];             // units: the chunks of every expert
+    if (tid < E) {
+      const int e = meta.ord[tid];
+      for (int c = 0; c < meta.nch[e]; ++c) {
+        ucost[meta.cpre[tid] + c] = meta.nch[e] > 1 ? min(meta.kc, meta.cnt[e] - c * meta.kc) : meta.cnt[e];
+        uid[meta.cpre[tid] + c] = e | (c << 8);
+      }
+    }
+    __syncthreads();
+    if (tid < nu) {
+      int rank = 0;
+      for (int v = 0; v < nu; ++v) rank += (ucost[v] > ucost[tid]) || (ucost[v] == ucost[tid] && v < tid);
+      scost[rank] = ucost[tid];
+      suid[rank] = uid[tid];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const int mx = (int)(blockIdx.x & 7);
+      int m = 0;
+      for (int i = 0; i < nu; ++i) {
+        int x = 0;
+#pragma unroll
+        for (int y = 1; y < 8; ++y)
+          if (load[y] < load[x]) x = y;
+        load[x] += scost[i];
+        if (x == mx) meta.xunit[m++] = suid[i];
+      }
+      meta.nxu = m;
+    }
+    __syncthreads();
+  }
   if (tid < E) base[tid] = meta.off[tid] + sp[tid];
   if (lwg == 0 && tid < E && p.dbg_counts) p.dbg_counts[tid] = meta.cnt[tid];
   if (skip_scatter) return;
