@@ -144,7 +144,6 @@ struct moe_step {
   void* xs;
   float* wpart2;
   float* wpart1;
-  char* zero;
   unsigned* ctrl;
 };
 
@@ -184,8 +183,7 @@ static int select_kernel(const moe_step_config& c, int cus, moe_step& h, char* e
 
 // Lays out the arena of h (h.cfg and h.grid set) and returns its size in
 // bytes; with a base address, also points h's sub-buffers into it.  The
-// barrier words (ctrl_words of them) come first and the 256-byte zero page
-// right after them.
+// barrier words (ctrl_words of them) come first.
 static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
   const moe_step_config& c = h.cfg;
   const int d = c.d_model, f = c.d_ff, E = c.n_experts, k = c.top_k;
@@ -212,7 +210,6 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
     return o;
   };
   const size_t o_ctrl = take(ctrl_words * sizeof(unsigned));
-  const size_t o_zero = take(256);
   const size_t o_idx = take(N * 4), o_gate = take(N * 4), o_dz = take(N * 4);
   const size_t o_hist = take((size_t)h.grid * E * 4);
   const size_t o_perm = take(N * 4), o_inv = take(N * 4);
@@ -243,7 +240,6 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
   if (base) {
     char* a = base;
     h.ctrl = reinterpret_cast<unsigned*>(a + o_ctrl);
-    h.zero = a + o_zero;
     h.idx = reinterpret_cast<int*>(a + o_idx);
     h.gate = reinterpret_cast<float*>(a + o_gate);
     h.dzsel = reinterpret_cast<float*>(a + o_dz);
@@ -273,18 +269,17 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
 // ---------------------------------------------------------------------------
 // The arena of the allocation-free entry point: a static device array (each
 // GPU the library runs on holds its own copy until the process ends).  The
-// barrier words (for grids of up to 1003 workgroups) and the zero page sit at
-// fixed offsets at its start, so no other call's buffers overlap them.
+// barrier words (for grids of up to 1003 workgroups) sit at its start, so no
+// other call's buffers overlap them.
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) char scratch[MOE_STEP_STATIC_SCRATCH_BYTES];
 constexpr size_t kStaticCtrlWords = 1024 * 32;   // grids of up to 1003 workgroups
 
 // Before a static-arena launch: the barrier words, status and abort word of
-// the previous call are cleared and the zero page is zeroed (a fill kernel,
-// so the call stays one stream-ordered sequence of launches).
-__global__ void static_clear(unsigned* ctrl, int words, uint32_t* zero) {
+// the previous call are cleared (a fill kernel, so the call stays one
+// stream-ordered sequence of launches).
+__global__ void static_clear(unsigned* ctrl, int words) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) ctrl[i] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x < 64) zero[threadIdx.x] = 0u;
 }
 
 // After it: the device status bits of the launch into stats[3].
@@ -458,7 +453,6 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.xs = h->xs;
   p.wpart2 = h->wpart2;
   p.wpart1 = h->wpart1;
-  p.zero = h->zero;
   p.ctrl.gen = h->ctrl;
   p.ctrl.status = h->ctrl + 32;
   p.ctrl.abort = h->ctrl + 64;
@@ -482,8 +476,7 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   // guarantees it but costs about 19 us more per update.
   const bool coop = (run_flags & MOE_RUN_COOPERATIVE) != 0u;
   if (static_arena) {
-    hipLaunchKernelGGL(static_clear, dim3(16), dim3(256), 0, stream, h->ctrl, (int)ctrl_words(h->grid),
-                       reinterpret_cast<uint32_t*>(h->zero));
+    hipLaunchKernelGGL(static_clear, dim3(16), dim3(256), 0, stream, h->ctrl, (int)ctrl_words(h->grid));
     if ((he = hipGetLastError()) != hipSuccess) {
       set_err(err, "clearing the barrier words: %s", hipGetErrorString(he));
       return MOE_ERR_HIP;

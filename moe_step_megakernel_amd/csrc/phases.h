@@ -120,7 +120,6 @@ struct KParams {
   float* wpart2;     // partial dW2 tiles of split contractions [blocks][tiles per expert][128 x 128]
   float* wpart1;     // the same for dW1
   void* xs;          // [N, d] token rows in expert order (bf16 mode), written by route_order
-  const char* zero;  // 256 zero bytes (source of out-of-range tile elements)
   Ctrl ctrl;
 };
 
@@ -889,7 +888,7 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
         st8x<NS == 2>(gp + o, da);
       }
     };
-    gemm::tile<T, NS, false, true>(lds, A, B, d, p.zero, epi);
+    gemm::tile<T, NS, false, true>(lds, A, B, d, epi);
     if (publish) {
       // every wave's stores of the tile have reached L2; one agent-scope
       // release for the workgroup (the XCD's L2 is written back), then the count
@@ -944,8 +943,8 @@ __device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& me
       }
     };
     // under the recomputation rule act holds H and the A fragments pass through GELU
-    if (p.recompute) gemm::tile<T, NS, false, true, true>(lds, A, B, f, p.zero, epi);
-    else gemm::tile<T, NS, false, true, false>(lds, A, B, f, p.zero, epi);
+    if (p.recompute) gemm::tile<T, NS, false, true, true>(lds, A, B, f, epi);
+    else gemm::tile<T, NS, false, true, false>(lds, A, B, f, epi);
   }
   return true;
 }
@@ -1234,7 +1233,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
   gemm::Operand B{bbase, N, nullptr, 1, pe, rows, N, n0};
   if (wi.c > 0) {
     float* pt = part + ((long)(meta.pbase[e] + wi.c - 1) * tpe + wi.t) * (gemm::BM * gemm::BN);
-    gemm::tile<T, NS, true, true, GA>(lds, A, B, rows, p.zero, [&](int r, int c, const float (&v)[8]) {
+    gemm::tile<T, NS, true, true, GA>(lds, A, B, rows, [&](int r, int c, const float (&v)[8]) {
       F8 o;
 #pragma unroll
       for (int u = 0; u < 8; ++u) o.v[u] = v[u];
@@ -1244,7 +1243,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
   }
   float sq = 0.f;
   gemm::tile<T, NS, true, true, GA>(
-      lds, A, B, rows, p.zero,
+      lds, A, B, rows,
       [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
         if (m0 + r < M && n0 + c < N) {
           F8 nv = cvt8(old);
@@ -1323,7 +1322,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
                       nt * gemm::BN, min(gemm::BN, f - nt * gemm::BN), d, 0};
       const int n0 = nt * gemm::BN;
       gemm::tile<T, NS, false, false>(
-          lds, A, B, d, p.zero,
+          lds, A, B, d,
           [&](int r, int c, const float (&v)[8], const Raw8<T>& graw) {
             if (r < mrows && n0 + c < f) {
               F8 g8 = cvt8(graw);
@@ -1467,7 +1466,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
                       nt * gemm::BN, min(gemm::BN, d - nt * gemm::BN), f, 0};
       const int n0 = nt * gemm::BN;
       gemm::tile<T, NS, false, false>(
-          lds, A, B, f, p.zero,
+          lds, A, B, f,
           [&](int r, int c, const float (&v)[8], int slot) {
             if (r < mrows && n0 + c < d) {
               F8 o;

@@ -346,9 +346,9 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
 
 
 // ---------------------------------------------------------------------------
-// bf16 tiles: direct-to-LDS loads (global_load_lds_dwordx4), four LDS stages,
-// so the loads of three k-tiles are in flight while the matrix cores work on
-// the fourth, at no register cost.  Each wave instruction fills 1 KB of LDS
+// bf16 tiles: direct-to-LDS loads (buffer_load_dwordx4 ... lds), up to four
+// LDS stages, so the loads of three k-tiles are in flight while the matrix
+// cores work on the fourth, at no register cost.  Each wave instruction fills 1 KB of LDS
 // contiguously (lane l -> bytes 16l..16l+15), so bank conflicts on the MFMA
 // reads are avoided by an XOR swizzle of 16-byte units instead of padding:
 //  * K-rows operand, LDS [128 rows][128 B]: logical k-unit u of row r sits in
@@ -357,8 +357,7 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
 //    k-row r sits in physical slot s ^ (4 * (r & 3)).  Half a transpose read
 //    (32 lanes) covers 4 k-rows x 64 bytes; the XOR puts the 4 rows' 64-byte
 //    pieces in the 4 distinct quarters of the 64 banks.
-// Lanes whose element is out of range load from a zero page instead.  The
-// loop waits on the vector-memory counter itself and synchronises with a bare
+// Out-of-range elements are zeroed by the loads' range check.  The loop waits on the vector-memory counter itself and synchronises with a bare
 // s_barrier, so the loads of later k-tiles stay in flight across it.
 // ---------------------------------------------------------------------------
 constexpr int DMA_OP = 16384;                  // bytes per operand per stage
@@ -368,16 +367,9 @@ constexpr int DMA_STAGE = 2 * DMA_OP;
 constexpr int dma_lds_bytes(int NS) { return NS * DMA_STAGE > BM * CROW * 4 ? NS * DMA_STAGE : BM * CROW * 4; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void glb_void_t;
 
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
-}
-
-// one direct-to-LDS load: 16 bytes per lane from src to LDS byte address
-// lds_off + 16 * lane (lds_off wave-uniform)
-__device__ __forceinline__ void dma16(const char* src, uint32_t lds_off) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(uintptr_t)lds_off, 16, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) for n in {0, 8, 16}; expcnt and lgkmcnt left alone
@@ -393,24 +385,43 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// The direct-to-LDS loads of one operand.  Wave w's instruction i (0..3)
-// fills LDS bytes [1024 (4w + i), +1024) of the operand's stage:
+// The direct-to-LDS loads of one operand, as buffer loads.  Wave w's
+// instruction i (0..3) fills LDS bytes [1024 (4w + i), +1024) of the
+// operand's stage:
 //  * K-rows: LDS row r = 8 (4w + i) + lane / 8 (128 bytes of k), physical
 //    16-byte unit lane % 8, which holds logical k-unit u = (lane % 8) ^
 //    ((4i + lane / 16) % 8) (the swizzle u ^ ((r / 2) % 8));
 //  * MN-rows: k-row kk = 16w + 4i + lane / 16 of the stage, physical slot
 //    lane % 16, which holds columns mn0 + 8 s.. with s = (lane % 16) ^
 //    4 ((lane / 16) % 4) (the swizzle s ^ 4 (kk % 4)).
-// Along k a lane's source only moves by a fixed stride, so each lane keeps
-// its k-tile-0 address per instruction and the number of k-tiles for which
-// that address is in range; later k-tiles, and lanes out of range, load the
-// zero page.  Issuing a k-tile then costs one add and one select per
-// instruction, with no multiplies or branches.
+// Every load goes through one wave-uniform buffer descriptor per operand and
+// k-tile whose base is the tile's source in that k-tile (a scalar 64-bit add
+// per k-tile); each lane keeps a fixed 32-bit offset from it per instruction.
+// Out-of-range elements come back as zeros from the descriptor's range check:
+// a lane whose row (K-rows) or column (MN-rows) lies outside the operand gets
+// offset kOutside, at or beyond any record count; for MN-rows the record
+// count of k-tile kt is the bytes of rows still in range from its base, so
+// the ragged k-rows of the last k-tile read as zero.  A K-rows operand whose
+// k extent is not a multiple of 64 re-derives its offsets in the last k-tile.
+// Issuing a k-tile so costs scalar work only (plus that one tail).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutside = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer: 32-bit data format, no swizzle
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 template <bool MN>
 struct DmaOp {
-  const char* ptr[4];  // this lane's source in k-tile 0, per instruction
-  int nv[4];           // k-tiles in which that source is in range
-  long step;           // source bytes per k-tile (wave-uniform)
+  uint64_t base;       // source of k-tile 0 (wave-uniform)
+  uint64_t step;       // source bytes per k-tile (wave-uniform)
+  int lim;             // K-rows: k elements in range; MN-rows: k-rows in range
+  int rowbytes;        // MN-rows: bytes per k-row (ld * 2)
+  int caprows;         // MN-rows: k-rows whose bytes stay below kOutside
+  uint32_t voff[4];    // this lane's offset from the k-tile's base, per instruction
   uint32_t wofs;       // this wave's LDS byte offset within an operand stage (wave-uniform)
 
   __device__ __forceinline__ void init(const Operand& o) {
@@ -418,34 +429,56 @@ struct DmaOp {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wofs = (uint32_t)w * 4096u;
     if constexpr (!MN) {
+      base = uniform_u64((uint64_t)(uintptr_t)(o.base + (long)o.p0 * o.ld * 2));
       step = 128;
+      lim = __builtin_amdgcn_readfirstlane(o.lim);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * (4 * w + i) + (lane >> 3);
         const int unit = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
-        const bool ok = row < o.nrows;
-        ptr[i] = ok ? o.base + map_row(o, o.p0 + row) * o.ld * 2 + unit * 16 : o.base;
-        nv[i] = ok ? max(0, (o.lim - unit * 8 + 63) >> 6) : 0;
+        voff[i] = row < o.nrows ? (uint32_t)(row * o.ld * 2 + unit * 16) : kOutside;
       }
     } else {
-      step = 128 * o.ld;
+      base = uniform_u64((uint64_t)(uintptr_t)(o.base + ((long)o.p0 * o.ld + o.mn0) * 2));
+      step = uniform_u64((uint64_t)(128L * o.ld));
+      lim = __builtin_amdgcn_readfirstlane(o.nrows);
+      rowbytes = __builtin_amdgcn_readfirstlane((int)o.ld * 2);
+      caprows = (int)(kOutside / (uint32_t)rowbytes);
       const int slot = (lane & 15) ^ (4 * ((lane >> 4) & 3));
-      const int mn = o.mn0 + slot * 8;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kk0 = 16 * w + 4 * i + (lane >> 4);
-        ptr[i] = o.base + ((long)(o.p0 + kk0) * o.ld + mn) * 2;
-        nv[i] = mn < o.lim ? max(0, (o.nrows - kk0 + 63) >> 6) : 0;
+        voff[i] = o.mn0 + slot * 8 < o.lim ? (uint32_t)(kk0 * o.ld * 2 + slot * 16) : kOutside;
       }
     }
   }
 
-  // the loads of k-tile kt into the operand stage at st
-  __device__ __forceinline__ void issue(int kt, char* st, const char* zero) const {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st)) + wofs;
-    const long off = (long)kt * step;
+  // the loads of k-tile kt into the operand stage at LDS byte address lst
+  __device__ __forceinline__ void issue(int kt, uint32_t lst) const {
+    const uint32_t lbase = lst + wofs;
+    const uint64_t b = base + (uint64_t)kt * step;
+    // K-rows: k elements of this k-tile in range; MN-rows: k-rows in range
+    const int left = lim - 64 * kt;
+    uint32_t nrec = kOutside;
+    if constexpr (MN) nrec = left <= 0 ? 0u : left >= caprows ? kOutside : (uint32_t)(left * rowbytes);
+    const rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)b, (short)0, (int)nrec, kRsrcWord3);
+    if (MN || __builtin_expect(left >= 64, 1)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(kt < nv[i] ? ptr[i] + off : zero, base + 1024u * i);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(uintptr_t)(lbase + 1024u * i), 16, (int)voff[i],
+                                                 0, 0, 0);
+    } else {
+      // the last k-tile of a K-rows operand whose k extent is not a multiple
+      // of 64: units at or beyond the limit read as zero
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int unit = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
+        const uint32_t v = unit * 8 < left ? voff[i] : kOutside;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(uintptr_t)(lbase + 1024u * i), 16, (int)v, 0, 0,
+                                                 0);
+      }
+    }
   }
 };
 
@@ -456,22 +489,50 @@ struct DmaOp {
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-// LDS byte address of this lane's fragment (K-rows: the b128 read; MN-rows:
-// the first of the two transpose reads, the second is 1024 bytes further)
+// Byte offset of this lane's fragment within an operand stage (K-rows: the
+// b128 read; MN-rows: the first of the two transpose reads, the second is
+// 1024 bytes further).
 template <bool MN>
-__device__ __forceinline__ uint32_t dma_frag_addr(const char* st, int row0, int chunk) {
+__device__ __forceinline__ uint32_t dma_frag_off(int row0, int chunk) {
   const int lane = threadIdx.x & 63;
   if constexpr (!MN) {
     const int r = row0 + (lane & 31);
     const int u = chunk * 2 + (lane >> 5);
-    return lds_addr(st + r * 128 + ((u ^ ((r >> 1) & 7)) << 4));
+    return (uint32_t)(r * 128 + ((u ^ ((r >> 1) & 7)) << 4));
   } else {
     const int g = lane >> 4, j = lane & 15;
     const int r = chunk * 16 + 8 * (g >> 1) + (j >> 2);
     const int c = row0 + 16 * (g & 1) + 4 * (j & 3);
-    return lds_addr(st + r * 256 + (((c >> 3) ^ (4 * (r & 3))) << 4) + (c & 7) * 2);
+    return (uint32_t)(r * 256 + (((c >> 3) ^ (4 * (r & 3))) << 4) + (c & 7) * 2);
   }
 }
+
+// LDS addresses of one operand's fragments for this lane, split into a
+// register and an instruction offset.  Within a stage, the two 32-row blocks
+// of a K-rows operand are 4096 bytes apart (rows r and r + 32 share the
+// swizzle), so a register per k chunk serves both; the k chunks of an MN-rows
+// operand are 4096 bytes apart (16 k-rows), so a register per row block
+// serves all four.  The stage slot's offset is added to the register.
+template <bool MN>
+struct FragAddr {
+  static constexpr int NREG = MN ? 2 : 4;
+  uint32_t r[NREG];
+
+  __device__ __forceinline__ void init(uint32_t op0, int row0) {
+#pragma unroll
+    for (int q = 0; q < NREG; ++q)
+      r[q] = op0 + (MN ? dma_frag_off<true>(row0 + 32 * q, 0) : dma_frag_off<false>(row0, q));
+  }
+  // row block I (0, 1), k chunk C (0..3)
+  template <int I, int C>
+  __device__ __forceinline__ uint32_t reg() const {
+    return r[MN ? I : C];
+  }
+  template <int I, int C>
+  static constexpr int imm() {
+    return MN ? C * 4096 : I * 4096;
+  }
+};
 
 // The fragments of one 16-element k chunk: a0/a1 for the two 32-row blocks of
 // A (m), b0/b1 for those of B (n), 8 bf16 per lane each.
@@ -508,8 +569,9 @@ __device__ __forceinline__ u32x4_t join(const u32x2_t& lo, const u32x2_t& hi) {
 // whose read it could observe early.  Accumulators live in AGPRs.
 //   WAIT = 0: wait for every read; 1: leave this block's reads outstanding;
 //   -1: no wait.
-#define MOE_RD_K(d, a) "ds_read_b128 %[" d "], %[" a "]\n\t"
-#define MOE_RD_MN(d, a) "ds_read_b64_tr_b16 %[" d "l], %[" a "]\n\tds_read_b64_tr_b16 %[" d "h], %[" a "] offset:1024\n\t"
+#define MOE_RD_K(d, a) "ds_read_b128 %[" d "], %[" a "] offset:%[o" a "]\n\t"
+#define MOE_RD_MN(d, a) \
+  "ds_read_b64_tr_b16 %[" d "l], %[" a "] offset:%[o" a "]\n\tds_read_b64_tr_b16 %[" d "h], %[" a "] offset:%[o" a "h]\n\t"
 #define MOE_MFMA4                                                   \
   "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"      \
   "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"      \
@@ -517,7 +579,10 @@ __device__ __forceinline__ u32x4_t join(const u32x2_t& lo, const u32x2_t& hi) {
   "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
 #define MOE_ACC_OUT [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1])
 #define MOE_CUR_IN [a0] "v"(c.a0), [a1] "v"(c.a1), [b0] "v"(c.b0), [b1] "v"(c.b1)
-#define MOE_ADDR_IN [pa0] "v"(pa0), [pa1] "v"(pa1), [pb0] "v"(pb0), [pb1] "v"(pb1)
+#define MOE_ADDR_IN                                                                                  \
+  [pa0] "v"(pa0), [pa1] "v"(pa1), [pb0] "v"(pb0), [pb1] "v"(pb1), [opa0] "i"(OA0), [opa0h] "i"(OA0 + 1024), \
+      [opa1] "i"(OA1), [opa1h] "i"(OA1 + 1024), [opb0] "i"(OB0), [opb0h] "i"(OB0 + 1024), [opb1] "i"(OB1),  \
+      [opb1h] "i"(OB1 + 1024)
 // one pipeline block for a layout pair: READS issues the reads into the
 // output operands OUTS; NREAD is the number of LDS instructions in READS
 #define MOE_PIPE_BODY(READS, OUTS, NREAD, FINISH)                                                         \
@@ -545,7 +610,7 @@ struct Pipe;
 // A K-rows, B MN-rows (forward products)
 template <>
 struct Pipe<false, true> {
-  template <bool MMA, int WAIT>
+  template <bool MMA, int WAIT, int OA0, int OA1, int OB0, int OB1>
   __device__ __forceinline__ static void step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], uint32_t pa0,
                                               uint32_t pa1, uint32_t pb0, uint32_t pb1) {
     u32x4_t x0, x1;
@@ -559,7 +624,7 @@ struct Pipe<false, true> {
 // both K-rows (dH = dO W2^T, dXs = dA W1^T)
 template <>
 struct Pipe<false, false> {
-  template <bool MMA, int WAIT>
+  template <bool MMA, int WAIT, int OA0, int OA1, int OB0, int OB1>
   __device__ __forceinline__ static void step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], uint32_t pa0,
                                               uint32_t pa1, uint32_t pb0, uint32_t pb1) {
     u32x4_t x0, x1, y0, y1;
@@ -572,7 +637,7 @@ struct Pipe<false, false> {
 // both MN-rows (weight gradients: k runs over the routed tokens)
 template <>
 struct Pipe<true, true> {
-  template <bool MMA, int WAIT>
+  template <bool MMA, int WAIT, int OA0, int OA1, int OB0, int OB1>
   __device__ __forceinline__ static void step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], uint32_t pa0,
                                               uint32_t pa1, uint32_t pb0, uint32_t pb1) {
     u32x2_t x0l, x0h, x1l, x1h, y0l, y0h, y1l, y1h;
@@ -613,11 +678,24 @@ __device__ __forceinline__ void pipe_mma(const Frags& c, f32x16_t (&acc)[2][2]) 
 // LDS read has at least one block of matrix work to hide behind.  NS = 4 with
 // one workgroup per compute unit; NS = 2 when two workgroups share one (each
 // then has half the LDS, and the other workgroup's work covers the waits).
+
+// one pipeline block reading chunk C of the stage at LDS offset so from the
+// stage of slot 0
+template <bool MMA, int WAIT, int C, bool MN_A, bool MN_B>
+__device__ __forceinline__ void pipe_step(Frags& n, const Frags& c, f32x16_t (&acc)[2][2], const FragAddr<MN_A>& fa,
+                                          const FragAddr<MN_B>& fb, uint32_t so) {
+  using FA = FragAddr<MN_A>;
+  using FB = FragAddr<MN_B>;
+  Pipe<MN_A, MN_B>::template step<MMA, WAIT, FA::template imm<0, C>(), FA::template imm<1, C>(),
+                                  FB::template imm<0, C>(), FB::template imm<1, C>()>(
+      n, c, acc, fa.template reg<0, C>() + so, fa.template reg<1, C>() + so, fb.template reg<0, C>() + so,
+      fb.template reg<1, C>() + so);
+}
+
 template <int NS, bool MN_A, bool MN_B, bool GA, class Epi, class Pre>
-__device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
-                                         Epi&& epi, Pre&& pre) {
+__device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi,
+                                         Pre&& pre) {
   static_assert(NS >= 2 && NS <= 4, "wait_vm covers up to two k-tiles in flight behind the one awaited");
-  using P = Pipe<MN_A, MN_B>;
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -630,44 +708,38 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
   da.init(A);
   db.init(B);
   const int nk = (K + 63) / 64;
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
   lds_sync();  // the previous user of this LDS is done (its global stores may still be in flight)
   for (int j = 0; j < NS - 1 && j < nk; ++j) {
-    char* st = lds + j * DMA_STAGE;
-    da.issue(j, st, zero);
-    db.issue(j, st + DMA_OP, zero);
+    da.issue(j, l0 + j * DMA_STAGE);
+    db.issue(j, l0 + j * DMA_STAGE + DMA_OP);
   }
   if (nk > 0) {
     const int w = threadIdx.x >> 6;
     const int wm = w & 1, wn = w >> 1;
-    // this lane's fragment addresses in slot 0, per chunk
-    uint32_t fa0[4], fa1[4], fb0[4], fb1[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      fa0[c] = dma_frag_addr<MN_A>(lds, wm * 64, c);
-      fa1[c] = dma_frag_addr<MN_A>(lds, wm * 64 + 32, c);
-      fb0[c] = dma_frag_addr<MN_B>(lds + DMA_OP, wn * 64, c);
-      fb1[c] = dma_frag_addr<MN_B>(lds + DMA_OP, wn * 64 + 32, c);
-    }
+    FragAddr<MN_A> fa;
+    FragAddr<MN_B> fb;
+    fa.init(l0, wm * 64);
+    fb.init(l0 + DMA_OP, wn * 64);
     wait_vm(min(NS - 2, nk - 1));
     lds_barrier();
     if (NS - 1 < nk) {
-      char* nx = lds + (NS - 1) * DMA_STAGE;
-      da.issue(NS - 1, nx, zero);
-      db.issue(NS - 1, nx + DMA_OP, zero);
+      da.issue(NS - 1, l0 + (NS - 1) * DMA_STAGE);
+      db.issue(NS - 1, l0 + (NS - 1) * DMA_STAGE + DMA_OP);
     }
     Frags F0, F1, F2, F3;
     // With GA, the A fragments of each chunk pass through GELU once their
     // reads have completed (after the wait that covers them) and before the
     // MFMAs that use them.
-    P::template step<false, -1>(F0, F0, acc, fa0[0], fa1[0], fb0[0], fb1[0]);
-    P::template step<false, 0>(F1, F1, acc, fa0[1], fa1[1], fb0[1], fb1[1]);
+    pipe_step<false, -1, 0>(F0, F0, acc, fa, fb, 0u);
+    pipe_step<false, 0, 1>(F1, F1, acc, fa, fb, 0u);
     if constexpr (GA) gelu_a(F0);
     for (int kt = 0; kt < nk - 1; ++kt) {
       const uint32_t so = (uint32_t)(kt % NS) * DMA_STAGE;
       const uint32_t sn = (uint32_t)((kt + 1) % NS) * DMA_STAGE;
-      P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
+      pipe_step<true, 1, 2>(F2, F0, acc, fa, fb, so);
       if constexpr (GA) gelu_a(F1);
-      P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
+      pipe_step<true, 0, 3>(F3, F1, acc, fa, fb, so);
       if constexpr (GA) {
         gelu_a(F2);
         gelu_a(F3);
@@ -676,20 +748,19 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
       wait_vm(min(NS - 2, nk - 2 - kt));
       lds_barrier();
       if (kt + NS < nk) {
-        char* nx = lds + so;
-        da.issue(kt + NS, nx, zero);
-        db.issue(kt + NS, nx + DMA_OP, zero);
+        da.issue(kt + NS, l0 + so);
+        db.issue(kt + NS, l0 + so + DMA_OP);
       }
-      P::template step<true, -1>(F0, F2, acc, fa0[0] + sn, fa1[0] + sn, fb0[0] + sn, fb1[0] + sn);
-      P::template step<true, 1>(F1, F3, acc, fa0[1] + sn, fa1[1] + sn, fb0[1] + sn, fb1[1] + sn);
+      pipe_step<true, -1, 0>(F0, F2, acc, fa, fb, sn);
+      pipe_step<true, 1, 1>(F1, F3, acc, fa, fb, sn);
       if constexpr (GA) gelu_a(F0);
     }
     {
       // last k-tile: its chunks 0 and 1 are in flight or landed
       const uint32_t so = (uint32_t)((nk - 1) % NS) * DMA_STAGE;
-      P::template step<true, 1>(F2, F0, acc, fa0[2] + so, fa1[2] + so, fb0[2] + so, fb1[2] + so);
+      pipe_step<true, 1, 2>(F2, F0, acc, fa, fb, so);
       if constexpr (GA) gelu_a(F1);
-      P::template step<true, 0>(F3, F1, acc, fa0[3] + so, fa1[3] + so, fb0[3] + so, fb1[3] + so);
+      pipe_step<true, 0, 3>(F3, F1, acc, fa, fb, so);
       if constexpr (GA) {
         gelu_a(F2);
         gelu_a(F3);
@@ -712,9 +783,9 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
 // staging.
 // GA: the A operand holds H and the product uses gelu(H) (recomputation rule).
 template <typename T, int NS, bool MN_A, bool MN_B, bool GA = false, class Epi, class Pre = NoPre>
-__device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, const char* zero,
-                                     Epi&& epi, Pre&& pre = Pre()) {
-  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B, GA>(lds, A, B, K, zero, epi, pre);
+__device__ __forceinline__ void tile(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi,
+                                     Pre&& pre = Pre()) {
+  if constexpr (sizeof(T) == 2) tile_dma<NS, MN_A, MN_B, GA>(lds, A, B, K, epi, pre);
   else tile_reg<T, MN_A, MN_B, GA>(lds, A, B, K, epi, pre);
 }
 
