@@ -103,9 +103,7 @@ __device__ __forceinline__ void st8(uint16_t* p, const F8& f) {
 
 // Non-temporal forms, for outputs that are only read again in a later phase
 // and are too large to stay in the caches meanwhile: they do not displace the
-// operand lines the phase is still reusing.  The product phases use them in the
-// two-per-CU kernel (large batches); with one workgroup per CU the outputs are
-// small enough to stay cached and the plain stores measured no slower.
+// operand lines the phase is still reusing.
 typedef unsigned ntu4_t __attribute__((ext_vector_type(4)));
 typedef float ntf4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void st8nt(uint16_t* p, const F8& f) {
@@ -122,9 +120,14 @@ __device__ __forceinline__ void st8(float* p, const F8& f) {
   reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
 }
 
-template <bool NT, typename P>
-__device__ __forceinline__ void st8x(P* p, const F8& f) {
-  if constexpr (NT) st8nt(p, f);
+
+// A store of the product epilogues.  `nt` (the same for the whole launch)
+// picks the non-temporal form: it keeps large outputs from displacing the
+// operand lines a phase still reuses, while small ones are better left in the
+// caches for the phase that reads them next.
+template <typename P>
+__device__ __forceinline__ void st8s(P* p, const F8& f, bool nt) {
+  if (nt) st8nt(p, f);
   else st8(p, f);
 }
 

@@ -107,6 +107,13 @@ static size_t ctrl_words(int G) { return (size_t)(G + 4) * 32 + moe::kXcdWords; 
 // against 0.451 ms; 4x1024: 0.52 against 0.59 ms).
 constexpr long kTwoPerCuRows = 4096;
 
+// Routed rows of a launch (n_tokens * top_k) from which the product outputs are
+// written with non-temporal stores.  Measured on the same layer (C++ driver,
+// one box): plain stores win at 2x1024 (0.421 against 0.490 ms) and tie on the
+// Zipf workload's 8192-token microbatches; non-temporal ones win at 32x1024
+// (1.723 against 1.756 ms).
+constexpr long kNonTemporalRows = 32768;
+
 struct moe_step {
   moe_step_config cfg;
   int grid = 0;
@@ -463,6 +470,7 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.ctrl.limit = (run_flags & MOE_RUN_TEST_TIMEOUT) ? moe::kTestTimeoutTicks : moe::kBarrierTimeoutTicks;
   p.epoch = ++h->epoch;
   p.recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) ? 1 : 0;
+  p.nt_stores = (long)n_tokens * c.top_k >= kNonTemporalRows ? 1 : 0;
 
   hipError_t he = hipSetDevice(c.device);
   if (he != hipSuccess) {

@@ -119,6 +119,7 @@ struct KParams {
   uint16_t* shadow;  // [2*E*d*f] bf16 copy of W1 | W2 (bf16 mode)
   float* wpart2;     // partial dW2 tiles of split contractions [blocks][tiles per expert][128 x 128]
   float* wpart1;     // the same for dW1
+  int nt_stores;     // product outputs written with non-temporal stores (large launches)
   void* xs;          // [N, d] token rows in expert order (bf16 mode), written by route_order
   Ctrl ctrl;
 };
@@ -878,14 +879,14 @@ __device__ __forceinline__ void phase_ffn1(const KParams& p, char* lds, const Me
           F8 hv;
 #pragma unroll
           for (int q = 0; q < 8; ++q) hv.v[q] = h[q];
-          st8x<NS == 2>(act + o, hv);
+          st8s(act + o, hv, p.nt_stores);
           return;
         }
         F8 a, da;
 #pragma unroll
         for (int q = 0; q < 8; ++q) gelu_and_grad(h[q], a.v[q], da.v[q]);
-        st8x<NS == 2>(act + o, a);
-        st8x<NS == 2>(gp + o, da);
+        st8s(act + o, a, p.nt_stores);
+        st8s(gp + o, da, p.nt_stores);
       }
     };
     gemm::tile<T, NS, false, true>(lds, A, B, d, epi);
@@ -939,7 +940,7 @@ __device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& me
         F8 o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) o.v[q] = v[q];
-        st8x<NS == 2>(p.out + (long)(p0 + r) * d + n0 + c, o);
+        st8s(p.out + (long)(p0 + r) * d + n0 + c, o, p.nt_stores);
       }
     };
     // under the recomputation rule act holds H and the A fragments pass through GELU
@@ -1237,7 +1238,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
       F8 o;
 #pragma unroll
       for (int u = 0; u < 8; ++u) o.v[u] = v[u];
-      st8x<NS == 2>(pt + r * gemm::BN + c, o);
+      st8s(pt + r * gemm::BN + c, o, p.nt_stores);
     });
     return;
   }
@@ -1249,7 +1250,7 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
           F8 nv = cvt8(old);
 #pragma unroll
           for (int u = 0; u < 8; ++u) nv.v[u] = zero ? v[u] : nv.v[u] + v[u];
-          st8x<NS == 2>(g + (long)(m0 + r) * N + n0 + c, nv);
+          st8s(g + (long)(m0 + r) * N + n0 + c, nv, p.nt_stores);
 #pragma unroll
           for (int u = 0; u < 8; ++u) sq += nv.v[u] * nv.v[u];
         }
@@ -1336,7 +1337,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
               }
 #pragma unroll
               for (int u = 0; u < 8; ++u) g8.v[u] *= v[u];
-              st8x<NS == 2>(dh + (long)(p0 + r) * f + n0 + c, g8);
+              st8s(dh + (long)(p0 + r) * f + n0 + c, g8, p.nt_stores);
             }
           },
           [&](int r, int c) {
@@ -1472,7 +1473,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
               F8 o;
 #pragma unroll
               for (int u = 0; u < 8; ++u) o.v[u] = v[u];
-              st8x<NS == 2>(dxs + (long)slot * d + n0 + c, o);
+              st8s(dxs + (long)slot * d + n0 + c, o, p.nt_stores);
             }
           },
           [&](int r, int c) { return (r < mrows && n0 + c < d) ? p.perm[p0 + r] : 0; });

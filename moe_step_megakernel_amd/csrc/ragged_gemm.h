@@ -214,17 +214,17 @@ __device__ __forceinline__ void mma_stage(const char* As, const char* Bs, f32x16
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if constexpr (sizeof(T) == 2) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
-                                                             __builtin_bit_cast(bf16x8_t, b[j]),
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                             __builtin_bit_cast(bf16x8_t, a[i]),
                                                              acc[i][j], 0, 0, 0);
         } else {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i].x), __uint_as_float(b[j].x),
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b[j].x), __uint_as_float(a[i].x),
                                                           acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i].y), __uint_as_float(b[j].y),
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b[j].y), __uint_as_float(a[i].y),
                                                           acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i].z), __uint_as_float(b[j].z),
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b[j].z), __uint_as_float(a[i].z),
                                                           acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i].w), __uint_as_float(b[j].w),
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b[j].w), __uint_as_float(a[i].w),
                                                           acc[i][j], 0, 0, 0);
         }
       }
@@ -264,6 +264,12 @@ __device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2],
   }
   float* cs = reinterpret_cast<float*>(lds);
   {
+    // every product is issued with its operands exchanged (B fragment first),
+    // so accumulator block (i, j) holds its block transposed: lane l, register
+    // r holds tile row 64 wm + 32 i + l % 32, column 64 wn + 32 j + 8 (r / 4) +
+    // 4 (l / 32) + r % 4 -- four consecutive columns per register group, one
+    // 16-byte LDS write each (rows CROW * 4 = 528 bytes apart, so 16
+    // consecutive lanes cover all 64 banks)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w & 1, wn = w >> 1;
 #pragma unroll
@@ -271,10 +277,11 @@ __device__ __forceinline__ void epilogue(char* lds, const f32x16_t (&acc)[2][2],
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = wn * 64 + j * 32 + (lane & 31);
-          cs[row * CROW + col] = acc[i][j][r];
+        for (int g = 0; g < 4; ++g) {
+          const int row = wm * 64 + i * 32 + (lane & 31);
+          const int col = wn * 64 + j * 32 + g * 8 + (lane >> 5) * 4;
+          *reinterpret_cast<float4*>(cs + row * CROW + col) =
+              make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
         }
   }
   lds_sync();
@@ -348,17 +355,19 @@ __device__ __forceinline__ void tile_reg(char* lds, const Operand& A, const Oper
 // ---------------------------------------------------------------------------
 // bf16 tiles: direct-to-LDS loads (buffer_load_dwordx4 ... lds), up to four
 // LDS stages, so the loads of three k-tiles are in flight while the matrix
-// cores work on the fourth, at no register cost.  Each wave instruction fills 1 KB of LDS
-// contiguously (lane l -> bytes 16l..16l+15), so bank conflicts on the MFMA
-// reads are avoided by an XOR swizzle of 16-byte units instead of padding:
+// cores work on the fourth, at no register cost.  Each wave instruction fills
+// 1 KB of LDS contiguously (lane l -> bytes 16l..16l+15), so bank conflicts on
+// the MFMA reads are avoided by an XOR swizzle of 16-byte units instead of
+// padding:
 //  * K-rows operand, LDS [128 rows][128 B]: logical k-unit u of row r sits in
 //    physical unit u ^ ((r >> 1) & 7);
 //  * MN-rows operand, LDS [64 k-rows][256 B]: logical 16-byte column slot s of
 //    k-row r sits in physical slot s ^ (4 * (r & 3)).  Half a transpose read
 //    (32 lanes) covers 4 k-rows x 64 bytes; the XOR puts the 4 rows' 64-byte
 //    pieces in the 4 distinct quarters of the 64 banks.
-// Out-of-range elements are zeroed by the loads' range check.  The loop waits on the vector-memory counter itself and synchronises with a bare
-// s_barrier, so the loads of later k-tiles stay in flight across it.
+// Out-of-range elements are zeroed by the loads' range check.  The loop waits
+// on the vector-memory counter itself and synchronises with a bare s_barrier,
+// so the loads of later k-tiles stay in flight across it.
 // ---------------------------------------------------------------------------
 constexpr int DMA_OP = 16384;                  // bytes per operand per stage
 constexpr int DMA_STAGE = 2 * DMA_OP;
@@ -573,10 +582,10 @@ __device__ __forceinline__ u32x4_t join(const u32x2_t& lo, const u32x2_t& hi) {
 #define MOE_RD_MN(d, a) \
   "ds_read_b64_tr_b16 %[" d "l], %[" a "] offset:%[o" a "]\n\tds_read_b64_tr_b16 %[" d "h], %[" a "] offset:%[o" a "h]\n\t"
 #define MOE_MFMA4                                                   \
-  "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"      \
-  "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"      \
-  "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"      \
-  "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+  "v_mfma_f32_32x32x16_bf16 %[c00], %[b0], %[a0], %[c00]\n\t"      \
+  "v_mfma_f32_32x32x16_bf16 %[c01], %[b1], %[a0], %[c01]\n\t"      \
+  "v_mfma_f32_32x32x16_bf16 %[c10], %[b0], %[a1], %[c10]\n\t"      \
+  "v_mfma_f32_32x32x16_bf16 %[c11], %[b1], %[a1], %[c11]\n\t"
 #define MOE_ACC_OUT [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1])
 #define MOE_CUR_IN [a0] "v"(c.a0), [a1] "v"(c.a1), [b0] "v"(c.b0), [b1] "v"(c.b1)
 #define MOE_ADDR_IN                                                                                  \
