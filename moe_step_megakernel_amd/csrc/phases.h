@@ -657,18 +657,20 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   if (p.flags & 0x10000u)   // readiness counters of this launch, zero before GEMM 1 starts
     for (int i = lwg * kThreads + tid; i < p.nrb; i += G * kThreads) p.ready[i] = 0;
   {
+    // 32 rows per thread in flight at once: with up to 16 experts and 512
+    // workgroups that is every row in one round of (L2-missing) loads
     const int e = tid % EP, part = tid / EP;
     int pre = 0, tot = 0;
     if (e < E) {
-      for (int w0 = part; w0 < G; w0 += parts * 8) {
-        int h[8];
+      for (int w0 = part; w0 < G; w0 += parts * 32) {
+        int h[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 32; ++u) {
           const int w = w0 + u * parts;
           h[u] = (w < G) ? p.hist[(long)w * E + e] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 32; ++u) {
           tot += h[u];
           if (w0 + u * parts < lwg) pre += h[u];
         }
