@@ -309,6 +309,56 @@ __device__ __forceinline__ void trace_mark(const KParams& p, int phase, int slot
     p.trace[((size_t)blockIdx.x * kPhases + phase) * 3 + slot] = wall_clock64();
 }
 
+// Stages columns [c0, c0 + dc) of W_r's expert groups [EG0, EG0 + NG) into
+// LDS in the order the router's segments read them (see router_segment_sums).
+// VEC: E is a multiple of 4, so a group is one 16-byte load.
+template <bool VEC, int EGT, int EG0>
+__device__ __forceinline__ void stage_router_rows(const KParams& p, float4* wl, int c0, int dc, int NG, int S) {
+  const int tid = threadIdx.x, d = p.d, E = p.E;
+  const int lg = __builtin_ctz(8 * S);   // log2 of the piece width 8 S
+  // two rows per step while a pass stages at most 4 groups, else one (the
+  // loads of a step stay within the register budget)
+  constexpr int R = EGT <= 4 ? 2 : 1;
+  for (int cb = 0; cb < dc; cb += R * kThreads) {
+    float4 w[R][EGT];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float* row = p.params + (long)min(c0 + cb + r * kThreads + tid, d - 1) * E + EG0 * 4;
+#pragma unroll
+      for (int g = 0; g < EGT; ++g) {
+        if (VEC) {
+          // groups past NG read group NG - 1 again; they are never stored
+          w[r][g] = *reinterpret_cast<const float4*>(row + 4 * min(g, NG - 1));
+        } else {
+          // expert e = 4 (EG0 + g) + t; e < E for t = 0 in every staged group
+          const int e = (EG0 + min(g, NG - 1)) * 4;
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float a = row[min(e + t, E - 1) - EG0 * 4];
+            v[t] = e + t < E ? a : 0.f;
+          }
+          w[r][g] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int cl = cb + r * kThreads + tid;
+      if (cl < dc) {
+        const bool live = c0 + cl < d;   // columns past d are zeros
+        const int i = cl >> lg, s = (cl >> 3) & (S - 1), j = cl & 7;
+        float4* dst = wl + (i * 8 + j) * NG * S + s;
+#pragma unroll
+        for (int g = 0; g < EGT; ++g)
+          if (g < NG)
+            dst[g * S] = make_float4(live ? w[r][g].x : 0.f, live ? w[r][g].y : 0.f, live ? w[r][g].z : 0.f,
+                                     live ? w[r][g].w : 0.f);
+      }
+    }
+  }
+}
+
 // Partial router logits of TL tokens over one column segment (see the
 // router phase): acc[u][e] = sum over the segment's columns c of
 // x[tok + u][c] W_r[c][e], for the EGT groups of 4 experts from group EG0 on
@@ -348,26 +398,13 @@ __device__ __forceinline__ void router_segment_sums(const KParams& p, const T* x
     Raw8<T> xa[TL][PG], xb[TL][PG];
     load_group(0, xa);
     __syncthreads();
-    // all of a thread's loads are issued before its LDS stores (16 per batch)
-#pragma unroll 16
-    for (int q = tid; q < dc * NG; q += kThreads) {
-      const int cl = q / NG, gl = q % NG, eg = EG0 + gl;
-      const int i = cl / (8 * S), rem = cl % (8 * S), s = rem >> 3, j = rem & 7;
-      const int c = c0 + cl;
-      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-      if ((E & 3) == 0) {
-        if (c < d) w = *reinterpret_cast<const float4*>(p.params + (long)c * E + eg * 4);
-      } else {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int e = eg * 4 + u;
-          v[u] = (c < d && e < E) ? p.params[(long)c * E + e] : 0.f;
-        }
-        w = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      wl[((i * 8 + j) * NG + gl) * S + s] = w;
-    }
+    // W_r chunk -> LDS, one column's NG groups (a contiguous row segment of
+    // W_r) per thread and step, two steps' loads in flight before their
+    // stores.  Column cl goes to piece cl / 8S, segment (cl / 8) % S, row
+    // cl % 8 of the piece; 8S is a power of two, so these are shifts and
+    // masks.  Columns past d read a clamped row and store zeros.
+    if ((E & 3) == 0) stage_router_rows<true, EGT, EG0>(p, wl, c0, dc, NG, S);
+    else stage_router_rows<false, EGT, EG0>(p, wl, c0, dc, NG, S);
     __syncthreads();
     for (int i0 = 0; i0 < ni; i0 += PG) {
       load_group(i0 + PG, xb);
@@ -434,8 +471,18 @@ __device__ __forceinline__ void router_reduce(float (&acc)[TL][kMaxExperts], flo
     __syncthreads();
     for (int o = tid; o < nb * ne; o += kThreads) {
       const int tk = o / ne, e = o % ne;
+      const float* src = part + tk * S * RW + e;
       float s = 0.f;
-      for (int sg = 0; sg < S; ++sg) s += part[(tk * S + sg) * RW + e];
+      // the reads of 16 segments are in flight together; the sum keeps
+      // segment order
+      for (int sg0 = 0; sg0 < S; sg0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = src[min(sg0 + u, S - 1) * RW];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (sg0 + u < S) s += v[u];
+      }
       zacc[tk * EP + e0 + e] = s;
     }
   } else {
@@ -1727,67 +1774,84 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
 // ===========================================================================
 // The persistent kernel: one launch per update (or microbatch)
 // ===========================================================================
+// The launch's KParams, read from the kernel-argument segment.  The pointer
+// passes through an empty asm statement at each call, so the compiler cannot
+// prove two calls equal: each phase loads the fields it uses (scalar loads
+// from the constant cache) instead of keeping all of the structure in scalar
+// registers for the whole launch, which the scalar register file cannot hold.
+__device__ __forceinline__ const KParams& kernel_args() {
+  using ArgPtr = const __attribute__((address_space(4))) KParams*;
+  ArgPtr q = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return *(const KParams*)q;
+}
+
 template <typename T, int OCC>
-__global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
+__global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams args) {
+  (void)args;   // read through kernel_args(), phase by phase
   constexpr int NS = dma_stages(OCC);
   extern __shared__ __align__(16) char smem_raw[];
   Meta& meta = *reinterpret_cast<Meta*>(smem_raw);
   char* work = smem_raw + kMetaBytes;   // LDS after the routing metadata
   // the host has expanded the whole-update bits into the per-group ones
-  const bool zero_r = (p.flags & 0x10u) != 0u, zero_e = (p.flags & 0x20u) != 0u;
-  const bool apply_r = (p.flags & 0x40u) != 0u, apply_e = (p.flags & 0x80u) != 0u;
-  const bool want_dx = p.dx != nullptr;
+  const unsigned flags = kernel_args().flags;
+  const bool zero_r = (flags & 0x10u) != 0u, zero_e = (flags & 0x20u) != 0u;
+  const bool apply_r = (flags & 0x40u) != 0u, apply_e = (flags & 0x80u) != 0u;
 
   int hk = 0;   // barriers passed in this launch (the first one learns the XCD membership)
-#define MOE_SYNC(ph)                                                               \
-  do {                                                                             \
-    trace_mark(p, ph, 1);                                                          \
-    if (!grid_barrier(p.ctrl, p.epoch * 8u + (ph) + 1u, &meta.bar, hk++)) return;  \
-    trace_mark(p, ph, 2);                                                          \
+#define MOE_SYNC(ph)                                                                    \
+  do {                                                                                  \
+    const KParams& pb = kernel_args();                                                  \
+    trace_mark(pb, ph, 1);                                                              \
+    if (!grid_barrier(pb.ctrl, pb.epoch * 8u + (ph) + 1u, &meta.bar, hk++)) return;     \
+    trace_mark(pb, ph, 2);                                                              \
   } while (0)
 
   // A launch enqueued after one that gave up (before moe_step_status reset the
   // abort word) writes nothing.
-  if (threadIdx.x == 0) meta.bar.flag = __hip_atomic_load(p.ctrl.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    meta.bar.flag = __hip_atomic_load(kernel_args().ctrl.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (meta.bar.flag != 0u) return;
-  if ((p.flags & 0x40000u) && blockIdx.x == gridDim.x - 1) {
+  if ((flags & 0x40000u) && blockIdx.x == gridDim.x - 1) {
     // failure-path test: this workgroup waits for a word nothing sets, gives
     // up, and never arrives at the first barrier
-    if (threadIdx.x == 0) (void)wait_for(p.ctrl, p.ctrl.never, 1u);
+    if (threadIdx.x == 0) (void)wait_for(kernel_args().ctrl, kernel_args().ctrl.never, 1u);
     return;
   }
-  const unsigned skip = p.flags >> 8;
-  trace_mark(p, 0, 0);
-  if (!(skip & 1u)) phase_route<T, OCC>(p, work, meta);
+  const unsigned skip = flags >> 8;
+  trace_mark(kernel_args(), 0, 0);
+  if (!(skip & 1u)) phase_route<T, OCC>(kernel_args(), work, meta);
   MOE_SYNC(0);
-  trace_mark(p, 1, 0);
-  phase_order<T>(p, work, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
+  trace_mark(kernel_args(), 1, 0);
+  phase_order<T>(kernel_args(), work, meta, (skip & 2u) != 0u);   // the offsets are always rebuilt
   MOE_SYNC(1);
-  trace_mark(p, 2, 0);
-  const bool ready12 = (p.flags & 0x10000u) != 0u;
-  if (!(skip & 4u)) phase_ffn1<T, NS>(p, work, meta, ready12);
+  trace_mark(kernel_args(), 2, 0);
+  const bool ready12 = (flags & 0x10000u) != 0u;
+  if (!(skip & 4u)) phase_ffn1<T, NS>(kernel_args(), work, meta, ready12);
   if (ready12) {   // readiness counters instead of a grid barrier
-    trace_mark(p, 2, 1);
-    trace_mark(p, 2, 2);
+    trace_mark(kernel_args(), 2, 1);
+    trace_mark(kernel_args(), 2, 2);
   } else {
     MOE_SYNC(2);
   }
-  trace_mark(p, 3, 0);
-  if (!(skip & 8u) && !phase_ffn2<T, NS>(p, work, meta, ready12 && !(skip & 4u))) return;
+  trace_mark(kernel_args(), 3, 0);
+  if (!(skip & 8u) && !phase_ffn2<T, NS>(kernel_args(), work, meta, ready12 && !(skip & 4u))) return;
   MOE_SYNC(3);
-  trace_mark(p, 4, 0);
-  if (!(skip & 16u)) phase_combine<T, OCC>(p, meta);
+  trace_mark(kernel_args(), 4, 0);
+  if (!(skip & 16u)) phase_combine<T, OCC>(kernel_args(), meta);
   MOE_SYNC(4);
-  trace_mark(p, 5, 0);
-  if (!(skip & 32u)) phase_bwd2<T, NS>(p, work, meta, zero_e);
+  trace_mark(kernel_args(), 5, 0);
+  if (!(skip & 32u)) phase_bwd2<T, NS>(kernel_args(), work, meta, zero_e);
   MOE_SYNC(5);
-  trace_mark(p, 6, 0);
-  if (!(skip & 64u)) phase_bwd1<T, NS>(p, work, meta, zero_r, zero_e, want_dx, !(skip & 32u));
+  trace_mark(kernel_args(), 6, 0);
+  const bool want_dx = kernel_args().dx != nullptr;
+  if (!(skip & 64u)) phase_bwd1<T, NS>(kernel_args(), work, meta, zero_r, zero_e, want_dx, !(skip & 32u));
   MOE_SYNC(6);
   if (meta.nsplit > 0 && !(skip & 64u)) {
     // complete the dW1 tiles whose contraction was split, so the global norm
     // below sees whole gradients; a grid barrier separates the two
+    const KParams& p = kernel_args();
     const int d = p.d, f = p.f, E = p.E;
     const int tpe = ceil_div(d, gemm::BM) * ceil_div(f, gemm::BN);
     const int n10 = E * ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
@@ -1801,11 +1865,11 @@ __global__ void __launch_bounds__(kThreads, OCC) moe_step_kernel(KParams p) {
     }
     if (!grid_barrier(p.ctrl, p.epoch * 8u + 8u, &meta.bar, hk++)) return;
   }
-  trace_mark(p, 7, 0);
-  if (!(skip & 128u)) phase_final<T, OCC>(p, work, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
+  trace_mark(kernel_args(), 7, 0);
+  if (!(skip & 128u)) phase_final<T, OCC>(kernel_args(), work, meta, zero_r || zero_e, apply_r, apply_e, want_dx);
   __syncthreads();
-  trace_mark(p, 7, 1);
-  trace_mark(p, 7, 2);
+  trace_mark(kernel_args(), 7, 1);
+  trace_mark(kernel_args(), 7, 2);
 #undef MOE_SYNC
 }
 
