@@ -547,6 +547,90 @@ __device__ __forceinline__ void router_block(const KParams& p, const T* x, float
   }
 }
 
+// Router logits of tokens [b0, b0 + nb) on the matrix cores, for d a multiple
+// of 128 up to kRouterMfmaMaxD: zacc[t][e] = sum_c x[b0 + t][c] W_r[c][e] in
+// fp32 with v_mfma_f32_16x16x4_f32, 16 tokens x 16 experts per product (token
+// tiles of 16 rows, expert tiles of 16 columns).  The contraction over the d
+// columns is split 16 ways: wave w and lane group g = lane / 16 own the
+// L = d / 16 consecutive columns from (4 w + g) L, and each product takes one
+// column of every lane group.  A lane supplies the x value of token row
+// lane % 16 and the W_r value of expert column lane % 16, both read straight
+// from global memory (each wave reads only its own quarter of W_r): all of a
+// lane's W_r values of an expert tile are requested at once, and the x values
+// of the next token tile while this tile is multiplied, so a block costs about
+// one memory round trip per expert tile.  The four waves' partial tiles go
+// through LDS (part, [4][ntt * 16][EP]) and are added in wave order into zacc
+// ([ntt * 16][EP]).
+constexpr int kRouterMfmaMaxD = 1024;
+template <typename T>
+__device__ __forceinline__ void router_mfma_block(const KParams& p, const T* x, float* zacc, float* part, int b0,
+                                                  int nb, int EP) {
+  constexpr int LM = kRouterMfmaMaxD / 16;   // columns per lane group at most
+  constexpr int NQ = LM / 8;                 // 8-column pieces per lane group at most
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = p.d, E = p.E;
+  const int L = d >> 4, nq = L >> 3;         // columns and 8-column pieces per lane group
+  const int i = lane & 15, g = lane >> 4;
+  const int kb = (wave * 4 + g) * L;         // first column of this lane group
+  const int ntt = (nb + 15) >> 4, net = (E + 15) >> 4;
+  const int TPB = ntt * 16;                  // token rows of the partial tiles
+  // the x pieces of token row i of tile tt (rows past nb read the last token,
+  // pieces past L the last piece; neither is used)
+  auto load_x = [&](int tt, Raw8<T> (&xr)[NQ]) {
+    const T* row = x + (long)(b0 + min(tt * 16 + i, nb - 1)) * d + kb;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) xr[q] = ldr8(row + 8 * min(q, nq - 1));
+  };
+  Raw8<T> xa[NQ], xb[NQ];
+  for (int et = 0; et < net; ++et) {
+    const int e = et * 16 + i;                // expert column of this lane
+    const bool ein = e < E;
+    const float* wcol = p.params + min(e, E - 1) + (long)kb * E;
+    float w[LM];
+#pragma unroll
+    for (int m = 0; m < LM; ++m) w[m] = wcol[(long)min(m, L - 1) * E];
+    if (!ein) {
+#pragma unroll
+      for (int m = 0; m < LM; ++m) w[m] = 0.f;
+    }
+    if (et == 0) load_x(0, xa);
+    for (int tt = 0; tt < ntt; ++tt) {
+      // x of the next tile (or, for the last, of the first tile of the next
+      // expert tile) in flight while this one is multiplied
+      const bool last = tt + 1 == ntt;
+      if (!last || et + 1 < net) load_x(last ? 0 : tt + 1, xb);
+      f4v c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (q < nq) {
+          const F8 xf = cvt8(xa[q]);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xf.v[s], w[q * 8 + s], c, 0, 0, 0);
+        }
+      }
+      // partial tile of this wave: the lane holds rows 4 (lane / 16) + r of
+      // column lane % 16
+      if (e < EP) {
+        float* dst = part + ((long)wave * TPB + tt * 16 + 4 * g) * EP + e;
+        dst[0] = c.x;
+        dst[EP] = c.y;
+        dst[2 * EP] = c.z;
+        dst[3 * EP] = c.w;
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) xa[q] = xb[q];
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < nb * EP; o += kThreads) {
+    const int t = o / EP, ee = o - t * EP;
+    const float* src = part + (long)t * EP + ee;
+    zacc[o] = ((src[0] + src[(long)TPB * EP]) + src[2L * TPB * EP]) + src[3L * TPB * EP];
+  }
+  __syncthreads();
+}
+
 // ===========================================================================
 // P0: weight-copy refresh, W_r^T, router logits + token_topk + gates + histogram
 // ===========================================================================
@@ -579,45 +663,10 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   const int e_me = tid % EP, slot = tid / EP;
   const T* x = reinterpret_cast<const T*>(p.x);
 
-  // Router logits, TP tokens per pass, each split over S column segments
-  // (TP * S / TL <= 256 threads, S a power of two <= 64 so a token's segments are
-  // adjacent lanes of one wave).  Segment s of a token owns the 8-column
-  // pieces 8s, 8s + 8S, 8s + 16S, ... and keeps all E partial sums in
-  // registers; W_r is staged in LDS in the order the segments read it (for
-  // each piece index i, row j of the piece and 4-expert group eg, the S
-  // segments' float4s side by side), so the reads of one wave are either
-  // distinct consecutive 16-byte words or broadcasts.
-  // The logits of a block live in LDS (zacc, [TP][EP]) within a quarter of the
-  // scratch; a larger token range takes several blocks.
-  // With 16 or more tokens per pass and at most 16 experts, each lane works
-  // on TL tokens (4 with one workgroup per CU, 2 with half the register
-  // file), so every W_r value it reads from LDS serves TL tokens.
-  constexpr int kScratch = scratch_bytes(OCC);
-  int TP = 1;
-  while (TP < min(t_hi - t_lo, 4 * kThreads) && 2 * TP * EP * 4 <= kScratch / 4) TP <<= 1;
-  const int EG = (E + 3) / 4;
-  constexpr int kTL = OCC == 1 ? 4 : 2;
-  const int TL = (TP >= 16 && EG <= 4) ? kTL : 1;
-  TP = min(TP, TL * kThreads);
-  int S = min(64, kThreads * TL / TP);
-  while (S > 1 && 8 * S > d) S >>= 1;
-  float* zacc = reinterpret_cast<float*>(smem + 256);                          // [TP][EP]
-  float4* wl = reinterpret_cast<float4*>(smem + 256 + TP * EP * 4);           // staged W_r chunk
-  // (the reads of padded expert groups may run up to 16 * S float4 past the chunk)
-  const int wbudget = kScratch - 256 - TP * EP * 4 - 16 * 64 * 16;
-  // a chunk holds at least one 8-column piece per segment for every expert
-  // group a pass stages (all EG groups in one pass up to 16 experts, else 8
-  // groups per pass with a whole register file, 4 with half of it; 8 * 8 * 16
-  // bytes always fit, so this ends with chunks of at least 8 S columns)
-  const int NGmax = EG <= 4 ? EG : (OCC == 1 ? 8 : 4);
-  while (S > 1 && 8 * S * NGmax * 16 > wbudget) S >>= 1;
-  const int t_me = tid / S, s_me = tid % S;
-
-  for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
-    const int nb = min(TP, t_hi - b0);
-    if (TL > 1) router_block<T, OCC, kTL>(p, x, wl, zacc, b0, nb, t_me, s_me, S, EG, EP, wbudget);
-    else router_block<T, OCC, 1>(p, x, wl, zacc, b0, nb, t_me, s_me, S, EG, EP, wbudget);
-    // token_topk over each group of EP lanes (the group never crosses a wave)
+  float* zacc = reinterpret_cast<float*>(smem + 256);   // [TP][EP] logits of a block
+  // token_topk over each group of EP lanes (the group never crosses a wave)
+  // for the logits of tokens [b0, b0 + nb) in zacc ([nb][EP])
+  auto topk_block = [&](int b0, int nb) {
     for (int g0 = 0; g0 < nb; g0 += TPI) {
       const int tok = b0 + g0 + slot;
       const bool live = (g0 + slot) < nb;
@@ -678,6 +727,61 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
           }
         }
       }
+    }
+  };
+  constexpr int kScratch = scratch_bytes(OCC);
+
+  if ((d & 127) == 0 && d <= kRouterMfmaMaxD) {
+    // matrix-core path: blocks of up to 4 token tiles of 16, as many as the
+    // partial tiles, zacc and the histogram leave room for.  Its own loop, so
+    // the other path's loop invariants are not computed (and spilled) here.
+    int ntt = min(4, ceil_div(t_hi - t_lo, 16));
+    while (ntt > 1 && 256 + 5 * 16 * ntt * EP * 4 > kScratch) --ntt;
+    const int TP = 16 * ntt;
+    float* part = zacc + TP * EP;   // [4][TP][EP] partial tiles
+    for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
+      const int nb = min(TP, t_hi - b0);
+      router_mfma_block<T>(p, x, zacc, part, b0, nb, EP);
+      topk_block(b0, nb);
+    }
+  } else {
+    // Router logits, TP tokens per pass, each split over S column segments
+    // (TP * S / TL <= 256 threads, S a power of two <= 64 so a token's segments are
+    // adjacent lanes of one wave).  Segment s of a token owns the 8-column
+    // pieces 8s, 8s + 8S, 8s + 16S, ... and keeps all E partial sums in
+    // registers; W_r is staged in LDS in the order the segments read it (for
+    // each piece index i, row j of the piece and 4-expert group eg, the S
+    // segments' float4s side by side), so the reads of one wave are either
+    // distinct consecutive 16-byte words or broadcasts.
+    // The logits of a block live in LDS (zacc, [TP][EP]) within a quarter of the
+    // scratch; a larger token range takes several blocks.
+    // With 16 or more tokens per pass and at most 16 experts, each lane works
+    // on TL tokens (4 with one workgroup per CU, 2 with half the register
+    // file), so every W_r value it reads from LDS serves TL tokens.
+    int TP = 1;
+    while (TP < min(t_hi - t_lo, 4 * kThreads) && 2 * TP * EP * 4 <= kScratch / 4) TP <<= 1;
+    const int EG = (E + 3) / 4;
+    constexpr int kTL = OCC == 1 ? 4 : 2;
+    const int TL = (TP >= 16 && EG <= 4) ? kTL : 1;
+    TP = min(TP, TL * kThreads);
+    int S = min(64, kThreads * TL / TP);
+    while (S > 1 && 8 * S > d) S >>= 1;
+    float4* wl = reinterpret_cast<float4*>(smem + 256 + TP * EP * 4);           // staged W_r chunk
+    // (the reads of padded expert groups may run up to 16 * S float4 past the chunk)
+    const int wbudget = kScratch - 256 - TP * EP * 4 - 16 * 64 * 16;
+    // a chunk holds at least one 8-column piece per segment for every expert
+    // group a pass stages (all EG groups in one pass up to 16 experts, else 8
+    // groups per pass with a whole register file, 4 with half of it; 8 * 8 * 16
+    // bytes always fit, so this ends with chunks of at least 8 S columns)
+    const int NGmax = EG <= 4 ? EG : (OCC == 1 ? 8 : 4);
+    while (S > 1 && 8 * S * NGmax * 16 > wbudget) S >>= 1;
+    const int t_me = tid / S, s_me = tid % S;
+
+    for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
+      const int nb = min(TP, t_hi - b0);
+      if (TL > 1) router_block<T, OCC, kTL>(p, x, wl, zacc, b0, nb, t_me, s_me, S, EG, EP, wbudget);
+      else router_block<T, OCC, 1>(p, x, wl, zacc, b0, nb, t_me, s_me, S, EG, EP, wbudget);
+      topk_block(b0, nb);
     }
   }
   __syncthreads();

@@ -366,12 +366,31 @@ def test_zipf_16x8x1024_accumulated_full_size():
     _run_and_compare(cfg, inp, BF16_TOL, steps=1)
 
 
-@pytest.mark.parametrize("wg_per_cu,T", [(1, 16 * 256 + 352), (2, 16 * 512 + 704)])
-def test_routing_exact_ties_bf16_several_tokens_per_lane(wg_per_cu, T):
+@pytest.mark.parametrize("dtype,T,d,f,E,k,wg_per_cu", [("f32", 1000, 128, 64, 3, 2, 1),
+                                                       ("f32", 777, 256, 136, 20, 3, 1),
+                                                       ("bf16", 1000, 128, 64, 16, 2, 1),
+                                                       ("bf16", 999, 384, 128, 20, 4, 2),
+                                                       ("bf16", 513, 256, 128, 64, 8, 1),
+                                                       ("bf16", 40000, 128, 64, 12, 2, 2),
+                                                       ("bf16", 18000, 128, 64, 16, 2, 1)])
+def test_router_on_matrix_cores(dtype, T, d, f, E, k, wg_per_cu):
+    # d a multiple of 128: router logits by 16x16 fp32 matrix products, the
+    # contraction split over the 4 waves; expert counts that leave padded
+    # columns (3, 20, 12), four expert tiles (E = 64), and token ranges of
+    # more than 64 per workgroup (several blocks of token tiles)
+    cfg = synth.small_config(f"router_mfma_{dtype}", T, d, f, E, k, dtype)
+    _run_and_compare(cfg, synth.make_inputs(cfg, 12), BF16_TOL if dtype == "bf16" else F32_TOL, steps=1,
+                     wg_per_cu=wg_per_cu)
+
+
+@pytest.mark.parametrize("wg_per_cu,T,d", [(1, 16 * 256 + 352, 96), (2, 16 * 512 + 704, 96), (1, 3000, 256),
+                                           (2, 3000, 256)])
+def test_routing_exact_ties_bf16_several_tokens_per_lane(wg_per_cu, T, d):
     # bf16 activations on the router path that gives each lane several tokens
-    # (at least 16 tokens per workgroup pass): duplicated router columns give
-    # bitwise-equal logits, so the lower expert index must win every tie
-    cfg = synth.small_config(f"ties_bf16_occ{wg_per_cu}", T, 96, 64, 12, 2, "bf16")
+    # (at least 16 tokens per workgroup pass; d = 256 takes the matrix-core
+    # path): duplicated router columns give bitwise-equal logits, so the lower
+    # expert index must win every tie
+    cfg = synth.small_config(f"ties_bf16_occ{wg_per_cu}_d{d}", T, d, 64, 12, 2, "bf16")
     inp = synth.make_inputs(cfg, 16)
     pairs = ((1, 3), (0, 5), (7, 11))
     for lo, hi in pairs:
