@@ -663,80 +663,81 @@ __device__ __forceinline__ void phase_route(const KParams& p, char* smem, Meta& 
   const int e_me = tid % EP, slot = tid / EP;
   const T* x = reinterpret_cast<const T*>(p.x);
 
+  constexpr int kScratch = scratch_bytes(OCC);
+  constexpr int kSelBytes = kThreads * kMaxTopK * 4;   // the top-k selections of one pass, at the end of the scratch
   float* zacc = reinterpret_cast<float*>(smem + 256);   // [TP][EP] logits of a block
-  // token_topk over each group of EP lanes (the group never crosses a wave)
-  // for the logits of tokens [b0, b0 + nb) in zacc ([nb][EP])
+  // token_topk over each group of EP lanes for the logits of tokens
+  // [b0, b0 + nb) in zacc ([nb][EP]), TPI tokens per pass.  Each lane of a
+  // token writes its biased logit back (non-finite ones become -inf and set
+  // an error bit), then counts the experts that come before it (a larger
+  // logit, or an equal one and a lower index): that count is its rank, and
+  // ranks below k are the selection, in order.  The selected logits go to
+  // sel ([TPI][kMaxTopK]) so every selected lane forms the softmax
+  // denominator over them in rank order.
+  float* sel = reinterpret_cast<float*>(smem + kScratch - kSelBytes);
   auto topk_block = [&](int b0, int nb) {
     for (int g0 = 0; g0 < nb; g0 += TPI) {
       const int tok = b0 + g0 + slot;
-      const bool live = (g0 + slot) < nb;
+      const bool active = (g0 + slot) < nb && e_me < E;
+      float* zr = zacc + (g0 + slot) * EP;
       float z = -INFINITY;
-      bool active = false;
-      if (live && e_me < E) {
-        z = zacc[(g0 + slot) * EP + e_me];
+      if (active) {
+        z = zr[e_me];
         if (p.bias) z += p.bias[e_me];
         if (p.dbg_logits) p.dbg_logits[(long)tok * E + e_me] = z;
         if (!(z == z) || z == INFINITY || z == -INFINITY) {   // NaN or infinite: device error
           __hip_atomic_fetch_or(p.ctrl.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           z = -INFINITY;
         }
-        active = true;
+        zr[e_me] = z;
       }
-      float zsel[kMaxTopK];
-      int esel[kMaxTopK];
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        zsel[j] = 0.f;
-        esel[j] = 0;
-        if (j < k) {
-          // best = (active, larger z, lower index)
-          float bv = z;
-          int be = active ? e_me : 0x7fffffff;
-          for (int m = EP >> 1; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, 64);
-            const int oe = __shfl_xor(be, m, 64);
-            const bool o_act = oe != 0x7fffffff, me_act = be != 0x7fffffff;
-            const bool take = o_act && (!me_act || ov > bv || (ov == bv && oe < be));
-            if (take) { bv = ov; be = oe; }
+      __syncthreads();
+      int rank = kMaxExperts;
+      if (active) {
+        rank = 0;
+        if ((EP & 3) == 0) {
+          for (int e4 = 0; e4 < E; e4 += 4) {
+            const float4 o = *reinterpret_cast<const float4*>(zr + e4);
+            rank += (o.x > z) || (o.x == z && e4 < e_me);
+            if (e4 + 1 < E) rank += (o.y > z) || (o.y == z && e4 + 1 < e_me);
+            if (e4 + 2 < E) rank += (o.z > z) || (o.z == z && e4 + 2 < e_me);
+            if (e4 + 3 < E) rank += (o.w > z) || (o.w == z && e4 + 3 < e_me);
           }
-          zsel[j] = bv;
-          esel[j] = be;
-          if (be == e_me) active = false;
+        } else {
+          for (int e2 = 0; e2 < E; ++e2) {
+            const float o = zr[e2];
+            rank += (o > z) || (o == z && e2 < e_me);
+          }
         }
+        if (rank < k) sel[slot * kMaxTopK + rank] = z;
       }
-      if (live) {
+      __syncthreads();
+      if (rank < k) {
+        const float* zs = sel + slot * kMaxTopK;
+        const float z0 = zs[0];
         float den = 0.f;
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j)
-          if (j < k) den += expf(zsel[j] - zsel[0]);
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-          if (j < k && e_me == j) {
-            const float gj = expf(zsel[j] - zsel[0]) / den;
-            const int q = tok * k + j;
-            int ej = esel[j];
-            if ((unsigned)ej >= (unsigned)E) {   // cannot happen; keeps every later index in range
-              __hip_atomic_fetch_or(p.ctrl.status, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              ej = 0;
-            }
-            p.idx[q] = ej;
-            p.gate[q] = gj;
-            if (p.dbg_idx) p.dbg_idx[q] = ej;
-            if (p.dbg_gate) p.dbg_gate[q] = gj;
-            atomicAdd(&hist[ej], 1);
-          }
-        }
+          if (j < k) den += expf(zs[j] - z0);
+        const float gj = expf(z - z0) / den;
+        const int q = tok * k + rank;
+        p.idx[q] = e_me;
+        p.gate[q] = gj;
+        if (p.dbg_idx) p.dbg_idx[q] = e_me;
+        if (p.dbg_gate) p.dbg_gate[q] = gj;
+        atomicAdd(&hist[e_me], 1);
       }
+      __syncthreads();
     }
   };
-  constexpr int kScratch = scratch_bytes(OCC);
 
   if ((d & 127) == 0 && d <= kRouterMfmaMaxD) {
     // matrix-core path: blocks of up to 4 token tiles of 16, as many as the
-    // partial tiles, zacc and the histogram leave room for.  Its own loop, so
-    // the other path's loop invariants are not computed (and spilled) here.
+    // partial tiles, zacc, the histogram and the selections leave room for.
+    // Its own loop, so the other path's loop invariants are not computed
+    // (and spilled) here.
     int ntt = min(4, ceil_div(t_hi - t_lo, 16));
-    while (ntt > 1 && 256 + 5 * 16 * ntt * EP * 4 > kScratch) --ntt;
+    while (ntt > 1 && 256 + 5 * 16 * ntt * EP * 4 + kSelBytes > kScratch) --ntt;
     const int TP = 16 * ntt;
     float* part = zacc + TP * EP;   // [4][TP][EP] partial tiles
     for (int b0 = t_lo; b0 < t_hi; b0 += TP) {
