@@ -1111,6 +1111,9 @@ __device__ __forceinline__ bool phase_ffn2(const KParams& p, char* lds, Meta& me
 // 256-column chunk.  CP chunks of the token are loaded at once (CP * k <= 8
 // row pieces of `out`), and the gates and slots of the half-wave's next token
 // are loaded one token ahead, so every lane keeps several loads in flight.
+// Token t goes to workgroup t % G (half-wave (t / G) % 8 of it), so every
+// workgroup gets the same number of tokens to within one even when there are
+// fewer tokens than half-waves.
 template <typename T, int CP>
 __device__ __forceinline__ float combine_tokens(const KParams& p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1134,11 +1137,11 @@ __device__ __forceinline__ float combine_tokens(const KParams& p) {
       }
     }
   };
-  int base = (lwg * kWaves + wave) * 2;
-  load_idx(base + half, g, pos);
+  int base = wave * 2 * G + lwg;   // token of half-wave 0; half-wave 1 takes base + G
+  load_idx(base + half * G, g, pos);
   // the loop bound is uniform over the wave (the half-wave sums need both halves)
   for (; base < p.T; base += stride) {
-    const int tok = base + half;
+    const int tok = base + half * G;
     const bool live = tok < p.T;
     load_idx(tok + stride, gn, pn);
     float dg[kMaxTopK];
@@ -1270,15 +1273,15 @@ __device__ __forceinline__ float combine_tokens_1chunk(const KParams& p) {
       if (live && j < k && c < d) o[s] = ldr8(p.out + (long)pp[j] * d + c);
     }
   };
-  int base = (lwg * kWaves + wave) * 2;
+  int base = wave * 2 * G + lwg;   // token of half-wave 0; half-wave 1 takes base + G
   Raw8<T> tr[CP], trn[CP];
   Raw8<float> o[NS], on[NS];
-  load_idx(base + half, g, pos);
-  load_idx(base + half + stride, gn, pn);
-  load_rows(base + half, pos, tr, o);
+  load_idx(base + half * G, g, pos);
+  load_idx(base + half * G + stride, gn, pn);
+  load_rows(base + half * G, pos, tr, o);
   // the loop bound is uniform over the wave (the half-wave sums need both halves)
   for (; base < p.T; base += stride) {
-    const int tok = base + half;
+    const int tok = base + half * G;
     const bool live = tok < p.T;
     load_idx(tok + 2 * stride, gnn, pnn);
     load_rows(tok + stride, pn, trn, on);
@@ -1694,10 +1697,10 @@ __device__ __forceinline__ void dx_tokens(const KParams& p) {
       }
     }
   };
-  int base = (lwg * kWaves + wave) * 2;
-  load_idx(base + half, dz, ev);
+  int base = wave * 2 * G + lwg;   // token of half-wave 0; half-wave 1 takes base + G
+  load_idx(base + half * G, dz, ev);
   for (; base < p.T; base += stride) {
-    const int tok = base + half;
+    const int tok = base + half * G;
     const bool live = tok < p.T;
     load_idx(tok + stride, dzn, evn);
     for (int c0 = 0; c0 < d; c0 += 256 * CP) {
