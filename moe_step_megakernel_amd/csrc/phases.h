@@ -1671,12 +1671,13 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
 // P7: dx row sums; global norm; clip + AdamW (+ bf16 weight copy)
 // ===========================================================================
 // dx of each token = router part sum_j dz_j W_r[:, e_j] + the token's k slot
-// rows of dXs, summed in slot order.  One token per half-wave as in the
+// rows of dXs, summed in slot order.  wrt is W_r^T, in LDS when it fits (each
+// token reads k rows of it).  One token per half-wave as in the
 // combine phase: lane h owns columns 8h.. of each 256-column chunk, CP chunks
 // are loaded at once, and the next token's dz / experts are loaded one token
 // ahead.
 template <typename T, int CP>
-__device__ __forceinline__ void dx_tokens(const KParams& p) {
+__device__ __forceinline__ void dx_tokens(const KParams& p, const float* wrt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, hl = lane & 31;
   const int G = gridDim.x, lwg = logical_wg();
@@ -1713,7 +1714,7 @@ __device__ __forceinline__ void dx_tokens(const KParams& p) {
         w[s] = Raw8<float>{};
         v[s] = Raw8<T>{};
         if (live && j < k && c < d) {
-          w[s] = ldr8(p.wrt + (long)ev[j] * d + c);
+          w[s] = ldr8(wrt + (long)ev[j] * d + c);
           v[s] = ldr8(dxs + ((long)tok * k + j) * d + c);
         }
       }
@@ -1760,7 +1761,25 @@ __device__ __forceinline__ void phase_final(const KParams& p, char* smem, Meta& 
   const int G = gridDim.x, lwg = logical_wg();
   const int d = p.d, f = p.f, E = p.E, k = p.k;
 
-  if (want_dx && !(p.flags & 0x200000u)) p.k <= 2 ? dx_tokens<T, 4>(p) : dx_tokens<T, 1>(p);
+  if (want_dx && !(p.flags & 0x200000u)) {
+    // the router part reads a row of W_r^T per slot: from LDS when W_r^T fits
+    // the scratch and the workgroup has at least 32 tokens (staging costs a
+    // workgroup about as much as 16 tokens' reads from L2: measured slower at
+    // 4 and 16 tokens per workgroup, faster at 64), else from L2
+    constexpr int kScratch = scratch_bytes(OCC);
+    const bool staged = (long)E * d * 4 <= kScratch && ((E * d) & 3) == 0 && p.T >= 32 * G;
+    if (staged) {
+      float4* dst = reinterpret_cast<float4*>(smem);
+      const float4* src = reinterpret_cast<const float4*>(p.wrt);
+      for (int i = tid; i < E * d / 4; i += kThreads) dst[i] = src[i];
+      __syncthreads();
+    }
+    // (separate calls, so the staged reads compile to LDS reads)
+    if (staged) p.k <= 2 ? dx_tokens<T, 4>(p, reinterpret_cast<const float*>(smem))
+                         : dx_tokens<T, 1>(p, reinterpret_cast<const float*>(smem));
+    else p.k <= 2 ? dx_tokens<T, 4>(p, p.wrt) : dx_tokens<T, 1>(p, p.wrt);
+    __syncthreads();   // the scratch is reused below
+  }
 
   // loss of this launch, summed over workgroups in index order
   if (lwg == 0 && p.stats) {
