@@ -10,17 +10,23 @@
 // last with MOE_RUN_APPLY.  Prints one line per skip mask with ms/update.
 //
 //   moe_step_bench [--config NAME | --inputs FILE] [--steps K] [--warmup W] [--skip MASK[,MASK...]]
-//                  [--wg-per-cu N] [--ready] [--coop] [--recompute] [--per-wg-barrier] [--copy-mib N]
+//                  [--wg-per-cu N] [--ready] [--coop] [--recompute] [--per-wg-barrier] [--fresh] [--copy-mib N]
 //     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024 (--tokens N changes its token count)
 //     --skip MASK: after the warm-up, time K updates whose launches skip the
 //                  phases in MASK (bit i = phase i, 0..7; bit 8 = the dispatch
 //                  gather inside phase 1; bit 9 = the k-way row sum of dx inside
 //                  phase 7), for per-phase timing and counter collection; a
 //                  comma-separated list times K updates per mask, in order
+//     --fresh: every update (warm-up and timed) starts from the initial
+//              parameters and zero moments at step 1, restored on the stream
+//              before its first launch and outside its timing (events around
+//              each update's launches), so every update routes like the first;
+//              without it the parameters keep training from update to update
 //     --copy-mib N: instead, time a plain device copy of N MiB (read N, write N),
 //                  the reference for scaling memory counters
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -112,7 +118,7 @@ int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024", inputs;
   int tokens = 0;   // --tokens: tokens per launch for a built-in shape (0 = the shape's own)
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
-  bool ready = false, coop = false, recompute = false, per_wg = false;
+  bool ready = false, coop = false, recompute = false, per_wg = false, fresh = false;
   std::vector<unsigned> skips{0u};
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -145,6 +151,7 @@ int main(int argc, char** argv) {
     else if (a == "--coop") coop = true;
     else if (a == "--recompute") recompute = true;
     else if (a == "--per-wg-barrier") per_wg = true;
+    else if (a == "--fresh") fresh = true;
     else {
       std::fprintf(stderr, "unknown argument %s\n", a.c_str());
       return 1;
@@ -281,8 +288,22 @@ int main(int argc, char** argv) {
                         (per_wg ? MOE_RUN_BARRIER_PER_WORKGROUP : 0u);
   int64_t step = 1;
   bool first = true;
-  // one update: the microbatches in order (x and t of microbatch mb at offset mb * T)
-  auto update = [&](uint32_t extra) -> int {
+  // --fresh: the initial parameters, restored before every update
+  float* params0 = nullptr;
+  if (fresh) {
+    CHECK_HIP(hipMalloc(&params0, P * 4));
+    CHECK_HIP(hipMemcpy(params0, params, P * 4, hipMemcpyDeviceToDevice));
+  }
+  // one update: the microbatches in order (x and t of microbatch mb at offset mb * T);
+  // with --fresh, e0/e1 (when given) bracket its launches and not the restore
+  auto update = [&](uint32_t extra, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) -> int {
+    if (fresh) {
+      CHECK_HIP(hipMemcpyAsync(params, params0, P * 4, hipMemcpyDeviceToDevice, stream));
+      CHECK_HIP(hipMemsetAsync(m, 0, P * 4, stream));
+      CHECK_HIP(hipMemsetAsync(v, 0, P * 4, stream));
+      step = 1;
+    }
+    if (ev0) CHECK_HIP(hipEventRecord(ev0, stream));
     for (int mb = 0; mb < M; ++mb) {
       io.x = dx_in + (size_t)mb * nt * es;
       io.target = dt + (size_t)mb * nt * es;
@@ -294,6 +315,7 @@ int main(int argc, char** argv) {
         return 2;
       }
     }
+    if (ev1) CHECK_HIP(hipEventRecord(ev1, stream));
     ++step;
     return 0;
   };
@@ -306,25 +328,46 @@ int main(int argc, char** argv) {
   hipEvent_t e0, e1;
   CHECK_HIP(hipEventCreate(&e0));
   CHECK_HIP(hipEventCreate(&e1));
+  std::vector<hipEvent_t> fe(fresh ? 2 * (size_t)std::max(steps, 1) : 0);
+  for (hipEvent_t& e : fe) CHECK_HIP(hipEventCreate(&e));
+  if (steps < 1) {
+    std::fprintf(stderr, "--steps must be at least 1\n");
+    return 1;
+  }
   for (const unsigned skip : skips) {
     const uint32_t sk = ((skip & 0xffu) << 8) | ((skip & 0x100u) ? MOE_RUN_SKIP_GATHER : 0u) |
                         ((skip & 0x200u) ? MOE_RUN_SKIP_ROWSUM : 0u);
-    CHECK_HIP(hipEventRecord(e0, stream));
-    for (int i = 0; i < steps; ++i)
-      if (update(sk)) return 2;
-    CHECK_HIP(hipEventRecord(e1, stream));
-    CHECK_HIP(hipEventSynchronize(e1));
+    float ms = 0.f;
+    if (fresh) {
+      // events around each update's launches; the restores stay outside them
+      for (int i = 0; i < steps; ++i) {
+        if (update(sk, fe[2 * i], fe[2 * i + 1])) return 2;
+      }
+      CHECK_HIP(hipEventSynchronize(fe[2 * steps - 1]));
+      for (int i = 0; i < steps; ++i) {
+        float u = 0.f;
+        CHECK_HIP(hipEventElapsedTime(&u, fe[2 * i], fe[2 * i + 1]));
+        ms += u;
+      }
+    } else {
+      CHECK_HIP(hipEventRecord(e0, stream));
+      for (int i = 0; i < steps; ++i)
+        if (update(sk)) return 2;
+      CHECK_HIP(hipEventRecord(e1, stream));
+      CHECK_HIP(hipEventSynchronize(e1));
+      CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+    }
     if (moe_step_status(h) != MOE_OK) {
       std::fprintf(stderr, "moe_step_status: %s\n", moe_step_last_error(h));
       return 2;
     }
-    float ms = 0.f;
-    CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
-    std::printf("%s skip=0x%03x grid=%d: %d updates of %d launch(es), %.4f ms/update, %.0f tokens/s\n",
-                inputs.empty() ? sh->name : inputs.c_str(), skip, moe_step_grid_size(h), steps, M, ms / steps,
-                (double)sh->T * M * steps / (ms * 1e-3));
+    std::printf("%s skip=0x%03x grid=%d: %d %supdates of %d launch(es), %.4f ms/update, %.0f tokens/s\n",
+                inputs.empty() ? sh->name : inputs.c_str(), skip, moe_step_grid_size(h), steps, fresh ? "fresh " : "",
+                M, ms / steps, (double)sh->T * M * steps / (ms * 1e-3));
     std::fflush(stdout);
   }
+  for (hipEvent_t e : fe) CHECK_HIP(hipEventDestroy(e));
+  if (params0) CHECK_HIP(hipFree(params0));
   moe_step_destroy(h);
   for (void* p : {(void*)dx_in, (void*)dt, (void*)params, (void*)grads, (void*)m, (void*)v, (void*)dxg, (void*)stats})
     CHECK_HIP(hipFree(p));

@@ -1421,6 +1421,59 @@ __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Me
   if (S == 1 && threadIdx.x == 0) p.norm_part[nidx] = s;
 }
 
+// One element of type T at byte offset vo + so from a buffer descriptor's
+// base, as fp32 (vo per lane, so uniform).
+template <typename T>
+__device__ __forceinline__ float ld_row_elem(gemm::rsrc_t r, int vo, int so) {
+  if constexpr (sizeof(T) == 2) return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0));
+  else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+}
+
+// Elements of type T of 16 consecutive rows at byte offsets so + vo + u * rb
+// (u = 0..15) from a buffer descriptor's base, as fp32.  The loads are one
+// assembly block that ends in its own wait, so all 16 are in flight together
+// (written as plain code under register pressure they were issued one at a
+// time, each waited for before the next).
+template <typename T>
+__device__ __forceinline__ void ld_rows16(gemm::rsrc_t r, int vo, int so, int rb, float (&out)[16]) {
+  uint32_t v[16];
+  int off = vo;
+#define MOE_LD16(OP)                                                                                           \
+  asm volatile(                                                                                                \
+               OP " %0, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %1, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %2, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %3, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %4, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %5, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %6, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %7, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %8, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %9, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                    \
+               OP " %10, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                   \
+               OP " %11, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                   \
+               OP " %12, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                   \
+               OP " %13, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                   \
+               OP " %14, %16, %17, %18 offen\n\tv_add_u32 %16, %19, %16\n\t"                                   \
+               OP " %15, %16, %17, %18 offen\n\t"                                                              \
+               "s_waitcnt vmcnt(0)"                                                                            \
+               : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),    \
+                 "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), \
+                 "=&v"(v[14]), "=&v"(v[15]), "+v"(off)                                                         \
+               : "s"(r), "s"(so), "s"(rb)                                                                      \
+               : "memory")
+  if constexpr (sizeof(T) == 2) {
+    MOE_LD16("buffer_load_ushort");
+#pragma unroll
+    for (int u = 0; u < 16; ++u) out[u] = bf16_to_f32(v[u]);
+  } else {
+    MOE_LD16("buffer_load_dword");
+#pragma unroll
+    for (int u = 0; u < 16; ++u) out[u] = __uint_as_float(v[u]);
+  }
+#undef MOE_LD16
+}
+
 template <typename T, int NS>
 __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_experts) {
   const int tid = threadIdx.x;
@@ -1503,49 +1556,67 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
             return graw;
           });
     } else {
-      // router-gradient partial: tokens [rc*RT, +RT) x columns [cc*256, +256)
+      // router-gradient partial: tokens [rc*RT, +RT) x columns [cc*256, +256).
+      // The chunk's dL/dz is laid out dense in LDS ([RT][EP], zero for the
+      // experts a token did not select); each thread sums x[t][c] dz[t][e]
+      // over the tokens in order, 16 experts at a time in registers.  The
+      // selected terms are added in the same order as a sparse sum and the
+      // others add zero, so no LDS read-modify-write chain is needed.
       const int ir = item - n10 - n9;
       const int rc = ir / CCH, cc = ir % CCH;
-      float* acc = reinterpret_cast<float*>(lds);                      // [E][256]
-      int* se = reinterpret_cast<int*>(acc + E * kThreads);            // [64*k] experts
-      float* sz = reinterpret_cast<float*>(se + 64 * kMaxTopK);        // [64*k] dL/dlogit
-      const int t0 = rc * RT, t1 = min(p.T, t0 + RT);
+      const int t0 = rc * RT, t1 = min(p.T, t0 + RT), nt = t1 - t0;
+      const int EP = (E + 15) & ~15;
+      float* dzd = reinterpret_cast<float*>(lds);   // [RT][EP]
       const int c = cc * kThreads + tid;
       __syncthreads();
-      for (int i = tid; i < E * kThreads; i += kThreads) acc[i] = 0.f;
-      for (int s0 = t0; s0 < t1; s0 += 64) {
-        const int s1 = min(t1, s0 + 64);
-        __syncthreads();
-        for (int i = tid; i < (s1 - s0) * k; i += kThreads) {
-          se[i] = p.idx[s0 * k + i];
-          sz[i] = p.dzsel[s0 * k + i];
-        }
-        __syncthreads();
-        if (c < d) {
-          constexpr int U = 32;
-          int tok = s0;
-          for (; tok + U <= s1; tok += U) {
-            float xv[U];
+      for (int i = tid; i < nt * EP; i += kThreads) dzd[i] = 0.f;
+      __syncthreads();
+      for (int i = tid; i < nt * k; i += kThreads) dzd[(i / k) * EP + p.idx[t0 * k + i]] = p.dzsel[t0 * k + i];
+      __syncthreads();
+      if (c < d) {
+        // x[t][c] through a buffer descriptor based at the chunk's first row
+        const gemm::rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(x + (long)t0 * d), (short)0, nt * d * (int)sizeof(T), gemm::kRsrcWord3);
+        const int vo = c * (int)sizeof(T), rb = d * (int)sizeof(T);
+        // x values of 32 tokens requested as two blocks of 16 loads
+        const int nfull = nt >> 5;
+        for (int e0 = 0; e0 < E; e0 += 16) {
+          float a[16];
 #pragma unroll
-            for (int u = 0; u < U; ++u) xv[u] = to_f32(x[(long)(tok + u) * d + c]);
+          for (int j = 0; j < 16; ++j) a[j] = 0.f;
+          for (int b = 0; b < nfull; ++b) {
+            float xv[32];
+            ld_rows16<T>(xr, vo, 32 * b * rb, rb, *reinterpret_cast<float(*)[16]>(&xv[0]));
+            ld_rows16<T>(xr, vo, (32 * b + 16) * rb, rb, *reinterpret_cast<float(*)[16]>(&xv[16]));
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-              for (int j = 0; j < k; ++j) {
-                const int q = (tok + u - s0) * k + j;
-                acc[se[q] * kThreads + tid] += xv[u] * sz[q];
+            for (int u = 0; u < 32; ++u) {
+              const float4* zr = reinterpret_cast<const float4*>(dzd + (32 * b + u) * EP + e0);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float4 z = zr[q];
+                a[4 * q + 0] += xv[u] * z.x;
+                a[4 * q + 1] += xv[u] * z.y;
+                a[4 * q + 2] += xv[u] * z.z;
+                a[4 * q + 3] += xv[u] * z.w;
               }
-          }
-          for (; tok < s1; ++tok) {
-            const float xv = to_f32(x[(long)tok * d + c]);
-            for (int j = 0; j < k; ++j) {
-              const int q = (tok - s0) * k + j;
-              acc[se[q] * kThreads + tid] += xv * sz[q];
             }
           }
+          for (int t = 32 * nfull; t < nt; ++t) {
+            const float x1 = ld_row_elem<T>(xr, vo, t * rb);
+            const float4* zr = reinterpret_cast<const float4*>(dzd + t * EP + e0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 z = zr[q];
+              a[4 * q + 0] += x1 * z.x;
+              a[4 * q + 1] += x1 * z.y;
+              a[4 * q + 2] += x1 * z.z;
+              a[4 * q + 3] += x1 * z.w;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (e0 + j < E) p.rpart[((long)rc * E + e0 + j) * d + c] = a[j];
         }
-      }
-      if (c < d) {
-        for (int e = 0; e < E; ++e) p.rpart[((long)rc * E + e) * d + c] = acc[e * kThreads + tid];
       }
     }
   }

@@ -3,7 +3,12 @@ rocprofv3 runs of the C++ driver of the C ABI (``_lib/moe_step_bench``) on the
 exact seeded inputs of the tests (``synth.dump``).
 
     python -m moe_step_megakernel_amd.profile --config NAME [--steps K] [--warmup W]
-           [--work DIR] [--out profiles]
+           [--fresh] [--work DIR] [--out profiles]
+
+With --fresh every update starts from the initial parameters and zero moments
+(``moe_step_bench --fresh``), so each one routes like the first; without it
+the parameters keep training over the run, which moves the routing of a
+skewed workload towards balance as the masks go by.
 
 Runs, each as its own process (the profiler starts the driver itself):
 
@@ -137,6 +142,8 @@ def main(argv=None):
     ap.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--inputs-dir", default="/tmp")
+    ap.add_argument("--fresh", action="store_true",
+                    help="every update from the initial parameters and zero moments (the routing of the first)")
     args = ap.parse_args(argv)
     sys.path.insert(0, ROOT)
     import synth
@@ -150,7 +157,7 @@ def main(argv=None):
     synth_dump.dump(cfg, 0, inputs)
     log(f"inputs of {cfg.name} written to {inputs}")
     masks = ",".join(f"0x{m:03x}" for _, m, _ in MASKS)
-    drv = [BENCH, "--inputs", inputs, "--warmup", str(args.warmup)]
+    drv = [BENCH, "--inputs", inputs, "--warmup", str(args.warmup)] + (["--fresh"] if args.fresh else [])
     M = cfg.microbatches
 
     # 1. uncounted timing
@@ -234,7 +241,7 @@ def main(argv=None):
              f"E={cfg.n_experts}, top-{cfg.top_k}, {cfg.dtype}; the seeded inputs of the tests "
              f"(`python -m synth.dump --config {cfg.name}`). Grid {grid} workgroups. Kernel sources sha256 "
              f"`{kernel_source_sha256()[:16]}…`. Made by `python -m moe_step_megakernel_amd.profile --config "
-             f"{cfg.name}` (from /tmp with TMPDIR=/tmp), which runs:", "",
+             f"{cfg.name}{' --fresh' if args.fresh else ''}` (from /tmp with TMPDIR=/tmp), which runs:", "",
              "```", "moe_step_bench " + shown(drv[1:]) + f" --steps {args.timing_steps} --skip {masks}",
              shown(kt_cmd),
              "rocprofv3 --pmc " + " ".join(PASS_A) + " -f csv -d <work>/pmcA -o pmc -- moe_step_bench ... --steps "
@@ -244,6 +251,8 @@ def main(argv=None):
              "A launch with mask m skips the phases whose bits are set (bit i = phase i; 0x100 = the dispatch "
              "gather inside route_order; 0x200 = the k-way row sum inside the last phase) and reuses the arena of "
              "the previous full launch.  Times are per update (all microbatch launches) from the uncounted run; "
+             + ("every update starts from the initial parameters and zero moments (restored outside its timing), "
+                "so every mask sees the routing of the first update; " if args.fresh else "") +
              "a phase's cost is its launch minus the skeleton's.  MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; "
              "MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs) over the launch; HBM bytes "
              f"= FETCH_SIZE x {fetch_scale:.3f} + WRITE_SIZE x {write_scale:.3f} KiB (the copy calibration).", "",
@@ -286,7 +295,7 @@ def main(argv=None):
            "kernel_source_sha256": kernel_source_sha256(),
            "hbm_bytes_per_launch": full["hbm"] / M, "hbm_bytes_per_update": full["hbm"],
            "fetch_scale": fetch_scale, "write_scale": write_scale,
-           "command": f"python -m moe_step_megakernel_amd.profile --config {cfg.name}",
+           "command": f"python -m moe_step_megakernel_amd.profile --config {cfg.name}" + (" --fresh" if args.fresh else ""),
            "measured": time.strftime("%Y-%m-%d"), "steps_inside_phases": diffs}
     with open(os.path.join(args.out, f"moe_step_kernel_{cfg.name}_hbm_traffic.json"), "w") as fh:
         json.dump(doc, fh, indent=1)
