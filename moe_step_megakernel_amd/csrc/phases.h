@@ -62,9 +62,12 @@ struct Meta {
   int nsplit;                   // experts with more than one chunk
   int splitlist[kMaxExperts];   // those experts, ascending
   // skewed routing on a grid of 8 x P workgroups: the (expert, chunk) units of
-  // the weight-gradient products dealt to this workgroup's XCD (x = b % 8),
-  // packed as expert | chunk << 8, in the order its workgroups take them
+  // the weight-gradient products, packed as expert | chunk << 8, longest
+  // first; their tiles in that order (unit i holds tiles i*tpe .. i*tpe+tpe-1)
+  // are split into 8 contiguous ranges of about equal cost, and [xb, xe) is
+  // the range of this workgroup's XCD (x = b % 8)
   int nxu;
+  int xb, xe;
   int xunit[kMaxExperts + kMaxExperts / 2 + 1];
   float red[8];                 // block reductions
   BarrierState bar;             // grid-barrier bookkeeping (result broadcast, XCD membership)
@@ -180,13 +183,22 @@ __device__ __forceinline__ Span xcd_span_last(int n) {
 // descending expert row count and deals them over all workgroups in a snake
 // (0..G-1, G-1..0, ...), so every workgroup gets about the same sum of
 // contraction lengths.
+// Cost of a weight-gradient tile beyond its k-tiles, in k-tile units: the
+// read-modify-write of its 64 KB fp32 gradient block and the epilogue (skewed
+// Zipf routing, 16 x 8192 tokens: about 10 us against 0.4 us per k-tile).
+constexpr int kWTileFixed = 24;
+// route_order splits the tiles of both weight gradients (dW2: f x d, dW1: d x f)
+// with one tile count per expert
+static_assert(gemm::BM == gemm::BN, "square tiles: dW1 and dW2 have the same tiles per expert");
 struct WItem {
   int e, c, t;   // expert, chunk, tile within the expert
 };
-// With a grid of 8 x P workgroups, skewed routing keeps each (expert, chunk)
-// unit on one XCD (route_order assigns the units to XCDs, longest first, to the
-// least loaded one), so the unit's operand rows are fetched into one L2 only;
-// the XCD's P workgroups take its tiles in a snake in that unit order.
+// With a grid of 8 x P workgroups, skewed routing gives each XCD a contiguous
+// range of the units' tiles (units longest first) of about equal cost, where a
+// tile costs its k-tiles plus a fixed share for its fp32 gradient
+// read-modify-write, which dominates a short contraction.  A unit's operand
+// rows so go to one L2, or two where a range boundary splits it; the XCD's P
+// workgroups take the range's tiles in a snake.
 struct DealW {
   Span sp;
   bool snake, xl;
@@ -205,8 +217,9 @@ struct DealW {
     }
     const int q = i * G + ((i & 1) ? G - 1 - w : w);
     if (xl) {
-      const int u = meta.xunit[q / tpe];
-      return {u & 0xff, u >> 8, q % tpe};
+      const int g = meta.xb + q;
+      const int u = meta.xunit[g / tpe];
+      return {u & 0xff, u >> 8, g % tpe};
     }
     int r = 0;
     while (r + 1 < E && meta.cpre[r + 1] * tpe <= q) ++r;
@@ -221,7 +234,7 @@ __device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int E, int 
   dl.G = dl.xl ? (int)(gridDim.x >> 3) : (int)gridDim.x;   // the snake runs over the XCD's workgroups
   dl.w = dl.xl ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   dl.tpe = tpe;
-  dl.n = tpe * (dl.xl ? meta.nxu : dl.snake ? meta.cpre[E] : E);
+  dl.n = dl.xl ? meta.xe - meta.xb : tpe * (dl.snake ? meta.cpre[E] : E);
   dl.sp = xcd_span(dl.n);
   return dl;
 }
@@ -889,13 +902,14 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   }
   __syncthreads();
   if (meta.skewed && (G & 7) == 0) {
-    // (expert, chunk) units of the weight-gradient products, costed by their
-    // rows; ranked longest first (ties: expert order, then chunk), then each
-    // goes to the least loaded of the 8 XCDs (lowest index on ties).  Every
-    // workgroup computes the same assignment and keeps its own XCD's units.
-    int* ucost = posl + kThreads;            // [kThreads] unit costs, in expert-rank order
+    // (expert, chunk) units of the weight-gradient products, ranked by their
+    // rows, longest first (ties: expert order, then chunk).  A unit's tiles
+    // cost kWTileFixed + its k-tiles each; XCD x takes the tiles whose cost
+    // midpoint lies in [x C / 8, (x + 1) C / 8) of the total cost C, in that
+    // order.  Every workgroup computes the same split and keeps its own range.
+    int* ucost = posl + kThreads;            // [kThreads] unit rows, in expert-rank order
     int* uid = ucost + kThreads;             // [kThreads] the units
-    int* scost = uid + kThreads;             // [kThreads] costs, longest first
+    int* scost = uid + kThreads;             // [kThreads] rows, longest first
     int* suid = scost + kThreads;            // [kThreads] units, longest first
     const int nu = meta.cpre[E];             // units: the chunks of every expert
     if (tid < E) {
@@ -913,19 +927,36 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
       suid[rank] = uid[tid];
     }
     __syncthreads();
-    if (tid == 0) {
-      int load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const int mx = (int)(blockIdx.x & 7);
-      int m = 0;
+    if (tid < nu) meta.xunit[tid] = suid[tid];
+    // one thread per unit: its cost, the cost of the units before it, and how
+    // many of its tiles lie below the two bounds (summed in LDS)
+    long* upre = reinterpret_cast<long*>(suid + kThreads);   // [kThreads]
+    int* cntx = reinterpret_cast<int*>(upre + kThreads);     // [2]
+    const long tpe = (long)ceil_div(p.f, gemm::BM) * ceil_div(p.d, gemm::BN);
+    const long uc = tid < nu ? kWTileFixed + ceil_div(scost[tid], 64) : 0;
+    if (tid < nu) upre[tid] = tpe * uc;
+    if (tid < 2) cntx[tid] = 0;
+    __syncthreads();
+    if (tid < nu) {
+      long pre = 0, total = 0;
       for (int i = 0; i < nu; ++i) {
-        int x = 0;
-#pragma unroll
-        for (int y = 1; y < 8; ++y)
-          if (load[y] < load[x]) x = y;
-        load[x] += scost[i];
-        if (x == mx) meta.xunit[m++] = suid[i];
+        const long ci = upre[i];
+        pre += i < tid ? ci : 0;
+        total += ci;
       }
-      meta.nxu = m;
+      const int x = (int)(blockIdx.x & 7);
+      const long first = 8 * pre + 4 * uc;   // 8 x the midpoint of the unit's first tile
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const long lim = (long)(x + h) * total;
+        if (lim > first) atomicAdd(&cntx[h], (int)min(tpe, (lim - first - 1) / (8 * uc) + 1));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      meta.xb = cntx[0];
+      meta.xe = cntx[1];
+      meta.nxu = nu;
     }
     __syncthreads();
   }
@@ -1474,6 +1505,58 @@ __device__ __forceinline__ void ld_rows16(gemm::rsrc_t r, int vo, int so, int rb
 #undef MOE_LD16
 }
 
+// fp32 elements of 32 consecutive rows at byte offsets vo + u * rb (u =
+// 0..31) from a buffer descriptor's base: one assembly block with its own
+// wait, so all 32 loads are in flight together.
+__device__ __forceinline__ void ld_rows32_f32(gemm::rsrc_t r, int vo, int rb, float (&out)[32]) {
+  uint32_t v[32];
+  int off = vo;
+  asm volatile(
+      "buffer_load_dword %0, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %1, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %2, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %3, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %4, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %5, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %6, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %7, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %8, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %9, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %10, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %11, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %12, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %13, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %14, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %15, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %16, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %17, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %18, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %19, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %20, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %21, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %22, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %23, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %24, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %25, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %26, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %27, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %28, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %29, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %30, %32, %33, 0 offen\n\tv_add_u32 %32, %34, %32\n\t"
+      "buffer_load_dword %31, %32, %33, 0 offen\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+        "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
+        "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]),
+        "=&v"(v[21]), "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]),
+        "=&v"(v[28]), "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31]),
+        "+v"(off)
+      : "s"(r), "s"(rb)
+      : "memory");
+#pragma unroll
+  for (int u = 0; u < 32; ++u) out[u] = __uint_as_float(v[u]);
+}
+
 template <typename T, int NS>
 __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& meta, bool zero_experts) {
   const int tid = threadIdx.x;
@@ -1709,7 +1792,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
       // dW_r[c][e] = sum over token chunks (ascending) of the partials
       // one (expert, column) pair per thread, columns consecutive across the
       // threads so every chunk's partials are read in 1 KB pieces; the chunk
-      // partials are added in ascending chunk order, eight loads in flight
+      // partials are added in ascending chunk order, 32 loads in flight
       const int ir = item - n11 - n12;
       const int o = ir * kThreads + tid;
       float sq = 0.f;
@@ -1719,6 +1802,15 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
         const long stride = (long)E * d;
         float s = 0.f;
         int r = 0;
+        for (; r + 32 <= RCH; r += 32) {
+          // a descriptor based at chunk r's partials: 32 chunk rows of E * d floats
+          const gemm::rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(p.rpart + (long)r * stride), (short)0, (int)(32 * stride * 4), gemm::kRsrcWord3);
+          float v[32];
+          ld_rows32_f32(rr, o * 4, (int)(stride * 4), v);
+#pragma unroll
+          for (int u = 0; u < 32; ++u) s += v[u];
+        }
         for (; r + 8 <= RCH; r += 8) {
           float v[8];
 #pragma unroll
