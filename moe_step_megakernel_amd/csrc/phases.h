@@ -64,10 +64,11 @@ struct Meta {
   // skewed routing on a grid of 8 x P workgroups: the (expert, chunk) units of
   // the weight-gradient products, packed as expert | chunk << 8, longest
   // first; their tiles in that order (unit i holds tiles i*tpe .. i*tpe+tpe-1)
-  // are split into 8 contiguous ranges of about equal cost, and [xb, xe) is
-  // the range of this workgroup's XCD (x = b % 8)
+  // are split into 8 contiguous ranges of about equal cost, and [xb[h], xe[h])
+  // is the range of this workgroup's XCD (x = b % 8) in the dW2 (h = 0) and
+  // the dW1 (h = 1) phase, whose tiles weigh their fixed costs differently
   int nxu;
-  int xb, xe;
+  int xb[2], xe[2];
   int xunit[kMaxExperts + kMaxExperts / 2 + 1];
   float red[8];                 // block reductions
   BarrierState bar;             // grid-barrier bookkeeping (result broadcast, XCD membership)
@@ -184,9 +185,11 @@ __device__ __forceinline__ Span xcd_span_last(int n) {
 // (0..G-1, G-1..0, ...), so every workgroup gets about the same sum of
 // contraction lengths.
 // Cost of a weight-gradient tile beyond its k-tiles, in k-tile units: the
-// read-modify-write of its 64 KB fp32 gradient block and the epilogue (skewed
-// Zipf routing, 16 x 8192 tokens: about 10 us against 0.4 us per k-tile).
-constexpr int kWTileFixed = 24;
+// read-modify-write of its 64 KB fp32 gradient block and the epilogue.  Fitted
+// to per-workgroup clocks under skewed Zipf routing (16 x 8192 tokens): in the
+// dW2 phase about 9 us per tile against 0.4 us per k-tile of a long
+// contraction, in the dW1 phase about 6 us against 0.55 us.
+constexpr int kWTileFixed[2] = {24, 11};
 // route_order splits the tiles of both weight gradients (dW2: f x d, dW1: d x f)
 // with one tile count per expert
 static_assert(gemm::BM == gemm::BN, "square tiles: dW1 and dW2 have the same tiles per expert");
@@ -202,7 +205,7 @@ struct WItem {
 struct DealW {
   Span sp;
   bool snake, xl;
-  int G, w, tpe, n;
+  int G, w, tpe, n, h;
   __device__ __forceinline__ int count() const {
     if (!snake) return sp.count();
     const int full = n / G, rem = n % G;   // rounds of G items, then a partial round
@@ -217,7 +220,7 @@ struct DealW {
     }
     const int q = i * G + ((i & 1) ? G - 1 - w : w);
     if (xl) {
-      const int g = meta.xb + q;
+      const int g = meta.xb[h] + q;
       const int u = meta.xunit[g / tpe];
       return {u & 0xff, u >> 8, g % tpe};
     }
@@ -227,14 +230,15 @@ struct DealW {
     return {meta.ord[r], rem / tpe, rem % tpe};
   }
 };
-__device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int E, int tpe) {
+__device__ __forceinline__ DealW deal_weight_tiles(const Meta& meta, int E, int tpe, int h) {
   DealW dl;
+  dl.h = h;
   dl.snake = meta.skewed != 0;
   dl.xl = dl.snake && (gridDim.x & 7) == 0;
   dl.G = dl.xl ? (int)(gridDim.x >> 3) : (int)gridDim.x;   // the snake runs over the XCD's workgroups
   dl.w = dl.xl ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   dl.tpe = tpe;
-  dl.n = dl.xl ? meta.xe - meta.xb : tpe * (dl.snake ? meta.cpre[E] : E);
+  dl.n = dl.xl ? meta.xe[h] - meta.xb[h] : tpe * (dl.snake ? meta.cpre[E] : E);
   dl.sp = xcd_span(dl.n);
   return dl;
 }
@@ -904,9 +908,10 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   if (meta.skewed && (G & 7) == 0) {
     // (expert, chunk) units of the weight-gradient products, ranked by their
     // rows, longest first (ties: expert order, then chunk).  A unit's tiles
-    // cost kWTileFixed + its k-tiles each; XCD x takes the tiles whose cost
-    // midpoint lies in [x C / 8, (x + 1) C / 8) of the total cost C, in that
-    // order.  Every workgroup computes the same split and keeps its own range.
+    // cost kWTileFixed[phase] + its k-tiles each; XCD x takes the tiles whose
+    // cost midpoint lies in [x C / 8, (x + 1) C / 8) of the total cost C, in
+    // that order, once per weight-gradient phase.  Every workgroup computes the
+    // same splits and keeps its own ranges.
     int* ucost = posl + kThreads;            // [kThreads] unit rows, in expert-rank order
     int* uid = ucost + kThreads;             // [kThreads] the units
     int* scost = uid + kThreads;             // [kThreads] rows, longest first
@@ -928,34 +933,46 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     }
     __syncthreads();
     if (tid < nu) meta.xunit[tid] = suid[tid];
-    // one thread per unit: its cost, the cost of the units before it, and how
-    // many of its tiles lie below the two bounds (summed in LDS)
-    long* upre = reinterpret_cast<long*>(suid + kThreads);   // [kThreads]
-    int* cntx = reinterpret_cast<int*>(upre + kThreads);     // [2]
+    // one thread per unit: its cost in both phases, the cost of the units
+    // before it, and how many of its tiles lie below the XCD's two bounds
+    // (summed in LDS)
+    long* upre = reinterpret_cast<long*>(suid + kThreads);   // [2][kThreads]
+    int* cntx = reinterpret_cast<int*>(upre + 2 * kThreads);  // [2][2]
     const long tpe = (long)ceil_div(p.f, gemm::BM) * ceil_div(p.d, gemm::BN);
-    const long uc = tid < nu ? kWTileFixed + ceil_div(scost[tid], 64) : 0;
-    if (tid < nu) upre[tid] = tpe * uc;
-    if (tid < 2) cntx[tid] = 0;
+    const int x = (int)(blockIdx.x & 7);
+    const long kt = tid < nu ? ceil_div(scost[tid], 64) : 0;
+    if (tid < nu) {
+      upre[tid] = tpe * (kWTileFixed[0] + kt);
+      upre[kThreads + tid] = tpe * (kWTileFixed[1] + kt);
+    }
+    if (tid < 4) cntx[tid] = 0;
     __syncthreads();
     if (tid < nu) {
-      long pre = 0, total = 0;
-      for (int i = 0; i < nu; ++i) {
-        const long ci = upre[i];
-        pre += i < tid ? ci : 0;
-        total += ci;
-      }
-      const int x = (int)(blockIdx.x & 7);
-      const long first = 8 * pre + 4 * uc;   // 8 x the midpoint of the unit's first tile
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const long lim = (long)(x + h) * total;
-        if (lim > first) atomicAdd(&cntx[h], (int)min(tpe, (lim - first - 1) / (8 * uc) + 1));
+      for (int ph = 0; ph < 2; ++ph) {
+        const long uc = kWTileFixed[ph] + kt;
+        long pre = 0, total = 0;
+        for (int i = 0; i < nu; ++i) {
+          const long ci = upre[ph * kThreads + i];
+          pre += i < tid ? ci : 0;
+          total += ci;
+        }
+        const long first = 8 * pre + 4 * uc;   // 8 x the midpoint of the unit's first tile
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const long lim = (long)(x + hh) * total;
+          // every tile below the bound, none, or (one unit per bound) a division
+          if (lim > first + 8 * uc * (tpe - 1)) atomicAdd(&cntx[2 * ph + hh], (int)tpe);
+          else if (lim > first) atomicAdd(&cntx[2 * ph + hh], (int)((lim - first - 1) / (8 * uc) + 1));
+        }
       }
     }
     __syncthreads();
     if (tid == 0) {
-      meta.xb = cntx[0];
-      meta.xe = cntx[1];
+      meta.xb[0] = cntx[0];
+      meta.xe[0] = cntx[1];
+      meta.xb[1] = cntx[2];
+      meta.xe[1] = cntx[3];
       meta.nxu = nu;
     }
     __syncthreads();
@@ -1579,7 +1596,7 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
   // same mix (the kinds differ a lot in cost)
   // (a cost-weighted deal as in dW1 + dX measured slower here at 2x1024 and
   // no faster at 32x1024)
-  const DealW d10 = deal_weight_tiles(meta, E, MT10 * NT10);
+  const DealW d10 = deal_weight_tiles(meta, E, MT10 * NT10, 0);
   const Span s9 = xcd_span(n9), sr = xcd_span_last(nr);
   const int c10 = d10.count();
   const int c9 = s9.count();
@@ -1724,7 +1741,7 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   float* gw1 = p.grads + (long)d * E;
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
-  DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11);
+  DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11, 1);
   Span s12 = xcd_span(n12);
   const Span srr = xcd_span_last(nrr);
   // dW1 tiles: k-tiles over the mean rows per expert; dX tiles: over f.  Built
