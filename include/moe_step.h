@@ -102,6 +102,27 @@ typedef struct {
                              loses one [tokens * top_k, d_ff] tensor; the update
                              is slower (each H element passes through GELU once
                              per output column tile that reads it). */
+  int32_t max_microbatches; /* 0 or 1: every launch adds its expert weight
+                             gradients to grads (the default).  M in [2, 16]
+                             (bf16 handles, not with MOE_MEM_RECOMPUTE):
+                             deferred expert weight gradients.  The pages
+                             accumulate one update over several microbatch
+                             launches ("How GPUs usually run it"); the expert
+                             weights do not change within an update, so here a
+                             launch that does not apply the experts keeps the
+                             operand rows of its dW1 / dW2 products (about
+                             2 * T * k * (d + f) bytes) in one of M arena slots,
+                             and the launch that applies them contracts dW1 and
+                             dW2 once over the rows of every slot, writing the
+                             W1 / W2 part of grads (added to it when the slot-0
+                             launch did not zero the gradients).  A launch with
+                             MOE_RUN_ZERO_GRAD(_EXPERTS) takes slot 0, each later
+                             one the next slot; more than M launches before the
+                             experts are applied is MOE_ERR_STATE.  Between those
+                             launches the W1 / W2 part of grads is not updated;
+                             the router gradient is added every launch as
+                             without deferral.  Results equal the default's up to
+                             the order of fp32 accumulation. */
 } moe_step_config;
 
 #define MOE_MEM_RECOMPUTE 0x1u

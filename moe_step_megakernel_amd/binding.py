@@ -46,6 +46,7 @@ class moe_step_config(ctypes.Structure):
         ("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
         ("adam_eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("clip_norm", ctypes.c_double),
         ("device", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32), ("memory_rules", ctypes.c_uint32),
+        ("max_microbatches", ctypes.c_int32),
     ]
 
 
@@ -105,11 +106,11 @@ def load_library():
 
 def make_config(d_model, d_ff, n_experts, top_k, max_tokens, dtype="bf16", lr=1e-3, beta1=0.9, beta2=0.999,
                 adam_eps=1e-8, weight_decay=0.01, clip_norm=1.0, device=0, wg_per_cu=0,
-                memory_rules=0) -> moe_step_config:
+                memory_rules=0, max_microbatches=0) -> moe_step_config:
     return moe_step_config(
         ctypes.sizeof(moe_step_config), MOE_STEP_ABI_VERSION, d_model, d_ff, n_experts, top_k, max_tokens,
         MOE_DTYPE_BF16 if dtype == "bf16" else MOE_DTYPE_F32, lr, beta1, beta2, adam_eps, weight_decay,
-        clip_norm, device, wg_per_cu, memory_rules)
+        clip_norm, device, wg_per_cu, memory_rules, max_microbatches)
 
 
 # --- the C entry points, same names -------------------------------------------------------------

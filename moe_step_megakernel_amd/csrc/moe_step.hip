@@ -57,6 +57,18 @@ int check_config(const moe_step_config* c, char* err) {
     set_err(err, "unknown memory rules 0x%x", c->memory_rules);
     return MOE_ERR_ARG;
   }
+  if (c->max_microbatches < 0 || c->max_microbatches > moe::kMaxSlots) {
+    set_err(err, "max_microbatches must be in [0, %d]", moe::kMaxSlots);
+    return MOE_ERR_ARG;
+  }
+  if (c->max_microbatches > 1 && (c->dtype != MOE_DTYPE_BF16 || (c->memory_rules & MOE_MEM_RECOMPUTE))) {
+    set_err(err, "deferred weight gradients (max_microbatches > 1) need a bf16 handle without MOE_MEM_RECOMPUTE");
+    return MOE_ERR_ARG;
+  }
+  if ((long long)c->max_microbatches * c->max_tokens * c->top_k >= (1LL << 30)) {
+    set_err(err, "max_microbatches * max_tokens * top_k must stay below 2^30");
+    return MOE_ERR_SHAPE;
+  }
   if (c->wg_per_cu < 0 || c->wg_per_cu > 2) {
     set_err(err, "wg_per_cu must be 0, 1 or 2");
     return MOE_ERR_ARG;
@@ -151,7 +163,19 @@ struct moe_step {
   void* xs;
   float* wpart2;
   float* wpart1;
+  int wpart_sets = 0;
   unsigned* ctrl;
+  // deferred weight gradients (cfg.max_microbatches > 1): per-slot arrays and
+  // the slot of the last launch (-1: the experts were applied, or none yet)
+  char* slot_act = nullptr;
+  char* slot_dout = nullptr;
+  char* slot_xs = nullptr;
+  char* slot_dh = nullptr;
+  long stride_nf = 0, stride_nd = 0;
+  int* slot_cnt = nullptr;
+  int* slot_off = nullptr;
+  int defer_slot = -1;
+  bool defer_zero = false;
 };
 
 // Chooses the kernel (element type, workgroups per compute unit), sets its LDS
@@ -226,8 +250,17 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
   //   dH [N, f]:      written by the dH tiles after the combine's barrier;
   //   A  [N, f]:      written by GEMM 1, last read by the dW2 tiles;
   //   dXs [N, d]:     written by the dX tiles after that phase's barrier.
-  const size_t o_out_dh = take(std::max(N * d * 4, N * f * es));
-  const size_t o_act_dxs = take(std::max(N * f * es, N * d * es));
+  // With deferred weight gradients A, dH, dO and X_e live in per-slot arrays
+  // until the applying launch, so O and dXs get buffers of their own.
+  const bool defer = c.max_microbatches > 1;
+  const size_t M = defer ? (size_t)c.max_microbatches : 0;
+  const size_t o_out_dh = take(defer ? N * d * 4 : std::max(N * d * 4, N * f * es));
+  const size_t o_act_dxs = take(defer ? N * d * es : std::max(N * f * es, N * d * es));
+  const size_t snf = align_up(N * f * es, 256), snd = align_up(N * d * es, 256);
+  const size_t o_slot_act = take(M * snf), o_slot_dh = take(M * snf);
+  const size_t o_slot_dout = take(M * snd), o_slot_xs = take(M * snd);
+  const size_t o_slot_cnt = take(defer ? (size_t)moe::kMaxSlots * E * 4 : 0);
+  const size_t o_slot_off = take(defer ? (size_t)moe::kMaxSlots * E * 4 : 0);
   // G' [N, f]: not kept under the recomputation rule (the dH epilogue forms it from H)
   const bool recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) != 0u;
   const size_t o_gp = take(recompute ? 0 : N * f * es), o_dout = take(N * d * es);
@@ -238,10 +271,13 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
   const size_t o_shadow = c.dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
   const size_t o_xs = c.dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
   // partial weight-gradient tiles of split contractions (skewed routing): at most
-  // E/2 extra chunks over all experts, each a 128 x 128 fp32 tile per gradient tile
+  // E/2 extra chunks over all experts (E in the applying launch of deferred
+  // weight gradients), each a 128 x 128 fp32 tile per gradient tile; the
+  // kernel never splits into more than the buffers hold
   const size_t wtiles = (size_t)cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
-  const size_t o_wpart2 = take(((size_t)E / 2 + 1) * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
-  const size_t o_wpart1 = take(((size_t)E / 2 + 1) * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
+  const size_t xchunks = c.max_microbatches > 1 ? (size_t)E + 1 : (size_t)E / 2 + 1;
+  const size_t o_wpart2 = take(xchunks * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
+  const size_t o_wpart1 = take(xchunks * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
   const int nrb = (int)((N + moe::gemm::BM - 1) / moe::gemm::BM) + E;   // row tiles of GEMM 1 (upper bound)
   const size_t o_ready = take((size_t)nrb * 4);
   if (base) {
@@ -269,6 +305,17 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
     h.xs = c.dtype == MOE_DTYPE_BF16 ? a + o_xs : nullptr;
     h.wpart2 = reinterpret_cast<float*>(a + o_wpart2);
     h.wpart1 = reinterpret_cast<float*>(a + o_wpart1);
+    h.wpart_sets = (int)xchunks;
+    if (defer) {
+      h.slot_act = a + o_slot_act;
+      h.slot_dh = a + o_slot_dh;
+      h.slot_dout = a + o_slot_dout;
+      h.slot_xs = a + o_slot_xs;
+      h.stride_nf = (long)snf;
+      h.stride_nd = (long)snd;
+      h.slot_cnt = reinterpret_cast<int*>(a + o_slot_cnt);
+      h.slot_off = reinterpret_cast<int*>(a + o_slot_off);
+    }
   }
   return off;
 }
@@ -460,6 +507,7 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.xs = h->xs;
   p.wpart2 = h->wpart2;
   p.wpart1 = h->wpart1;
+  p.wpart_sets = h->wpart_sets;
   p.ctrl.gen = h->ctrl;
   p.ctrl.status = h->ctrl + 32;
   p.ctrl.abort = h->ctrl + 64;
@@ -471,6 +519,41 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.epoch = ++h->epoch;
   p.recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) ? 1 : 0;
   p.nt_stores = (long)n_tokens * c.top_k >= kNonTemporalRows ? 1 : 0;
+  // deferred weight gradients: this launch's slot of the update
+  int slot = -1;
+  const bool zero_e = (run_flags & MOE_RUN_ZERO_GRAD_EXPERTS) != 0u;
+  if (c.max_microbatches > 1) {
+    if (static_arena || !h->slot_act) {
+      set_err(err, "deferred weight gradients need a handle (max_microbatches > 1)");
+      return MOE_ERR_ARG;
+    }
+    if (run_flags & (MOE_RUN_SKIP_MASK | MOE_RUN_TEST_TIMEOUT)) {
+      set_err(err, "phase skipping and the timeout test are not available with deferred weight gradients");
+      return MOE_ERR_ARG;
+    }
+    slot = zero_e ? 0 : h->defer_slot + 1;
+    if (slot >= c.max_microbatches) {
+      set_err(err, "launch %d of an update whose experts are not applied yet; max_microbatches is %d", slot + 1,
+              c.max_microbatches);
+      return MOE_ERR_STATE;
+    }
+    p.defer = 1;
+    p.slot = slot;
+    p.defer_final = apply_e ? 1 : 0;
+    p.defer_zero = (slot == 0 ? zero_e : h->defer_zero) ? 1 : 0;
+    p.slot_act = h->slot_act;
+    p.slot_dout = h->slot_dout;
+    p.slot_xs = h->slot_xs;
+    p.slot_dh = h->slot_dh;
+    p.stride_nf = h->stride_nf;
+    p.stride_nd = h->stride_nd;
+    p.slot_cnt = h->slot_cnt;
+    p.slot_off = h->slot_off;
+    p.act = h->slot_act + (long)slot * h->stride_nf;
+    p.dh = h->slot_dh + (long)slot * h->stride_nf;
+    p.dout = h->slot_dout + (long)slot * h->stride_nd;
+    p.xs = h->slot_xs + (long)slot * h->stride_nd;
+  }
 
   hipError_t he = hipSetDevice(c.device);
   if (he != hipSuccess) {
@@ -505,6 +588,10 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   }
   h->last_stream = stream;
   h->launched = true;
+  if (slot >= 0) {
+    if (slot == 0) h->defer_zero = zero_e;
+    h->defer_slot = apply_e ? -1 : slot;
+  }
   if (run_flags & MOE_RUN_TEST_TIMEOUT) h->last_full_tokens = -1;
   else if (!(run_flags & MOE_RUN_SKIP_MASK)) h->last_full_tokens = n_tokens;
   return MOE_OK;

@@ -10,7 +10,8 @@
 // last with MOE_RUN_APPLY.  Prints one line per skip mask with ms/update.
 //
 //   moe_step_bench [--config NAME | --inputs FILE] [--steps K] [--warmup W] [--skip MASK[,MASK...]]
-//                  [--wg-per-cu N] [--ready] [--coop] [--recompute] [--per-wg-barrier] [--fresh] [--copy-mib N]
+//                  [--wg-per-cu N] [--ready] [--coop] [--recompute] [--per-wg-barrier] [--fresh] [--defer]
+//                  [--copy-mib N]
 //     NAME: tiny_f32 | bf16_2x1024 | bf16_32x1024 | top8_4x1024 (--tokens N changes its token count)
 //     --skip MASK: after the warm-up, time K updates whose launches skip the
 //                  phases in MASK (bit i = phase i, 0..7; bit 8 = the dispatch
@@ -22,6 +23,8 @@
 //              before its first launch and outside its timing (events around
 //              each update's launches), so every update routes like the first;
 //              without it the parameters keep training from update to update
+//     --defer: deferred expert weight gradients (max_microbatches = the
+//              update's microbatch count, when more than one)
 //     --copy-mib N: instead, time a plain device copy of N MiB (read N, write N),
 //                  the reference for scaling memory counters
 #include <hip/hip_runtime.h>
@@ -118,7 +121,7 @@ int main(int argc, char** argv) {
   std::string cfg_name = "bf16_2x1024", inputs;
   int tokens = 0;   // --tokens: tokens per launch for a built-in shape (0 = the shape's own)
   int steps = 20, warmup = 3, copy_mib = 0, wg_per_cu = 0;
-  bool ready = false, coop = false, recompute = false, per_wg = false, fresh = false;
+  bool ready = false, coop = false, recompute = false, per_wg = false, fresh = false, defer = false;
   std::vector<unsigned> skips{0u};
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -152,6 +155,7 @@ int main(int argc, char** argv) {
     else if (a == "--recompute") recompute = true;
     else if (a == "--per-wg-barrier") per_wg = true;
     else if (a == "--fresh") fresh = true;
+    else if (a == "--defer") defer = true;
     else {
       std::fprintf(stderr, "unknown argument %s\n", a.c_str());
       return 1;
@@ -228,6 +232,7 @@ int main(int argc, char** argv) {
   cfg.clip_norm = 1.0;
   cfg.wg_per_cu = wg_per_cu;
   cfg.memory_rules = recompute ? MOE_MEM_RECOMPUTE : 0u;
+  cfg.max_microbatches = defer && M > 1 ? M : 0;
   moe_step_t h = nullptr;
   if (moe_step_create(&cfg, &h) != MOE_OK) {
     std::fprintf(stderr, "moe_step_create: %s\n", moe_step_last_error(nullptr));

@@ -24,7 +24,10 @@
 namespace moe {
 
 constexpr int kPhases = 8;
-constexpr int kMetaBytes = 3072;
+constexpr int kMetaBytes = 4096;
+// microbatch slots of deferred expert weight gradients (one per launch of an
+// update, from its first launch to the one that applies the experts)
+constexpr int kMaxSlots = 16;
 // OCC workgroups per compute unit: the kernel is built for one (all of a
 // SIMD's registers per wave, 4-stage GEMM pipeline) or two (at most 256
 // registers per wave, 2-stage pipeline, half the LDS each).
@@ -69,9 +72,17 @@ struct Meta {
   // the dW1 (h = 1) phase, whose tiles weigh their fixed costs differently
   int nxu;
   int xb[2], xe[2];
-  int xunit[kMaxExperts + kMaxExperts / 2 + 1];
+  int xunit[3 * kMaxExperts + 1];   // E units plus the extra chunks (at most E under the rules below)
   float red[8];                 // block reductions
   BarrierState bar;             // grid-barrier bookkeeping (result broadcast, XCD membership)
+  // rows of each expert that the weight-gradient products of this launch
+  // contract over: its own (cnt), or with deferred weight gradients those of
+  // every slot of the update in the applying launch and none in the others
+  int wcnt[kMaxExperts];
+  int wtot;
+  // deferred weight gradients: one expert's rows (cnt, first sorted position)
+  // in each slot, filled per tile
+  int stab[2][kMaxSlots];
 };
 static_assert(sizeof(Meta) <= kMetaBytes, "meta");
 
@@ -123,8 +134,23 @@ struct KParams {
   uint16_t* shadow;  // [2*E*d*f] bf16 copy of W1 | W2 (bf16 mode)
   float* wpart2;     // partial dW2 tiles of split contractions [blocks][tiles per expert][128 x 128]
   float* wpart1;     // the same for dW1
+  int wpart_sets;    // blocks each of them holds (extra chunks over all experts)
   int nt_stores;     // product outputs written with non-temporal stores (large launches)
   void* xs;          // [N, d] token rows in expert order (bf16 mode), written by route_order
+  // deferred expert weight gradients (bf16): act, dout, xs and dh above are
+  // this launch's slot of per-slot arrays; the launch that applies the
+  // experts contracts dW1 / dW2 over the rows of slots 0..slot
+  int defer;         // 1: weight gradients deferred to the applying launch
+  int slot;          // this launch's slot
+  int defer_final;   // this launch applies the experts: the dW products run, over every slot
+  int defer_zero;    // the update's slot-0 launch zeroed the expert gradients (write, not add)
+  const char* slot_act;   // slot 0 of act, dout, xs, dh; slot s at + s * stride
+  const char* slot_dout;
+  const char* slot_xs;
+  const char* slot_dh;
+  long stride_nf, stride_nd;   // bytes per slot of the [N, f] and [N, d] arrays
+  int* slot_cnt;     // [kMaxSlots][E] rows of each expert per slot
+  int* slot_off;     // [kMaxSlots][E] first sorted position of each expert per slot
   Ctrl ctrl;
 };
 
@@ -190,6 +216,7 @@ __device__ __forceinline__ Span xcd_span_last(int n) {
 // dW2 phase about 9 us per tile against 0.4 us per k-tile of a long
 // contraction, in the dW1 phase about 6 us against 0.55 us.
 constexpr int kWTileFixed[2] = {24, 11};
+static_assert(3 * kMaxExperts <= kThreads, "route_order ranks the weight-gradient units one per thread");
 // route_order splits the tiles of both weight gradients (dW2: f x d, dW1: d x f)
 // with one tile count per expert
 static_assert(gemm::BM == gemm::BN, "square tiles: dW1 and dW2 have the same tiles per expert");
@@ -873,21 +900,58 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
   }
   __syncthreads();
   if (tid < E) {
+    // the rows the weight-gradient products contract over; with deferred
+    // weight gradients this launch's counts and offsets go to its slot (the
+    // applying launch reads the earlier slots', written by earlier launches)
+    int w = meta.cnt[tid];
+    if (p.defer) {
+      if (lwg == 0) {
+        p.slot_cnt[p.slot * E + tid] = meta.cnt[tid];
+        p.slot_off[p.slot * E + tid] = meta.off[tid];
+      }
+      if (p.defer_final)
+        for (int s = 0; s < p.slot; ++s) w += p.slot_cnt[s * E + tid];
+      else
+        w = 0;
+    }
+    meta.wcnt[tid] = w;
+  }
+  __syncthreads();
+  if (tid < E) {
     // rank of this expert by row count, for dealing the weight-gradient tiles
-    const int c = meta.cnt[tid];
+    const int c = meta.wcnt[tid];
     int r = 0;
-    for (int e = 0; e < E; ++e) r += (meta.cnt[e] > c) || (meta.cnt[e] == c && e < tid);
+    for (int e = 0; e < E; ++e) r += (meta.wcnt[e] > c) || (meta.wcnt[e] == c && e < tid);
     meta.ord[r] = tid;
   }
   if (tid == 0) {
-    int mx = 0;
-    for (int e = 0; e < E; ++e) mx = max(mx, meta.cnt[e]);
-    meta.skewed = (long)mx * E > 2L * meta.off[E];
-    const int kc = 64 * max(1, ceil_div(ceil_div(2 * meta.off[E], max(E, 1)), 64));
+    int mx = 0, tot = 0;
+    for (int e = 0; e < E; ++e) {
+      mx = max(mx, meta.wcnt[e]);
+      tot += meta.wcnt[e];
+    }
+    meta.wtot = tot;
+    // The applying launch of deferred weight gradients contracts over every
+    // slot's rows: its contractions are long and few per workgroup, so it
+    // always splits them, in chunks of the mean rows per expert (at most E
+    // extra chunks; half the mean measured 0.6% slower on the Zipf workload,
+    // its extra partial tiles costing more than the finer deal saved);
+    // otherwise chunks of twice the mean under skew (at most E/2 extra).
+    const bool dfin = p.defer && p.defer_final;
+    meta.skewed = dfin ? tot > 0 : (long)mx * E > 2L * tot;
+    int kc = 64 * max(1, ceil_div(ceil_div(ceil_div(2 * tot, max(E, 1)), dfin ? 2 : 1), 64));
+    // never more extra chunks than the partial-tile buffers hold (the rule
+    // above stays within them; this keeps any other rule inside too)
+    for (;;) {
+      int extra = 0;
+      for (int e = 0; e < E; ++e) extra += meta.skewed ? max(1, ceil_div(meta.wcnt[e], kc)) - 1 : 0;
+      if (extra <= p.wpart_sets) break;
+      kc *= 2;
+    }
     meta.kc = kc;
     int pb = 0, ns = 0;
     for (int e = 0; e < E; ++e) {
-      const int n = meta.skewed ? max(1, ceil_div(meta.cnt[e], kc)) : 1;
+      const int n = meta.skewed ? max(1, ceil_div(meta.wcnt[e], kc)) : 1;
       meta.nch[e] = n;
       meta.pbase[e] = pb;
       pb += n - 1;
@@ -920,7 +984,7 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     if (tid < E) {
       const int e = meta.ord[tid];
       for (int c = 0; c < meta.nch[e]; ++c) {
-        ucost[meta.cpre[tid] + c] = meta.nch[e] > 1 ? min(meta.kc, meta.cnt[e] - c * meta.kc) : meta.cnt[e];
+        ucost[meta.cpre[tid] + c] = meta.nch[e] > 1 ? min(meta.kc, meta.wcnt[e] - c * meta.kc) : meta.wcnt[e];
         uid[meta.cpre[tid] + c] = e | (c << 8);
       }
     }
@@ -1430,26 +1494,64 @@ template <typename T, int NS, bool GA = false>
 __device__ __forceinline__ void weight_grad_tile(const KParams& p, char* lds, Meta& meta, const WItem& wi,
                                                  const char* abase, const int* amap, int adiv, int M,
                                                  const char* bbase, int N, int m0, int n0, float* g, float* part,
-                                                 int tpe, bool zero, int nidx) {
+                                                 int tpe, bool zero, int nidx, const char* aslot0 = nullptr,
+                                                 long astride = 0, const char* bslot0 = nullptr, long bstride = 0) {
   const int e = wi.e, S = meta.nch[e], kc = meta.kc;
   const int r0 = S > 1 ? wi.c * kc : 0;
-  const int rows = S > 1 ? min(kc, meta.cnt[e] - r0) : meta.cnt[e];
+  const int rows = S > 1 ? min(kc, meta.wcnt[e] - r0) : meta.wcnt[e];
   const int pe = meta.off[e] + r0;
   gemm::Operand A{abase, M, amap, adiv, pe, rows, M, m0};
   gemm::Operand B{bbase, N, nullptr, 1, pe, rows, N, n0};
+  // deferred weight gradients (bf16, the applying launch): the contraction
+  // runs over the expert's rows of every slot, in slot order; rows [r0, r0 +
+  // rows) of that concatenation, one operand piece per slot they touch
+  const bool deferred = sizeof(T) == 2 && p.defer;
+  const int nsl = p.slot + 1;
+  if (deferred) {
+    __syncthreads();   // the previous tile is done with meta.stab
+    if (threadIdx.x < nsl) {
+      const int s = threadIdx.x;
+      const bool own = s == p.slot;
+      meta.stab[0][s] = own ? meta.cnt[e] : p.slot_cnt[s * p.E + e];
+      meta.stab[1][s] = own ? meta.off[e] : p.slot_off[s * p.E + e];
+    }
+    __syncthreads();
+    zero = p.defer_zero != 0;
+  }
+  auto piece = [&](int s, gemm::Operand& pa, gemm::Operand& pb, int& K) {
+    int pre = 0;   // the expert's rows in the slots before s
+    for (int q = 0; q < s; ++q) pre += meta.stab[0][q];
+    const int lo = max(r0, pre), hi = min(r0 + rows, pre + meta.stab[0][s]);
+    if (lo >= hi) return false;
+    const int ps = meta.stab[1][s] + lo - pre;
+    pa = gemm::Operand{aslot0 + s * astride, M, nullptr, 1, ps, hi - lo, M, m0};
+    pb = gemm::Operand{bslot0 + s * bstride, N, nullptr, 1, ps, hi - lo, N, n0};
+    K = hi - lo;
+    return true;
+  };
+  auto run = [&](auto&& epi, auto&& pre) {
+    if constexpr (sizeof(T) == 2) {
+      if (deferred) {
+        gemm::tile_dma_pieces<NS, true, true, GA>(lds, nsl, piece, epi, pre);
+        return;
+      }
+    }
+    gemm::tile<T, NS, true, true, GA>(lds, A, B, rows, epi, pre);
+  };
   if (wi.c > 0) {
     float* pt = part + ((long)(meta.pbase[e] + wi.c - 1) * tpe + wi.t) * (gemm::BM * gemm::BN);
-    gemm::tile<T, NS, true, true, GA>(lds, A, B, rows, [&](int r, int c, const float (&v)[8]) {
-      F8 o;
+    run(
+        [&](int r, int c, const float (&v)[8]) {
+          F8 o;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) o.v[u] = v[u];
-      st8s(pt + r * gemm::BN + c, o, p.nt_stores);
-    });
+          for (int u = 0; u < 8; ++u) o.v[u] = v[u];
+          st8s(pt + r * gemm::BN + c, o, p.nt_stores);
+        },
+        gemm::NoPre());
     return;
   }
   float sq = 0.f;
-  gemm::tile<T, NS, true, true, GA>(
-      lds, A, B, rows,
+  run(
       [&](int r, int c, const float (&v)[8], const Raw8<float>& old) {
         if (m0 + r < M && n0 + c < N) {
           F8 nv = cvt8(old);
@@ -1598,7 +1700,9 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
   // no faster at 32x1024)
   const DealW d10 = deal_weight_tiles(meta, E, MT10 * NT10, 0);
   const Span s9 = xcd_span(n9), sr = xcd_span_last(nr);
-  const int c10 = d10.count();
+  // deferred weight gradients: only the applying launch has dW2 tiles
+  const bool wgrad = !p.defer || p.defer_final;
+  const int c10 = wgrad ? d10.count() : 0;
   const int c9 = s9.count();
   const int cr = max(0, ceil_div(sr.end - sr.begin, sr.step));
   for (int q = 0; q < c10 + c9 + cr; ++q) {
@@ -1611,11 +1715,13 @@ __device__ __forceinline__ void phase_bwd2(const KParams& p, char* lds, Meta& me
       if (p.recompute)
         weight_grad_tile<T, NS, true>(p, lds, meta, wi, reinterpret_cast<const char*>(p.act), nullptr, 1, f,
                                       reinterpret_cast<const char*>(p.dout), d, m0, n0, gw2 + (long)e * f * d,
-                                      p.wpart2, MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
+                                      p.wpart2, MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t,
+                                      p.slot_act, p.stride_nf, p.slot_dout, p.stride_nd);
       else
         weight_grad_tile<T, NS, false>(p, lds, meta, wi, reinterpret_cast<const char*>(p.act), nullptr, 1, f,
                                        reinterpret_cast<const char*>(p.dout), d, m0, n0, gw2 + (long)e * f * d,
-                                       p.wpart2, MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t);
+                                       p.wpart2, MT10 * NT10, zero_experts, e * (MT10 * NT10) + wi.t,
+                                      p.slot_act, p.stride_nf, p.slot_dout, p.stride_nd);
       continue;
     }
     const int item = q < c10 + c9 ? n10 + s9.item(q - c10)
@@ -1742,18 +1848,20 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
   T* dxs = reinterpret_cast<T*>(p.dxs);
 
   DealW d11 = deal_weight_tiles(meta, E, MT11 * NT11, 1);
+  // deferred weight gradients: only the applying launch has dW1 tiles
+  const bool wgrad = !p.defer || p.defer_final;
   Span s12 = xcd_span(n12);
   const Span srr = xcd_span_last(nrr);
   // dW1 tiles: k-tiles over the mean rows per expert; dX tiles: over f.  Built
   // into the kernel for two workgroups per CU only (large batches), where it
   // measured faster; in the other kernel its code alone cost more than it saved.
   if constexpr (NS == 2)
-    if (!d11.snake) cost_deal(n11, ceil_div(meta.off[E], 64 * E) + 6, n12, ceil_div(f, 64) + 3, d11.sp, s12);
+    if (!d11.snake && wgrad) cost_deal(n11, ceil_div(meta.wtot, 64 * E) + 6, n12, ceil_div(f, 64) + 3, d11.sp, s12);
   // fix-ups of the dW2 tiles whose contraction was split in the previous phase
   const int tpe10 = ceil_div(f, gemm::BM) * ceil_div(d, gemm::BN);
   const int nfx = fix_dw2 ? meta.nsplit * tpe10 : 0;
   const Span sfx = xcd_span(nfx);
-  const int c11 = d11.count();
+  const int c11 = wgrad ? d11.count() : 0;
   const int c12 = s12.count();
   const int crr = max(0, ceil_div(srr.end - srr.begin, srr.step));
   const int cfx = max(0, ceil_div(sfx.end - sfx.begin, sfx.step));
@@ -1768,7 +1876,8 @@ __device__ __forceinline__ void phase_bwd1(const KParams& p, char* lds, Meta& me
                               sizeof(T) == 2 ? reinterpret_cast<const char*>(p.xs) : reinterpret_cast<const char*>(p.x),
                               sizeof(T) == 2 ? nullptr : p.perm, sizeof(T) == 2 ? 1 : p.k, d,
                               reinterpret_cast<const char*>(p.dh), f, m0, n0, gw1 + (long)e * d * f, p.wpart1,
-                              MT11 * NT11, zero_experts, n10 + e * (MT11 * NT11) + wi.t);
+                              MT11 * NT11, zero_experts, n10 + e * (MT11 * NT11) + wi.t, p.slot_xs, p.stride_nd,
+                              p.slot_dh, p.stride_nf);
       continue;
     }
     if (q >= c11 + c12 + crr) {

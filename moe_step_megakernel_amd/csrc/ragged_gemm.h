@@ -701,17 +701,21 @@ __device__ __forceinline__ void pipe_step(Frags& n, const Frags& c, f32x16_t (&a
       fb.template reg<1, C>() + so);
 }
 
-template <int NS, bool MN_A, bool MN_B, bool GA, class Epi, class Pre>
-__device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi,
-                                         Pre&& pre) {
-  static_assert(NS >= 2 && NS <= 4, "wait_vm covers up to two k-tiles in flight behind the one awaited");
-  f32x16_t acc[2][2];
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// The k-loop of one tile over operands A, B (contraction length K), added
+// into acc; no epilogue.  On return every load of the tile has completed.
+template <int NS, bool MN_A, bool MN_B, bool GA>
+__device__ __forceinline__ void tile_dma_acc(char* lds, const Operand& A, const Operand& B, int K,
+                                             f32x16_t (&acc)[2][2]) {
+  static_assert(NS >= 2 && NS <= 4, "wait_vm covers up to two k-tiles in flight behind the one awaited");
   DmaOp<MN_A> da;
   DmaOp<MN_B> db;
   da.init(A);
@@ -782,8 +786,32 @@ __device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Oper
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]));
   }
+}
+
+template <int NS, bool MN_A, bool MN_B, bool GA, class Epi, class Pre>
+__device__ __forceinline__ void tile_dma(char* lds, const Operand& A, const Operand& B, int K, Epi&& epi,
+                                         Pre&& pre) {
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  tile_dma_acc<NS, MN_A, MN_B, GA>(lds, A, B, K, acc);
   // every wave is done with the stages (all direct-to-LDS loads completed at
   // the last vmcnt wait, none was issued after it)
+  lds_sync();
+  epilogue(lds, acc, epi, pre);
+}
+
+// One bf16 tile whose contraction runs over n operand pieces: piece(i, A, B,
+// K) fills the operands of piece i and returns false to skip it.  The pieces
+// are added into one set of accumulators in order; one epilogue.
+template <int NS, bool MN_A, bool MN_B, bool GA, class Piece, class Epi, class Pre>
+__device__ __forceinline__ void tile_dma_pieces(char* lds, int n, Piece&& piece, Epi&& epi, Pre&& pre) {
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  for (int i = 0; i < n; ++i) {
+    Operand A, B;
+    int K = 0;
+    if (piece(i, A, B, K)) tile_dma_acc<NS, MN_A, MN_B, GA>(lds, A, B, K, acc);
+  }
   lds_sync();
   epilogue(lds, acc, epi, pre);
 }

@@ -12,9 +12,9 @@ from . import binding as B
 class MoeLayerStep:
     def __init__(self, d_model, d_ff, n_experts, top_k, max_tokens, dtype="bf16", lr=1e-3, beta1=0.9,
                  beta2=0.999, adam_eps=1e-8, weight_decay=0.01, clip_norm=1.0, device=0, wg_per_cu=0,
-                 memory_rules=0):
+                 memory_rules=0, max_microbatches=0):
         self.cfg = B.make_config(d_model, d_ff, n_experts, top_k, max_tokens, dtype, lr, beta1, beta2, adam_eps,
-                                 weight_decay, clip_norm, device, wg_per_cu, memory_rules)
+                                 weight_decay, clip_norm, device, wg_per_cu, memory_rules, max_microbatches)
         self.dtype = dtype
         self.dev = torch.device("cuda", device)
         self.P = B.moe_step_param_count(self.cfg)

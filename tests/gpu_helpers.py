@@ -42,7 +42,8 @@ class GpuRun:
     """One layer on cuda:0 with the inputs of ``inp`` (all microbatches)."""
 
     def __init__(self, cfg: synth.LayerConfig, inp: synth.LayerInputs, *, clip_norm=None, wg_per_cu=0,
-                 ready_gemm12=False, cooperative=False, max_tokens=None, stream=None, memory_rules=0):
+                 ready_gemm12=False, cooperative=False, max_tokens=None, stream=None, memory_rules=0,
+                 max_microbatches=0):
         self.ready_gemm12 = ready_gemm12
         self.stream = stream
         self.cooperative = cooperative
@@ -53,7 +54,8 @@ class GpuRun:
                                   lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.eps,
                                   weight_decay=cfg.weight_decay,
                                   clip_norm=cfg.clip_norm if clip_norm is None else clip_norm,
-                                  wg_per_cu=wg_per_cu, memory_rules=memory_rules)
+                                  wg_per_cu=wg_per_cu, memory_rules=memory_rules,
+                                  max_microbatches=max_microbatches)
         self.layer.load_params(torch.from_numpy(inp.flat_params()))
         self.set_inputs(cfg, inp)
 

@@ -46,9 +46,15 @@ def test_param_count(d, f, E, k, expect):
     (dict(n_experts=65), B.MOE_ERR_SHAPE), (dict(top_k=9, n_experts=16), B.MOE_ERR_SHAPE),
     (dict(max_tokens=0), B.MOE_ERR_ARG), (dict(beta1=1.0), B.MOE_ERR_ARG), (dict(wg_per_cu=3), B.MOE_ERR_ARG),
     (dict(max_tokens=(1 << 24) + 1), B.MOE_ERR_SHAPE),
+    # deferred expert weight gradients: 2..16 slots, bf16 only, not with the recomputation rule
+    (dict(max_microbatches=1), B.MOE_OK), (dict(max_microbatches=16), B.MOE_OK),
+    (dict(max_microbatches=17), B.MOE_ERR_ARG), (dict(max_microbatches=-1), B.MOE_ERR_ARG),
+    (dict(max_microbatches=4, dtype="f32"), B.MOE_ERR_ARG),
+    (dict(max_microbatches=4, memory_rules=B.MOE_MEM_RECOMPUTE), B.MOE_ERR_ARG),
+    (dict(max_microbatches=16, max_tokens=1 << 24, top_k=4), B.MOE_ERR_SHAPE),
 ])
 def test_config_validation(kw, expect):
-    base = dict(d_model=64, d_ff=128, n_experts=4, top_k=2, max_tokens=256)
+    base = dict(d_model=64, d_ff=128, n_experts=4, top_k=2, max_tokens=256, dtype="bf16")
     base.update(kw)
     cfg = B.make_config(**base)
     assert B.moe_step_check_config(cfg) == expect

@@ -43,12 +43,12 @@ def _check_routing(cfg, inp, out, w_router):
 
 
 def _run_and_compare(cfg, inp, tol, *, steps=2, clip_norm=None, wg_per_cu=0, ready_gemm12=False, cooperative=False,
-                     memory_rules=0):
+                     memory_rules=0, max_microbatches=0):
     say(f"[gpu] {cfg.name} T={cfg.tokens}x{cfg.microbatches} d={cfg.d_model} f={cfg.d_ff} E={cfg.n_experts} "
         f"k={cfg.top_k} {cfg.dtype} clip={cfg.clip_norm if clip_norm is None else clip_norm} "
-        f"wg_per_cu={wg_per_cu} memory_rules={memory_rules}")
+        f"wg_per_cu={wg_per_cu} memory_rules={memory_rules} max_microbatches={max_microbatches}")
     run = GpuRun(cfg, inp, clip_norm=clip_norm, wg_per_cu=wg_per_cu, ready_gemm12=ready_gemm12,
-                 cooperative=cooperative, memory_rules=memory_rules)
+                 cooperative=cooperative, memory_rules=memory_rules, max_microbatches=max_microbatches)
     try:
         params = inp.flat_params().astype(np.float64)
         m = np.zeros_like(params)
@@ -357,6 +357,55 @@ def test_bf16_32x1024_full_size():
 def test_top8_4x1024_full_size():
     cfg = synth.CONFIGS["top8_4x1024"]
     _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL, steps=2)
+
+
+@pytest.mark.parametrize("T,d,f,E,k,mb,wg_per_cu,skew,slots", [
+    (1000, 256, 384, 16, 2, 3, 2, True, 3),    # split chunks over the slots' concatenated rows
+    (1000, 256, 384, 16, 2, 3, 1, True, 16),   # the one-per-CU kernel, spare slots
+    (700, 128, 256, 8, 2, 4, 2, False, 4),     # balanced routing
+    (513, 256, 128, 64, 8, 2, 1, False, 2),    # 64 experts, top-8, empty experts in some slots
+    (1000, 256, 384, 16, 2, 1, 2, True, 2),    # one microbatch: slot 0 applies
+])
+def test_deferred_weight_gradients(T, d, f, E, k, mb, wg_per_cu, skew, slots):
+    # max_microbatches > 1: each microbatch launch keeps its dW operand rows
+    # in a slot and the applying launch contracts dW1 / dW2 over all slots;
+    # the same update within the same gates, over two updates (the slots are
+    # reused by the second)
+    cfg = synth.small_config("deferred", T, d, f, E, k, "bf16", microbatches=mb)
+    inp = synth.make_inputs(cfg, 23)
+    if skew:
+        bias = np.zeros(E, np.float32)
+        bias[0], bias[1] = 4.0, 2.0
+        inp.router_bias = bias
+    _run_and_compare(cfg, inp, BF16_TOL, steps=2, wg_per_cu=wg_per_cu, max_microbatches=slots)
+
+
+def test_deferred_weight_gradients_slot_limit():
+    # more launches than slots before the experts are applied is refused, and
+    # the handle stays usable: the next update from a zeroing launch matches
+    cfg = synth.small_config("deferred_limit", 512, 128, 256, 8, 2, "bf16", microbatches=3)
+    inp = synth.make_inputs(cfg, 24)
+    run = GpuRun(cfg, inp, wg_per_cu=2, max_microbatches=2)
+    try:
+        x, t = run.microbatch(0)
+        L = run.layer
+        L.run(x, t, tokens_in_update=3 * cfg.tokens, step=1, zero_grad=True, apply=False)
+        L.run(x, t, tokens_in_update=3 * cfg.tokens, step=1, zero_grad=False, apply=False)
+        with pytest.raises(B.MoeStepError) as ei:
+            L.run(x, t, tokens_in_update=3 * cfg.tokens, step=1, zero_grad=False, apply=False)
+        assert ei.value.status == B.MOE_ERR_STATE
+        torch.cuda.synchronize()
+        L.status()
+    finally:
+        run.close()
+    cfg2 = synth.small_config("deferred_limit", 512, 128, 256, 8, 2, "bf16", microbatches=2)
+    _run_and_compare(cfg2, synth.make_inputs(cfg2, 24), BF16_TOL, steps=1, wg_per_cu=2, max_microbatches=2)
+
+
+@pytest.mark.timeout(1200)
+def test_zipf_16x8x1024_accumulated_deferred_weight_gradients():
+    cfg = synth.CONFIGS["zipf_16x8x1024"]
+    _run_and_compare(cfg, synth.make_inputs(cfg, 0), BF16_TOL, steps=1, max_microbatches=cfg.microbatches)
 
 
 @pytest.mark.timeout(1200)
