@@ -212,6 +212,9 @@ def main(argv=None):
                     help="every workgroup writes its XCD's L2 back at each grid barrier (instead of one per XCD)")
     ap.add_argument("--recompute", action="store_true",
                     help="memory rule: store H only and recompute gelu(H) / gelu'(H) where they are read")
+    ap.add_argument("--no-defer", action="store_true",
+                    help="updates over several microbatch launches add their expert weight gradients every "
+                         "launch instead of deferring them to the applying launch")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
@@ -236,10 +239,14 @@ def main(argv=None):
           f"E={cfg.n_experts} k={cfg.top_k} {cfg.dtype}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, 0)
     dev = torch.device("cuda", 0)
+    # updates over several microbatch launches defer the expert weight
+    # gradients to the applying launch (bf16, plain updates) unless told not to
+    defer = cfg.microbatches if (cfg.microbatches > 1 and cfg.dtype == "bf16" and not args.recompute
+                                 and args.selective == 0 and not args.no_defer) else 0
     layer = MoeLayerStep(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.tokens, cfg.dtype, lr=cfg.lr,
                          beta1=cfg.beta1, beta2=cfg.beta2, adam_eps=cfg.eps, weight_decay=cfg.weight_decay,
                          clip_norm=cfg.clip_norm, wg_per_cu=args.wg_per_cu,
-                         memory_rules=1 if args.recompute else 0)
+                         memory_rules=1 if args.recompute else 0, max_microbatches=defer)
     layer.load_params(torch.from_numpy(inp.flat_params()))
 
     def tok(a, bits):
@@ -378,7 +385,8 @@ def main(argv=None):
                    "tokens_per_update": cfg.tokens_in_update, "global_batch": cfg.tokens_in_update,
                    "seq_len": 1024, "parallelism": "single-gpu",
                    **({"ready_gemm12": True} if args.ready_gemm12 else {}),
-                   **({"memory_rules": "recompute"} if args.recompute else {})},
+                   **({"memory_rules": "recompute"} if args.recompute else {}),
+                   **({"deferred_weight_gradients": defer} if defer else {})},
         "ms_per_update_median": float(np.median(upd_ms)), "ms_per_update_p10": float(np.percentile(upd_ms, 10)),
         "ms_per_update_p90": float(np.percentile(upd_ms, 90)),
         "ms_per_update_fresh_median": float(np.median(fresh_ms)),

@@ -144,6 +144,8 @@ def main(argv=None):
     ap.add_argument("--inputs-dir", default="/tmp")
     ap.add_argument("--fresh", action="store_true",
                     help="every update from the initial parameters and zero moments (the routing of the first)")
+    ap.add_argument("--defer", action="store_true",
+                    help="deferred expert weight gradients (max_microbatches = the update's microbatches)")
     args = ap.parse_args(argv)
     sys.path.insert(0, ROOT)
     import synth
@@ -157,7 +159,8 @@ def main(argv=None):
     synth_dump.dump(cfg, 0, inputs)
     log(f"inputs of {cfg.name} written to {inputs}")
     masks = ",".join(f"0x{m:03x}" for _, m, _ in MASKS)
-    drv = [BENCH, "--inputs", inputs, "--warmup", str(args.warmup)] + (["--fresh"] if args.fresh else [])
+    drv = [BENCH, "--inputs", inputs, "--warmup", str(args.warmup)] + (["--fresh"] if args.fresh else []) + \
+        (["--defer"] if args.defer else [])
     M = cfg.microbatches
 
     # 1. uncounted timing
@@ -241,7 +244,8 @@ def main(argv=None):
              f"E={cfg.n_experts}, top-{cfg.top_k}, {cfg.dtype}; the seeded inputs of the tests "
              f"(`python -m synth.dump --config {cfg.name}`). Grid {grid} workgroups. Kernel sources sha256 "
              f"`{kernel_source_sha256()[:16]}…`. Made by `python -m moe_step_megakernel_amd.profile --config "
-             f"{cfg.name}{' --fresh' if args.fresh else ''}` (from /tmp with TMPDIR=/tmp), which runs:", "",
+             f"{cfg.name}{' --fresh' if args.fresh else ''}{' --defer' if args.defer else ''}` (from /tmp with TMPDIR=/tmp), "
+             "which runs:", "",
              "```", "moe_step_bench " + shown(drv[1:]) + f" --steps {args.timing_steps} --skip {masks}",
              shown(kt_cmd),
              "rocprofv3 --pmc " + " ".join(PASS_A) + " -f csv -d <work>/pmcA -o pmc -- moe_step_bench ... --steps "
@@ -295,7 +299,8 @@ def main(argv=None):
            "kernel_source_sha256": kernel_source_sha256(),
            "hbm_bytes_per_launch": full["hbm"] / M, "hbm_bytes_per_update": full["hbm"],
            "fetch_scale": fetch_scale, "write_scale": write_scale,
-           "command": f"python -m moe_step_megakernel_amd.profile --config {cfg.name}" + (" --fresh" if args.fresh else ""),
+           "command": f"python -m moe_step_megakernel_amd.profile --config {cfg.name}" + (" --fresh" if args.fresh else "")
+           + (" --defer" if args.defer else ""),
            "measured": time.strftime("%Y-%m-%d"), "steps_inside_phases": diffs}
     with open(os.path.join(args.out, f"moe_step_kernel_{cfg.name}_hbm_traffic.json"), "w") as fh:
         json.dump(doc, fh, indent=1)
