@@ -123,8 +123,12 @@ constexpr long kTwoPerCuRows = 4096;
 // written with non-temporal stores.  Measured on the same layer (C++ driver,
 // one box): plain stores win at 2x1024 (0.421 against 0.490 ms) and tie on the
 // Zipf workload's 8192-token microbatches; non-temporal ones win at 32x1024
-// (1.723 against 1.756 ms).
+// (1.723 against 1.756 ms).  With deferred weight gradients the outputs go to
+// a fresh slot every launch, and at the Zipf microbatches (16,384 rows)
+// non-temporal stores win (7.59 against 7.74 ms per update; without deferral
+// they lose there, 8.90 against 8.82 ms, same box).
 constexpr long kNonTemporalRows = 32768;
+constexpr long kNonTemporalRowsDeferred = 16384;
 
 struct moe_step {
   moe_step_config cfg;
@@ -518,7 +522,8 @@ static int run_impl(moe_step* h, char* err, const moe_step_io* io, int32_t n_tok
   p.ctrl.limit = (run_flags & MOE_RUN_TEST_TIMEOUT) ? moe::kTestTimeoutTicks : moe::kBarrierTimeoutTicks;
   p.epoch = ++h->epoch;
   p.recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) ? 1 : 0;
-  p.nt_stores = (long)n_tokens * c.top_k >= kNonTemporalRows ? 1 : 0;
+  p.nt_stores =
+      (long)n_tokens * c.top_k >= (c.max_microbatches > 1 ? kNonTemporalRowsDeferred : kNonTemporalRows) ? 1 : 0;
   // deferred weight gradients: this launch's slot of the update
   int slot = -1;
   const bool zero_e = (run_flags & MOE_RUN_ZERO_GRAD_EXPERTS) != 0u;
