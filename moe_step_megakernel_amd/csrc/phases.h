@@ -890,6 +890,7 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     int o = 0, mo = 0;
     for (int e = 0; e < E; ++e) {
       meta.cnt[e] = st[e];
+      meta.wcnt[e] = st[e];
       meta.off[e] = o;
       meta.moff[e] = mo;
       o += st[e];
@@ -899,12 +900,13 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
     meta.moff[E] = mo;
   }
   __syncthreads();
-  if (tid < E) {
-    // the rows the weight-gradient products contract over; with deferred
-    // weight gradients this launch's counts and offsets go to its slot (the
-    // applying launch reads the earlier slots', written by earlier launches)
-    int w = meta.cnt[tid];
-    if (p.defer) {
+  if (p.defer) {
+    // the rows the weight-gradient products contract over (wcnt, this
+    // launch's own otherwise): with deferred weight gradients this launch's
+    // counts and offsets go to its slot, and the applying launch adds the
+    // earlier slots' (written by earlier launches)
+    if (tid < E) {
+      int w = meta.cnt[tid];
       if (lwg == 0) {
         p.slot_cnt[p.slot * E + tid] = meta.cnt[tid];
         p.slot_off[p.slot * E + tid] = meta.off[tid];
@@ -913,10 +915,10 @@ __device__ __forceinline__ void phase_order(const KParams& p, char* smem, Meta& 
         for (int s = 0; s < p.slot; ++s) w += p.slot_cnt[s * E + tid];
       else
         w = 0;
+      meta.wcnt[tid] = w;
     }
-    meta.wcnt[tid] = w;
+    __syncthreads();
   }
-  __syncthreads();
   if (tid < E) {
     // rank of this expert by row count, for dealing the weight-gradient tiles
     const int c = meta.wcnt[tid];
