@@ -26,12 +26,14 @@ BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 
 
-def algorithmic_bytes(cfg) -> dict:
+def algorithmic_bytes(cfg, deferred=False) -> dict:
     """HBM bytes the update must move, phase by phase, with every cross-phase value
     stored once: token rows gathered into expert order, H and A in the activation
     dtype, expert outputs O in fp32, dO and dH and the per-slot input gradient in
     the activation dtype, fp32 gradients, 30 bytes per parameter for clip+AdamW
-    (28 in fp32 mode).  Per microbatch unless marked."""
+    (28 in fp32 mode).  Per microbatch unless marked.  With deferred weight
+    gradients the expert gradients are written once per update, not once per
+    microbatch."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, d, f, E, k = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k
     N = T * k
@@ -52,8 +54,10 @@ def algorithmic_bytes(cfg) -> dict:
     }
     per_mb = sum(ph.values())
     adamw = P * (30 if cfg.dtype == "bf16" else 28)
-    return {"per_microbatch": per_mb, "adamw": adamw,
-            "per_update": per_mb * cfg.microbatches + adamw, "phases": ph}
+    per_update = per_mb * cfg.microbatches + adamw
+    if deferred:
+        per_update -= 2 * W * 4 * (cfg.microbatches - 1)
+    return {"per_microbatch": per_mb, "adamw": adamw, "per_update": per_update, "phases": ph}
 
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -354,11 +358,11 @@ def main(argv=None):
         print("# phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in phases["phase_us"].items())
               + f"  barrier idle mean {phases['barrier_idle_frac_mean']:.3f}", file=sys.stderr, flush=True)
 
-    ab = algorithmic_bytes(cfg)
+    ab = algorithmic_bytes(cfg, deferred=defer > 0)
     # the dominant (and only) kernel: one launch per microbatch, its average
-    # duration from the timed region
+    # duration from the timed region (bytes: the update's, averaged over its launches)
     avg_launch_s = total_ms / (args.steps * M) / 1e3
-    bytes_per_launch = ab["per_microbatch"] + ab["adamw"] / M
+    bytes_per_launch = ab["per_update"] / M
     achieved = bytes_per_launch / avg_launch_s / 1e9
     traffic = measured_traffic(cfg)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
