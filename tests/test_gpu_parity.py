@@ -380,6 +380,19 @@ def test_deferred_weight_gradients(T, d, f, E, k, mb, wg_per_cu, skew, slots):
     _run_and_compare(cfg, inp, BF16_TOL, steps=2, wg_per_cu=wg_per_cu, max_microbatches=slots)
 
 
+@pytest.mark.parametrize("ready_gemm12,cooperative", [(True, False), (False, True)])
+def test_deferred_weight_gradients_other_launch_modes(ready_gemm12, cooperative):
+    # deferral with the readiness counters between the expert products, and
+    # with a cooperative launch
+    cfg = synth.small_config("deferred_modes", 1000, 256, 384, 16, 2, "bf16", microbatches=3)
+    inp = synth.make_inputs(cfg, 26)
+    bias = np.zeros(cfg.n_experts, np.float32)
+    bias[0], bias[1] = 4.0, 2.0
+    inp.router_bias = bias
+    _run_and_compare(cfg, inp, BF16_TOL, steps=2, wg_per_cu=2, ready_gemm12=ready_gemm12, cooperative=cooperative,
+                     max_microbatches=3)
+
+
 def test_deferred_weight_gradients_slot_limit():
     # more launches than slots before the experts are applied is refused, and
     # the handle stays usable: the next update from a zeroing launch matches
