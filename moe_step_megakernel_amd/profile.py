@@ -39,6 +39,7 @@ import os
 import re
 import subprocess
 import sys
+import tempfile
 import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -139,7 +140,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=5, help="updates per mask")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--timing-steps", type=int, default=30, help="updates per mask in the uncounted timing run")
-    ap.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--work", default=os.path.join(tempfile.gettempdir(), "moe_step_prof"),
+                    help="directory for the raw rocprofv3 output")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--inputs-dir", default="/tmp")
     ap.add_argument("--fresh", action="store_true",
