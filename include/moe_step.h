@@ -93,15 +93,23 @@ typedef struct {
                              router dot products over lanes and the loss's
                              per-workgroup partial sums follow the workgroup
                              count. */
-  uint32_t memory_rules;  /* opt-in rules that trade time for arena memory (the
-                             pages' "Open problems", Generality 2); 0 = none.
+  uint32_t memory_rules;  /* opt-in arena rules (the pages' "Open problems",
+                             Generality 2: rules for lifetimes and
+                             recomputation); 0 = none.
                              MOE_MEM_RECOMPUTE: of the first expert product only
                              H = x W1 is stored; gelu(H) is recomputed on the
                              operand fragments of the second product and of the
                              dW2 product, gelu'(H) in the dH epilogue.  The arena
                              loses one [tokens * top_k, d_ff] tensor; the update
                              is slower (each H element passes through GELU once
-                             per output column tile that reads it). */
+                             per output column tile that reads it).
+                             MOE_MEM_GUARDS: a checking layout, not a saving: a
+                             zone of at least 1 MiB follows every sub-buffer of
+                             the arena (about 26 MiB more), zero from create
+                             on like the rest of the arena and never written by
+                             a correct kernel; moe_step_check_guards reads the
+                             zones.  Results are those of the plain layout.
+                             Refused by moe_step_run_static. */
   int32_t max_microbatches; /* 0 or 1: every launch adds its expert weight
                              gradients to grads (the default).  M in [2, 16]
                              (bf16 handles, not with MOE_MEM_RECOMPUTE):
@@ -126,6 +134,7 @@ typedef struct {
 } moe_step_config;
 
 #define MOE_MEM_RECOMPUTE 0x1u
+#define MOE_MEM_GUARDS 0x2u
 
 /* Buffers of one launch.  Shapes use T = n_tokens, P = moe_step_param_count. */
 typedef struct {
@@ -304,6 +313,19 @@ int moe_step_run_static(const moe_step_config* cfg, const moe_step_io* io, int32
  * and before this call makes no writes (every workgroup finds the abort word
  * set on entry and returns). */
 int moe_step_status(moe_step_t h);
+
+/* Checks the guard zones of a handle created with MOE_MEM_GUARDS in
+ * memory_rules: each sub-buffer of the planned arena (Latch "How a training
+ * megakernel works", "What Latch does", step 4) is followed by a zone that
+ * must still hold the zeros that create wrote.  Waits for the handle's last
+ * stream, then copies every zone to the host.  Returns MOE_OK if all are
+ * intact; MOE_ERR_STATE if a zone holds a nonzero byte (last_error names the
+ * buffer before the first such zone and the offset past its end) or if the
+ * handle has no zones; MOE_ERR_HIP or MOE_ERR_NOMEM if a copy or a host
+ * buffer fails.  *damaged (optional) receives the number of written zones
+ * (0 on every other outcome).  A write of zeros past a buffer's end is not
+ * seen. */
+int moe_step_check_guards(moe_step_t h, int32_t* damaged);
 
 /* Words of io.trace needed for MOE_RUN_TRACE: workgroups * phases * 3. */
 size_t moe_step_trace_words(moe_step_t h);

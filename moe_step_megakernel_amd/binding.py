@@ -32,6 +32,7 @@ def MOE_RUN_SKIP_PHASE(i: int) -> int:
 MOE_DEVICE_BARRIER_TIMEOUT, MOE_DEVICE_NONFINITE_LOGIT, MOE_DEVICE_BAD_ROUTE = 0x1, 0x2, 0x4
 MOE_STEP_STATIC_SCRATCH_BYTES = 32 << 20
 MOE_MEM_RECOMPUTE = 0x1
+MOE_MEM_GUARDS = 0x2
 N_PHASES = 8
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_HIP", -4: "MOE_ERR_NOMEM",
@@ -90,6 +91,8 @@ def load_library():
     lib.moe_step_run_static.restype = ctypes.c_int
     lib.moe_step_status.argtypes = [ctypes.c_void_p]
     lib.moe_step_status.restype = ctypes.c_int
+    lib.moe_step_check_guards.argtypes = [ctypes.c_void_p, P(ctypes.c_int32)]
+    lib.moe_step_check_guards.restype = ctypes.c_int
     lib.moe_step_trace_words.argtypes = [ctypes.c_void_p]
     lib.moe_step_trace_words.restype = ctypes.c_size_t
     lib.moe_step_grid_size.argtypes = [ctypes.c_void_p]
@@ -163,6 +166,13 @@ def moe_step_status(handle) -> None:
     rc = load_library().moe_step_status(handle)
     if rc != MOE_OK:
         raise MoeStepError("moe_step_status", rc, moe_step_last_error(handle))
+
+
+def moe_step_check_guards(handle) -> None:
+    damaged = ctypes.c_int32(0)
+    rc = load_library().moe_step_check_guards(handle, ctypes.byref(damaged))
+    if rc != MOE_OK:
+        raise MoeStepError("moe_step_check_guards", rc, moe_step_last_error(handle))
 
 
 def moe_step_trace_words(handle) -> int:

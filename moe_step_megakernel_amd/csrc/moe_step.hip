@@ -53,7 +53,7 @@ int check_config(const moe_step_config* c, char* err) {
     set_err(err, "optimizer hyper-parameters out of range");
     return MOE_ERR_ARG;
   }
-  if (c->memory_rules & ~MOE_MEM_RECOMPUTE) {
+  if (c->memory_rules & ~(MOE_MEM_RECOMPUTE | MOE_MEM_GUARDS)) {
     set_err(err, "unknown memory rules 0x%x", c->memory_rules);
     return MOE_ERR_ARG;
   }
@@ -169,6 +169,14 @@ struct moe_step {
   float* wpart1;
   int wpart_sets = 0;
   unsigned* ctrl;
+  // guard zones of a MOE_MEM_GUARDS handle: the arena offset of each zone and
+  // the sub-buffer it follows
+  struct Guard {
+    size_t off, len;
+    const char* after;
+  };
+  Guard guards[32];
+  int n_guards = 0;
   // deferred weight gradients (cfg.max_microbatches > 1): per-slot arrays and
   // the slot of the last launch (-1: the experts were applied, or none yet)
   char* slot_act = nullptr;
@@ -216,6 +224,10 @@ static int select_kernel(const moe_step_config& c, int cus, moe_step& h, char* e
   return MOE_OK;
 }
 
+// Bytes of each guard zone of a MOE_MEM_GUARDS handle: more than a 128-row tile
+// of the widest stored activation reaches past its buffer.
+constexpr size_t kGuardBytes = 1u << 20;
+
 // Lays out the arena of h (h.cfg and h.grid set) and returns its size in
 // bytes; with a base address, also points h's sub-buffers into it.  The
 // barrier words (ctrl_words of them) come first.
@@ -238,16 +250,25 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
     for (int t : cand)
       if (t >= 1) rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h.grid)));
   }
+  // MOE_MEM_GUARDS: a zone of at least kGuardBytes after every sub-buffer,
+  // zero like the rest of the arena at create, that no kernel may write
+  const bool guarded = (c.memory_rules & MOE_MEM_GUARDS) != 0u;
+  constexpr int kMaxGuards = (int)(sizeof(h.guards) / sizeof(h.guards[0]));
+  h.n_guards = 0;
   size_t off = 0;
-  auto take = [&](size_t bytes) {
+  auto take = [&](const char* name, size_t bytes) {
     size_t o = off;
     off = align_up(off + (bytes ? bytes : 1), 256);
+    if (guarded && h.n_guards < kMaxGuards) {   // from the byte after the buffer on, its padding included
+      off += kGuardBytes;
+      h.guards[h.n_guards++] = {o + bytes, off - (o + bytes), name};
+    }
     return o;
   };
-  const size_t o_ctrl = take(ctrl_words * sizeof(unsigned));
-  const size_t o_idx = take(N * 4), o_gate = take(N * 4), o_dz = take(N * 4);
-  const size_t o_hist = take((size_t)h.grid * E * 4);
-  const size_t o_perm = take(N * 4), o_inv = take(N * 4);
+  const size_t o_ctrl = take("ctrl", ctrl_words * sizeof(unsigned));
+  const size_t o_idx = take("idx", N * 4), o_gate = take("gate", N * 4), o_dz = take("dz", N * 4);
+  const size_t o_hist = take("hist", (size_t)h.grid * E * 4);
+  const size_t o_perm = take("perm", N * 4), o_inv = take("inv", N * 4);
   // Stored activations share memory where their lifetimes (phases between the
   // grid barriers) do not overlap:
   //   O  [N, d] fp32: written by GEMM 2, last read by the combine;
@@ -258,32 +279,32 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
   // until the applying launch, so O and dXs get buffers of their own.
   const bool defer = c.max_microbatches > 1;
   const size_t M = defer ? (size_t)c.max_microbatches : 0;
-  const size_t o_out_dh = take(defer ? N * d * 4 : std::max(N * d * 4, N * f * es));
-  const size_t o_act_dxs = take(defer ? N * d * es : std::max(N * f * es, N * d * es));
+  const size_t o_out_dh = take("out_dh", defer ? N * d * 4 : std::max(N * d * 4, N * f * es));
+  const size_t o_act_dxs = take("act_dxs", defer ? N * d * es : std::max(N * f * es, N * d * es));
   const size_t snf = align_up(N * f * es, 256), snd = align_up(N * d * es, 256);
-  const size_t o_slot_act = take(M * snf), o_slot_dh = take(M * snf);
-  const size_t o_slot_dout = take(M * snd), o_slot_xs = take(M * snd);
-  const size_t o_slot_cnt = take(defer ? (size_t)moe::kMaxSlots * E * 4 : 0);
-  const size_t o_slot_off = take(defer ? (size_t)moe::kMaxSlots * E * 4 : 0);
+  const size_t o_slot_act = take("slot_act", M * snf), o_slot_dh = take("slot_dh", M * snf);
+  const size_t o_slot_dout = take("slot_dout", M * snd), o_slot_xs = take("slot_xs", M * snd);
+  const size_t o_slot_cnt = take("slot_cnt", defer ? (size_t)moe::kMaxSlots * E * 4 : 0);
+  const size_t o_slot_off = take("slot_off", defer ? (size_t)moe::kMaxSlots * E * 4 : 0);
   // G' [N, f]: not kept under the recomputation rule (the dH epilogue forms it from H)
   const bool recompute = (c.memory_rules & MOE_MEM_RECOMPUTE) != 0u;
-  const size_t o_gp = take(recompute ? 0 : N * f * es), o_dout = take(N * d * es);
-  const size_t o_wrt = take((size_t)E * d * 4);
-  const size_t o_rpart = take(rch * E * d * 4);
-  const size_t o_loss = take((size_t)h.grid * 4);
-  const size_t o_norm = take((size_t)(n10 + n11 + nrr) * 4);
-  const size_t o_shadow = c.dtype == MOE_DTYPE_BF16 ? take(2ull * E * d * f * 2) : 0;
-  const size_t o_xs = c.dtype == MOE_DTYPE_BF16 ? take(N * d * 2) : 0;
+  const size_t o_gp = take("gp", recompute ? 0 : N * f * es), o_dout = take("dout", N * d * es);
+  const size_t o_wrt = take("wrt", (size_t)E * d * 4);
+  const size_t o_rpart = take("rpart", rch * E * d * 4);
+  const size_t o_loss = take("loss", (size_t)h.grid * 4);
+  const size_t o_norm = take("norm", (size_t)(n10 + n11 + nrr) * 4);
+  const size_t o_shadow = c.dtype == MOE_DTYPE_BF16 ? take("shadow", 2ull * E * d * f * 2) : 0;
+  const size_t o_xs = c.dtype == MOE_DTYPE_BF16 ? take("xs", N * d * 2) : 0;
   // partial weight-gradient tiles of split contractions (skewed routing): at most
   // E/2 extra chunks over all experts (E in the applying launch of deferred
   // weight gradients), each a 128 x 128 fp32 tile per gradient tile; the
   // kernel never splits into more than the buffers hold
   const size_t wtiles = (size_t)cdiv(f, moe::gemm::BM) * cdiv(d, moe::gemm::BN);
   const size_t xchunks = c.max_microbatches > 1 ? (size_t)E + 1 : (size_t)E / 2 + 1;
-  const size_t o_wpart2 = take(xchunks * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
-  const size_t o_wpart1 = take(xchunks * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
+  const size_t o_wpart2 = take("wpart2", xchunks * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
+  const size_t o_wpart1 = take("wpart1", xchunks * wtiles * moe::gemm::BM * moe::gemm::BN * 4);
   const int nrb = (int)((N + moe::gemm::BM - 1) / moe::gemm::BM) + E;   // row tiles of GEMM 1 (upper bound)
-  const size_t o_ready = take((size_t)nrb * 4);
+  const size_t o_ready = take("ready", (size_t)nrb * 4);
   if (base) {
     char* a = base;
     h.ctrl = reinterpret_cast<unsigned*>(a + o_ctrl);
@@ -717,6 +738,10 @@ int moe_step_run_static(const moe_step_config* cfg, const moe_step_io* io, int32
     set_err(err, "io and io->stats are required (stats[3] receives the device status)");
     return MOE_ERR_ARG;
   }
+  if (cfg->memory_rules & MOE_MEM_GUARDS) {
+    set_err(err, "MOE_MEM_GUARDS needs a handle (moe_step_check_guards reads its zones)");
+    return MOE_ERR_ARG;
+  }
   if (run_flags & MOE_RUN_SKIP_MASK) {
     set_err(err, "phase skipping needs a handle (it reuses the previous launch's arena)");
     return MOE_ERR_ARG;
@@ -780,6 +805,57 @@ int moe_step_status(moe_step_t h) {
     if (he == hipSuccess) he = hipDeviceSynchronize();
     h->epoch = 0;
     return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
+}
+
+int moe_step_check_guards(moe_step_t h, int32_t* damaged) {
+  if (damaged) *damaged = 0;
+  if (!h) return MOE_ERR_ARG;
+  if (!(h->cfg.memory_rules & MOE_MEM_GUARDS)) {
+    set_err(h->err, "the handle was created without MOE_MEM_GUARDS");
+    return MOE_ERR_STATE;
+  }
+  hipError_t he = hipSetDevice(h->cfg.device);
+  if (he == hipSuccess && h->launched) he = hipStreamSynchronize(h->last_stream);
+  if (he != hipSuccess) {
+    set_err(h->err, "waiting for the stream: %s", hipGetErrorString(he));
+    return MOE_ERR_HIP;
+  }
+  size_t most = 0;
+  for (int i = 0; i < h->n_guards; ++i) most = std::max(most, h->guards[i].len);
+  unsigned char* buf = new (std::nothrow) unsigned char[most];
+  if (!buf) {
+    set_err(h->err, "host allocation failed");
+    return MOE_ERR_NOMEM;
+  }
+  int bad = 0;
+  const char* first = nullptr;
+  size_t first_at = 0;
+  for (int i = 0; i < h->n_guards; ++i) {
+    const moe_step::Guard& g = h->guards[i];
+    he = hipMemcpy(buf, h->arena + g.off, g.len, hipMemcpyDeviceToHost);
+    if (he != hipSuccess) {
+      delete[] buf;
+      set_err(h->err, "reading a guard zone: %s", hipGetErrorString(he));
+      return MOE_ERR_HIP;
+    }
+    for (size_t b = 0; b < g.len; ++b)
+      if (buf[b] != 0) {
+        if (!first) {
+          first = g.after;
+          first_at = b;
+        }
+        ++bad;
+        break;
+      }
+  }
+  delete[] buf;
+  if (damaged) *damaged = bad;
+  if (bad) {
+    set_err(h->err, "%d guard zone(s) written; the first follows arena buffer %s (byte %zu past its end)", bad,
+            first, first_at);
+    return MOE_ERR_STATE;
   }
   return MOE_OK;
 }

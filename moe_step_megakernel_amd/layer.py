@@ -123,6 +123,11 @@ class MoeLayerStep:
     def status(self):
         B.moe_step_status(self.handle)
 
+    def check_guards(self):
+        """Raises MoeStepError unless every guard zone of the arena is intact
+        (handles made with memory_rules including MOE_MEM_GUARDS)."""
+        B.moe_step_check_guards(self.handle)
+
     def trace_words(self):
         return B.moe_step_trace_words(self.handle)
 

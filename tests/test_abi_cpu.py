@@ -52,6 +52,11 @@ def test_param_count(d, f, E, k, expect):
     (dict(max_microbatches=4, dtype="f32"), B.MOE_ERR_ARG),
     (dict(max_microbatches=4, memory_rules=B.MOE_MEM_RECOMPUTE), B.MOE_ERR_ARG),
     (dict(max_microbatches=16, max_tokens=1 << 24, top_k=4), B.MOE_ERR_SHAPE),
+    # memory rules: the two known bits alone or together; any other bit is refused
+    (dict(memory_rules=B.MOE_MEM_GUARDS), B.MOE_OK),
+    (dict(memory_rules=B.MOE_MEM_GUARDS | B.MOE_MEM_RECOMPUTE), B.MOE_OK),
+    (dict(memory_rules=B.MOE_MEM_GUARDS, max_microbatches=4), B.MOE_OK),
+    (dict(memory_rules=0x4), B.MOE_ERR_ARG),
 ])
 def test_config_validation(kw, expect):
     base = dict(d_model=64, d_ff=128, n_experts=4, top_k=2, max_tokens=256, dtype="bf16")
@@ -91,6 +96,9 @@ def test_null_handle_calls_are_safe():
     assert lib.moe_step_trace_words(None) == 0
     assert lib.moe_step_grid_size(None) == 0
     assert lib.moe_step_arena_bytes(None) == 0
+    damaged = ctypes.c_int32(7)
+    assert lib.moe_step_check_guards(None, ctypes.byref(damaged)) == B.MOE_ERR_ARG and damaged.value == 0
+    assert lib.moe_step_check_guards(None, None) == B.MOE_ERR_ARG
     lib.moe_step_destroy(None)
     assert isinstance(B.moe_step_last_error(None), str)
 
@@ -142,3 +150,12 @@ def test_layer_checks_tensors_before_any_pointer_is_passed(dtype):
         with pytest.raises((TypeError, ValueError)):
             layer._check_tensors(10, args["x"], args["target"], args["dx"], args["router_bias"], args["debug"],
                                  args["trace"])
+
+
+def test_static_entry_refuses_guard_zones_before_hip():
+    import torch
+    cfg = B.make_config(64, 128, 4, 2, 256, memory_rules=B.MOE_MEM_GUARDS)
+    io = B.make_io(stats=torch.zeros(4))   # checked for NULL only; refused before any HIP call
+    lib = B.load_library()
+    assert lib.moe_step_run_static(ctypes.byref(cfg), ctypes.byref(io), 16, 16, 1, 0, None) == B.MOE_ERR_ARG
+    assert "MOE_MEM_GUARDS" in B.moe_step_last_error(None)
