@@ -104,8 +104,9 @@ typedef struct {
                              is slower (each H element passes through GELU once
                              per output column tile that reads it).
                              MOE_MEM_GUARDS: a checking layout, not a saving: a
-                             zone of at least 1 MiB follows every sub-buffer of
-                             the arena (about 26 MiB more), zero from create
+                             zone of max(1 MiB, 128 * max(d_model, d_ff) * 4
+                             bytes) follows every sub-buffer of the arena (26
+                             of them for bf16, 24 for fp32), zero from create
                              on like the rest of the arena and never written by
                              a correct kernel; moe_step_check_guards reads the
                              zones.  Results are those of the plain layout.

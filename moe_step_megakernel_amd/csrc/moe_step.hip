@@ -175,7 +175,7 @@ struct moe_step {
     size_t off, len;
     const char* after;
   };
-  Guard guards[32];
+  Guard guards[32];   // plan_arena takes at most 26 sub-buffers
   int n_guards = 0;
   // deferred weight gradients (cfg.max_microbatches > 1): per-slot arrays and
   // the slot of the last launch (-1: the experts were applied, or none yet)
@@ -224,10 +224,6 @@ static int select_kernel(const moe_step_config& c, int cus, moe_step& h, char* e
   return MOE_OK;
 }
 
-// Bytes of each guard zone of a MOE_MEM_GUARDS handle: more than a 128-row tile
-// of the widest stored activation reaches past its buffer.
-constexpr size_t kGuardBytes = 1u << 20;
-
 // Lays out the arena of h (h.cfg and h.grid set) and returns its size in
 // bytes; with a base address, also points h's sub-buffers into it.  The
 // barrier words (ctrl_words of them) come first.
@@ -250,9 +246,12 @@ static size_t plan_arena(moe_step& h, char* base, size_t ctrl_words) {
     for (int t : cand)
       if (t >= 1) rch = std::max(rch, (size_t)cdiv(t, moe::router_chunk_tokens(t, d, h.grid)));
   }
-  // MOE_MEM_GUARDS: a zone of at least kGuardBytes after every sub-buffer,
-  // zero like the rest of the arena at create, that no kernel may write
+  // MOE_MEM_GUARDS: a zone after every sub-buffer, zero like the rest of the
+  // arena at create, that no kernel may write.  At least 1 MiB, and at least
+  // 128 rows of the widest fp32 row, so that a whole tile written past a
+  // buffer's end stays inside the zone.
   const bool guarded = (c.memory_rules & MOE_MEM_GUARDS) != 0u;
+  const size_t kGuardBytes = std::max((size_t)1 << 20, (size_t)moe::gemm::BM * std::max(d, f) * 4);
   constexpr int kMaxGuards = (int)(sizeof(h.guards) / sizeof(h.guards[0]));
   h.n_guards = 0;
   size_t off = 0;
