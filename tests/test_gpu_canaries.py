@@ -64,6 +64,7 @@ def _run_guarded(cfg, inp, *, wg_per_cu=0, max_microbatches=0, trace=False):
     L = run.layer
     T, E, k, d = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.d_model
     act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    bits = torch.int16 if cfg.dtype == "bf16" else torch.int32   # inputs compared bit for bit
     guards = []
     try:
         _guard_layer(run, dev, guards)
@@ -95,10 +96,8 @@ def _run_guarded(cfg, inp, *, wg_per_cu=0, max_microbatches=0, trace=False):
                 for g in [gx, gt, gdx, *dbg.values()] + ([gtr] if gtr is not None else []):
                     g.check()
                 # the inputs are read only
-                assert torch.equal(gx.view.view(torch.int16 if act == torch.bfloat16 else torch.int32),
-                                   x0.contiguous().view(torch.int16 if act == torch.bfloat16 else torch.int32))
-                assert torch.equal(gt.view.view(torch.int16 if act == torch.bfloat16 else torch.int32),
-                                   t0.contiguous().view(torch.int16 if act == torch.bfloat16 else torch.int32))
+                assert torch.equal(gx.view.view(bits), x0.contiguous().view(bits))
+                assert torch.equal(gt.view.view(bits), t0.contiguous().view(bits))
                 # the update ran: every token has k distinct experts, the counts add up
                 idx = dbg["topk_idx"].view.cpu().numpy()
                 assert idx.min() >= 0 and idx.max() < E
