@@ -31,18 +31,19 @@ class Guarded:
 
     def __init__(self, name, shape, dtype, dev):
         self.name = name
-        nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
-        self.words = (nbytes + 3) // 4
-        self.big = torch.empty(self.words + 2 * GUARD, dtype=torch.int32, device=dev)
+        self.nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        self.big = torch.empty((self.nbytes + 3) // 4 + 2 * GUARD, dtype=torch.int32, device=dev)
         self.big.fill_(PATTERN)
-        self.view = self.big.view(torch.uint8)[4 * GUARD:4 * GUARD + nbytes].view(dtype).view(shape)
+        self.view = self.big.view(torch.uint8)[4 * GUARD:4 * GUARD + self.nbytes].view(dtype).view(shape)
 
     def check(self):
-        host = self.big.cpu().numpy()
-        head, tail = host[:GUARD], host[GUARD + self.words:]
-        for side, g in (("head", head), ("tail", tail)):
-            bad = np.flatnonzero(g != np.int32(PATTERN))
-            assert bad.size == 0, f"{self.name}: {bad.size} guard words of the {side} overwritten (first at {bad[0]})"
+        """Every byte before the view and from its last byte on (the padding of
+        its last word included) still holds the pattern."""
+        raw = self.big.view(torch.uint8).cpu().numpy()
+        want = np.resize(np.frombuffer(np.array([PATTERN], "<i4").tobytes(), np.uint8), raw.size)
+        for side, lo, hi in (("head", 0, 4 * GUARD), ("tail", 4 * GUARD + self.nbytes, raw.size)):
+            bad = np.flatnonzero(raw[lo:hi] != want[lo:hi])
+            assert bad.size == 0, f"{self.name}: {bad.size} guard bytes of the {side} overwritten (first at {bad[0]})"
 
 
 def _guard_layer(run, dev, keep):
